@@ -1,0 +1,173 @@
+/*
+ * wq.h -- C ABI of libwq: weight-only quantized decode matvecs on AMD MI355X
+ * (gfx950).
+ *
+ * The operation is the batch-1 decode product y = x . W^T of a linear layer
+ * whose weight W [N_out][K_in] is stored quantized: it is applied once per
+ * generated token, so its cost is the bytes of W it streams.  Sources, by
+ * page title and section:
+ *
+ *   [README]   gittoolsai.com "gpt-fast" (Chinese mirror of the project
+ *              README): "量化" (quantization) with "Int8 仅权重量化" and
+ *              "Int4 仅权重量化" (int8 / int4 weight-only, group size 32);
+ *              "基准测试" (batch-1 benchmark table: tokens/s and GB/s per
+ *              format); "推测采样" (speculative sampling); "Mixtral 8x7B".
+ *   [GUIDE]    onegen.ai "Efficiently implementing the Mixtral 8x7B model
+ *              with gpt-fast": "Key Features" (int8/int4 weight-only
+ *              quantization; a draft model's tokens verified by the larger
+ *              model).
+ *   [TAGS]     awesome-repositories.com "meta-pytorch/gpt-fast": tag
+ *              "Grouped Quantization".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every buffer is DEVICE memory owned by the caller.  The library allocates
+ *   nothing and keeps no state besides a thread-local error text.  Passing a
+ *   host pointer is outside the contract (the kernel would fault).
+ * - Row-major layouts; bf16 values are passed as their uint16 bit patterns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *   is enqueued and the call returns without synchronising.
+ * - Outputs must not alias inputs.  Where both `y_f32` and `y_bf16` are
+ *   accepted, either may be NULL but not both; y_bf16 is the fp32 result
+ *   rounded to nearest-even.
+ * - Return value: a wq_status.  Arguments are checked on the host before
+ *   anything is launched; a non-OK return launched nothing, except
+ *   WQ_ERR_LAUNCH, which reports a failed launch.  No call aborts or prints;
+ *   wq_last_error() gives the detail of the calling thread's last failure.
+ * - Weights must be finite.  This is not checked; the result of a
+ *   non-finite weight is unspecified.
+ * - Alignment: x, weight and code pointers 16-byte aligned (WQ_ERR_ALIGN).
+ * - Sizes: n >= 0, k >= 0 (n == 0 is a no-op).  K limits per format are
+ *   stated at each call; a larger K returns WQ_ERR_SHAPE.
+ * - Only gfx950 devices are supported (WQ_ERR_DEVICE otherwise).
+ * - Results are deterministic: the same inputs give bitwise the same
+ *   outputs (fixed reduction order, no atomics).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  WQ_OK = 0,
+  WQ_ERR_NULL = 1,   /* a required pointer is NULL                       */
+  WQ_ERR_SHAPE = 2,  /* a size is negative, unsupported or inconsistent  */
+  WQ_ERR_ALIGN = 3,  /* a pointer is not 16-byte aligned                 */
+  WQ_ERR_DEVICE = 4, /* no current HIP device, or it is not gfx950       */
+  WQ_ERR_LAUNCH = 5  /* the HIP runtime reported a launch failure        */
+} wq_status;
+
+/* ------------------------------------------------------------------------ */
+/* Quantizers (offline: once per weight, not per token) -- [README] "Int8   */
+/* 仅权重量化", "Int4 仅权重量化"; [TAGS] "Grouped Quantization".            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * int8 weight-only, per output row (symmetric).
+ *   in : w      fp32 [n][k], k % 4 == 0 (16-byte aligned)
+ *   out: q      int8 [n][k]    codes in [-127, 127]
+ *        scale  bf16 [n]       s = bf16(fp32(max_k |w[r][k]| / 127))
+ * q[r][k] = round-half-even of the exact quotient w[r][k] / s (the stored
+ * bf16 s), clamped to [-127, 127]; a zero scale gives zero codes.  Hence
+ * |w - q s| <= s / 2.  Codes are bit-identical to the CPU oracle's.
+ * q 4-byte and scale 2-byte aligned; no upper limit on k.
+ */
+int wq_quantize_int8(const float* w, int64_t n, int64_t k, int8_t* q, uint16_t* scale,
+                     void* stream);
+
+/*
+ * int4 weight-only, groups of 32 consecutive inputs of one row (asymmetric).
+ *   in : w        fp32 [n][k], k % 32 == 0 (w, qpacked 16-byte aligned,
+ *                  sz 4-byte aligned)
+ *   out: qpacked  u8   [n][k/2]    byte j = code(2j) | code(2j+1) << 4
+ *        sz       bf16 [n][k/32][2] = (scale s, zero z) per group
+ * z = bf16(min of the group) is what code 0 decodes to; t = fp32(max - z);
+ * s = bf16(fp32(t / 15)) if t > 0 else 0.  code = round-half-even of the
+ * exact quotient (w - z) / s clamped to [0, 15] (0 when s == 0); the value a
+ * code stands for is z + code * s.  0.625 byte per weight.  Bit-identical to
+ * the CPU oracle.
+ */
+int wq_quantize_int4g32(const float* w, int64_t n, int64_t k, uint8_t* qpacked, uint16_t* sz,
+                        void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode matvecs, batch 1 -- [README] "基准测试" (Base / 8-bit / 4-bit     */
+/* (G=32) rows: the per-token linear layers of batch-1 generation).         */
+/* Accumulation is fp32.                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Unquantized baseline.  x bf16 [k]; w bf16 [n][k];
+ * y[r] = sum_k x[k] * w[r][k].   k % 8 == 0, k <= 65536.
+ */
+int wq_gemv_bf16(const uint16_t* x, const uint16_t* w, int64_t n, int64_t k, float* y_f32,
+                 uint16_t* y_bf16, void* stream);
+
+/*
+ * int8 per-row.  x bf16 [k]; q int8 [n][k]; scale bf16 [n] (as written by
+ * wq_quantize_int8); y[r] = scale[r] * sum_k x[k] * q[r][k].
+ * k % 16 == 0, k <= 65536.
+ */
+int wq_gemv_int8(const uint16_t* x, const int8_t* q, const uint16_t* scale, int64_t n, int64_t k,
+                 float* y_f32, uint16_t* y_bf16, void* stream);
+
+/*
+ * int4 G=32.  x bf16 [k]; qpacked, sz as written by wq_quantize_int4g32;
+ * y[r] = sum_g ( s[r][g] * sum_{k in g} x[k] code[r][k] + z[r][g] * sum_{k in g} x[k] ).
+ * k % 32 == 0, k <= 131072.
+ */
+int wq_gemv_int4g32(const uint16_t* x, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
+                    int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
+
+/*
+ * Speculative-decoding verify -- [GUIDE] "Key Features" (the larger model
+ * checks the draft's tokens), [README] "推测采样".  The m draft tokens go
+ * through one int4 G=32 linear in one pass, each weight read once:
+ *   x bf16 [m][k], 1 <= m <= 8; y [m][n]; row i of y equals
+ *   wq_gemv_int4g32 applied to row i of x (to fp32 rounding).
+ * k % 32 == 0; k <= 131072 for m == 1, 32768 for 2 <= m <= 5, 16384 for
+ * m >= 6.
+ */
+int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
+                   int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
+
+/*
+ * Top-2 mixture-of-experts decode step for one token, int8 per-row experts
+ * -- [README] "Mixtral 8x7B" (sparse MoE, int8 on one GPU).
+ *   x       bf16 [dim]
+ *   logits  fp32 [e]                 router logits (e == 8)
+ *   w13     int8 [e][2f][dim], s13 bf16 [e][2f]   rows 0..f-1: W1 (gate),
+ *                                                 rows f..2f-1: W3 (up)
+ *   w2      int8 [e][dim][f],  s2  bf16 [e][dim]
+ *   work    fp32 [2][f]          caller-provided scratch (overwritten)
+ *   sel     int32 [2] or NULL    selected experts, larger gate first
+ *   gates   fp32 [2] or NULL     their renormalised gates
+ * Routing: softmax over the e logits, keep the two largest (equal logits:
+ * lower index first), renormalise the pair (g_a = 1 / (1 + exp(l_b - l_a))).
+ * Each selected expert computes a = silu(W1 x) * (W3 x) in fp32 and
+ * o = W2 a; y = g_a o_a + g_b o_b.  Only the two selected experts' weights
+ * are read; routing happens on the device (no host synchronisation).
+ * dim % 16 == 0, f % 16 == 0, 16 <= dim <= 32768, 16 <= f <= 32768; x, w13,
+ * w2 and work 16-byte aligned.
+ */
+int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
+                  const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim,
+                  int64_t f, float* work, float* y_f32, uint16_t* y_bf16, int32_t* sel,
+                  float* gates, void* stream);
+
+/* Static text for a wq_status value ("unknown status" otherwise). */
+const char* wq_status_string(int status);
+
+/* Detail of the calling thread's last non-OK return ("" if none).  The
+ * pointer stays valid until the thread's next failing call. */
+const char* wq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/wq.h declares, and rejects bad arguments on the host before any
+launch.
+
+Pointers here are fake addresses that are also misaligned, so that a call
+which slipped past the check under test would still stop at the alignment
+check and never reach a device.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+BAD = 0x1001          # non-null, misaligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_quantized_wq_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32",
+                 "wq_gemm_smallM", "moe_top2_gemv", "wq_status_string", "wq_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(wq):
+    lib = ctypes.CDLL(wq.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(wq):
+    assert wq.status_string(0) == "ok"
+    assert "aligned" in wq.status_string(3)
+    assert wq.status_string(99) == "unknown status"
+
+
+def _rc(fn, *args):
+    return getattr(__import__("weight_only_quantized_wq_amd")._binding.lib, fn)(*args)
+
+
+def test_null_pointers(wq):
+    assert _rc("wq_gemv_bf16", None, BAD, 4, 64, BAD, None, None) == 1
+    assert _rc("wq_gemv_int8", BAD, BAD, None, 4, 64, BAD, None, None) == 1
+    assert _rc("wq_gemv_int4g32", BAD, BAD, None, 4, 64, BAD, None, None) == 1
+    assert _rc("wq_gemv_int4g32", BAD, BAD, BAD, 4, 64, None, None, None) == 1
+    assert _rc("wq_gemm_smallM", None, 2, BAD, BAD, 4, 64, BAD, None, None) == 1
+    assert _rc("wq_quantize_int8", None, 4, 64, BAD, BAD, None) == 1
+    assert _rc("wq_quantize_int4g32", BAD, 4, 64, None, BAD, None) == 1
+    assert _rc("moe_top2_gemv", BAD, None, 8, BAD, BAD, BAD, BAD, 64, 64, BAD, BAD, None, None, None, None) == 1
+    assert "non-null" in wq.last_error()
+
+
+def test_shape_errors(wq):
+    assert _rc("wq_gemv_int4g32", BAD, BAD, BAD, 4, 48, BAD, None, None) == 2      # k % 32
+    assert _rc("wq_gemv_int8", BAD, BAD, BAD, 4, 40, BAD, None, None) == 2         # k % 16
+    assert _rc("wq_gemv_bf16", BAD, BAD, 4, 12, BAD, None, None) == 2              # k % 8
+    assert _rc("wq_gemv_bf16", BAD, BAD, -1, 16, BAD, None, None) == 2             # n < 0
+    assert _rc("wq_gemm_smallM", BAD, 0, BAD, BAD, 4, 64, BAD, None, None) == 2    # m = 0
+    assert _rc("wq_gemm_smallM", BAD, 9, BAD, BAD, 4, 64, BAD, None, None) == 2    # m = 9
+    assert _rc("wq_quantize_int4g32", BAD, 4, 40, BAD, BAD, None) == 2
+    assert _rc("wq_quantize_int8", BAD, 4, 6, BAD, BAD, None) == 2
+    assert _rc("moe_top2_gemv", BAD, BAD, 4, BAD, BAD, BAD, BAD, 64, 64, BAD, BAD, None, None, None, None) == 2
+    assert _rc("moe_top2_gemv", BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 40, BAD, BAD, None, None, None, None) == 2
+    assert "multiple" in wq.last_error() or "16" in wq.last_error()
+
+
+def test_alignment_errors_before_any_launch(wq):
+    # n = 0: even a missing alignment check would return without launching
+    assert _rc("wq_gemv_int4g32", BAD, 0x2000, 0x2000, 0, 64, 0x2000, None, None) == 3
+    assert _rc("wq_gemv_bf16", 0x2000, BAD, 0, 64, 0x2000, None, None) == 3
+    assert _rc("wq_gemv_int8", 0x2000, BAD, 0x2000, 0, 64, 0x2000, None, None) == 3
+    assert _rc("wq_quantize_int4g32", BAD, 0, 64, 0x2000, 0x2000, None) == 3
+    assert "aligned" in wq.last_error()
+
+
+def test_python_binding_rejects_host_tensors(wq):
+    import torch
+    x = torch.zeros(64, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        wq.wq_gemv_bf16(x, x, 1, 64, x, None, stream=0)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    import importlib.util
+    src = os.path.join(ROOT, "weight_only_quantized_wq_amd", "_binding.py")
+    spec = importlib.util.spec_from_file_location("wq_binding_copy", src)
+    mod = importlib.util.module_from_spec(spec)
+    monkeypatch.setattr(os.path, "exists", lambda p: False if p.endswith("libwq.so") else os.path.isfile(p))
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)

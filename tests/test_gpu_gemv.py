@@ -1,0 +1,184 @@
+"""GPU decode matvecs (bf16, int8, int4 G=32, small-M verify) vs the oracle.
+
+Quantized weights come from the ORACLE's quantizers (host), so these tests
+check the matvec kernels alone.  Shapes span every launch plan (one wave per
+row up to 16 waves per row), several row batches and ragged tails in both N
+and the per-wave chunk coverage of K; K = 0 and N = 1 are included.  fp32
+outputs must be within 2e-3 and bf16 outputs within 1e-2 (max-norm relative
+error against the fp64 oracle); repeated calls must be bitwise identical and
+must not write outside the output.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import (dev, host, host_u16, guarded, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say)
+from oracle.bf16 import round_f32_to_bf16
+from oracle.quant import quantize_int8, quantize_int4g32
+from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
+from synth.gen import host_normal, host_bf16_normal
+
+pytestmark = pytest.mark.gpu
+SENT = -12345.0
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_quantized_wq_amd as m
+    return m
+
+
+def _d(a):
+    """Upload; an empty array becomes a small zero buffer (k = 0 still needs
+    valid, aligned pointers)."""
+    if a.size == 0:
+        return dev(np.zeros(64, a.dtype))
+    return dev(a)
+
+
+def _outputs(n, m=1):
+    import torch
+    b32, y32 = guarded(m * n, torch.float32, SENT)
+    b16, y16 = guarded(m * n, torch.int16, 0x7BAD)
+    return (b32, y32), (b16, y16)
+
+
+def _check_guards(b32, b16, n):
+    h32 = host(b32)
+    h16 = host(b16)
+    assert np.all(h32[:64] == SENT) and np.all(h32[64 + n:] == SENT)
+    assert np.all(h16[:64] == 0x7BAD) and np.all(h16[64 + n:] == 0x7BAD)
+
+
+def _compare(y32, y16, ref, shape):
+    got32 = host(y32).reshape(shape)
+    got16 = bf16_bits_to_f64(host_u16(y16)).reshape(shape)
+    e32 = rel_err(got32, ref)
+    e16 = rel_err(got16, ref)
+    assert e32 <= TOL_F32, e32
+    assert e16 <= TOL_BF16, e16
+    # the bf16 output is the fp32 output rounded to nearest-even
+    assert np.array_equal(host_u16(y16), round_f32_to_bf16(host(y32)))
+    return e32, e16
+
+
+BF16_SHAPES = [(37, 8), (5, 1024), (300, 4096), (129, 3584), (40, 11008), (33, 14336), (9, 28672),
+               (3, 65536), (1, 4096), (7, 0)]
+
+
+@pytest.mark.parametrize("n,k", BF16_SHAPES)
+def test_gemv_bf16(wq, n, k):
+    say(f"gemv_bf16 n={n} k={k}")
+    w = round_f32_to_bf16(host_normal((n, k), 0.02, 920, n, k, 0))
+    x = host_bf16_normal((k,), 920, n, k, 1)
+    ref = gemv_bf16(x, w)
+    (b32, y32), (b16, y16) = _outputs(n)
+    wd, xd = _d(w), _d(x)
+    wq.wq_gemv_bf16(xd, wd, n, k, y32, y16)
+    e = _compare(y32, y16, ref, (n,))
+    _check_guards(b32, b16, n)
+    first = host(y32).copy()
+    wq.wq_gemv_bf16(xd, wd, n, k, y32, y16)
+    assert np.array_equal(host(y32), first)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+INT8_SHAPES = [(37, 16), (5, 1024), (300, 4096), (129, 4112), (40, 11008), (33, 14336), (9, 28672),
+               (3, 65536), (1, 4096), (7, 0)]
+
+
+@pytest.mark.parametrize("n,k", INT8_SHAPES)
+def test_gemv_int8(wq, n, k):
+    say(f"gemv_int8 n={n} k={k}")
+    w = host_normal((n, k), 0.02, 930, n, k, 0)
+    q, s = quantize_int8(w)
+    x = host_bf16_normal((k,), 930, n, k, 1)
+    ref = gemv_int8(x, q, s)
+    (b32, y32), (b16, y16) = _outputs(n)
+    qd, sd, xd = _d(q), _d(s), _d(x)
+    wq.wq_gemv_int8(xd, qd, sd, n, k, y32, y16)
+    e = _compare(y32, y16, ref, (n,))
+    _check_guards(b32, b16, n)
+    first = host(y32).copy()
+    wq.wq_gemv_int8(xd, qd, sd, n, k, y32, None)
+    assert np.array_equal(host(y32), first)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+INT4_SHAPES = [(37, 32), (5, 1024), (300, 4096), (129, 8192), (40, 11008), (33, 14336), (17, 28672),
+               (9, 57344), (2, 131072), (1, 4096), (7, 0)]
+
+
+@pytest.mark.parametrize("n,k", INT4_SHAPES)
+def test_gemv_int4g32(wq, n, k):
+    say(f"gemv_int4g32 n={n} k={k}")
+    w = host_normal((n, k), 0.02, 940, n, k, 0)
+    p, sz = quantize_int4g32(w) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0, 2), np.uint16))
+    x = host_bf16_normal((k,), 940, n, k, 1)
+    ref = gemv_int4g32(x, p, sz)
+    (b32, y32), (b16, y16) = _outputs(n)
+    pd, szd, xd = _d(p), _d(sz), _d(x)
+    wq.wq_gemv_int4g32(xd, pd, szd, n, k, y32, y16)
+    e = _compare(y32, y16, ref, (n,))
+    _check_guards(b32, b16, n)
+    first = host(y32).copy()
+    wq.wq_gemv_int4g32(xd, pd, szd, n, k, y32, None)
+    assert np.array_equal(host(y32), first)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+SMALLM_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 32), (70, 8192)]] + \
+    [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 4, 5)] + [(5, 8, 32768), (1, 10, 131072)]
+
+
+@pytest.mark.parametrize("m,n,k", SMALLM_CASES)
+def test_gemm_small_m(wq, m, n, k):
+    say(f"gemm_smallM m={m} n={n} k={k}")
+    w = host_normal((n, k), 0.015, 950, m, n, k)
+    p, sz = quantize_int4g32(w)
+    x = host_bf16_normal((m, k), 950, m, n, k + 1)
+    ref = gemm_small_m(x, p, sz)
+    (b32, y32), (b16, y16) = _outputs(n, m)
+    pd, szd, xd = dev(p), dev(sz), dev(x)
+    wq.wq_gemm_smallM(xd, m, pd, szd, n, k, y32, y16)
+    e = _compare(y32, y16, ref, (m, n))
+    _check_guards(b32, b16, m * n)
+    # each token row matches the single-token matvec
+    import torch
+    one = torch.empty(n, dtype=torch.float32, device="cuda")
+    got = host(y32).reshape(m, n)
+    for i in range(m):
+        wq.wq_gemv_int4g32(xd[i * k:(i + 1) * k] if xd.dim() == 1 else xd[i], pd, szd, n, k, one, None)
+        assert rel_err(host(one), got[i]) <= 1e-5
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+def test_n_zero_is_noop(wq):
+    import torch
+    y = torch.full((4,), SENT, dtype=torch.float32, device="cuda")
+    x = torch.zeros(64, dtype=torch.int16, device="cuda")
+    w = torch.zeros(64 * 4, dtype=torch.int16, device="cuda")
+    sz = torch.zeros(16, dtype=torch.int16, device="cuda")
+    wq.wq_gemv_bf16(x, w, 0, 64, y, None)
+    wq.wq_gemv_int8(x, w, sz, 0, 64, y, None)
+    wq.wq_gemv_int4g32(x, w, sz, 0, 64, y, None)
+    wq.wq_gemm_smallM(x, 1, w, sz, 0, 64, y, None)
+    torch.cuda.synchronize()
+    assert np.all(host(y) == SENT)
+
+
+def test_misaligned_pointers_rejected(wq):
+    import torch
+    x = torch.zeros(256, dtype=torch.int16, device="cuda")
+    w = torch.zeros(4096, dtype=torch.int16, device="cuda")
+    sz = torch.zeros(64, dtype=torch.int16, device="cuda")
+    y = torch.zeros(16, dtype=torch.float32, device="cuda")
+    bad = x.data_ptr() + 2
+    for call in (lambda: wq.wq_gemv_bf16(bad, w, 4, 64, y, None),
+                 lambda: wq.wq_gemv_int8(bad, w, sz, 4, 64, y, None),
+                 lambda: wq.wq_gemv_int4g32(bad, w, sz, 4, 64, y, None),
+                 lambda: wq.wq_gemm_smallM(bad, 2, w, sz, 4, 64, y, None),
+                 lambda: wq.wq_gemv_int4g32(x, w, sz.data_ptr() + 2, 4, 64, y, None)):
+        with pytest.raises(wq.WQError) as ei:
+            call()
+        assert ei.value.status == 3

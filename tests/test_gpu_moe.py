@@ -1,0 +1,145 @@
+"""GPU top-2 MoE decode step vs the oracle.
+
+Small and ragged shapes with oracle-quantized experts, the full Mixtral-8x7B
+expert shape (dim 4096, ffn 14336, 8 experts) with seeded random int8 codes
+and bf16 row scales, routing ties, identical experts, and the check that the
+unselected experts' weights are never read (they hold codes that would change
+the result).
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import dev, host, host_u16, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say
+from oracle.bf16 import round_f32_to_bf16
+from oracle.quant import quantize_int8
+from oracle.moe import moe_top2, route_top2
+from synth.gen import host_normal, host_bf16_normal, host_logits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wq():
+    import weight_only_quantized_wq_amd as m
+    return m
+
+
+def _experts(e, dim, f, seed):
+    q13, s13, q2, s2 = [], [], [], []
+    for i in range(e):
+        a, b = quantize_int8(host_normal((2 * f, dim), 0.02, 960, seed, i, 0))
+        c, d = quantize_int8(host_normal((dim, f), 0.02, 960, seed, i, 1))
+        q13.append(a), s13.append(b), q2.append(c), s2.append(d)
+    return np.stack(q13), np.stack(s13), np.stack(q2), np.stack(s2)
+
+
+def _run(wq, x, logits, q13, s13, q2, s2, dim, f):
+    import torch
+    work = torch.empty(2 * f, dtype=torch.float32, device="cuda")
+    y32 = torch.empty(dim, dtype=torch.float32, device="cuda")
+    y16 = torch.empty(dim, dtype=torch.int16, device="cuda")
+    sel = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    gates = torch.zeros(2, dtype=torch.float32, device="cuda")
+    wq.moe_top2_gemv(dev(x), dev(logits), 8, dev(q13), dev(s13), dev(q2), dev(s2), dim, f, work, y32, y16,
+                     sel, gates)
+    return host(y32), host_u16(y16), tuple(host(sel).tolist()), host(gates)
+
+
+def _check(got32, got16, ref):
+    e32 = rel_err(got32, ref)
+    e16 = rel_err(bf16_bits_to_f64(got16), ref)
+    assert e32 <= TOL_F32, e32
+    assert e16 <= TOL_BF16, e16
+    assert np.array_equal(got16, round_f32_to_bf16(got32))
+    return e32, e16
+
+
+@pytest.mark.parametrize("dim,f,seed", [(64, 128, 0), (1024, 2816, 1), (4096, 512, 2), (48, 4096, 3)])
+def test_moe_oracle_quantized(wq, dim, f, seed):
+    say(f"moe dim={dim} f={f}")
+    q13, s13, q2, s2 = _experts(8, dim, f, seed)
+    x = host_bf16_normal((dim,), 961, seed, 0, 1)
+    logits = host_logits(8, 961, seed, 0, 2)
+    ref, sel_ref, g_ref = moe_top2(x, logits, q13, s13, q2, s2)
+    y32, y16, sel, gates = _run(wq, x, logits, q13, s13, q2, s2, dim, f)
+    assert sel == tuple(sel_ref)
+    assert np.allclose(gates, g_ref, rtol=2e-6, atol=0)
+    e = _check(y32, y16, ref)
+    say(f"  sel={sel} err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+def test_moe_ties_and_identical_experts(wq):
+    dim, f = 64, 96
+    q13, s13, q2, s2 = _experts(1, dim, f, 7)
+    Q13, S13 = np.repeat(q13, 8, 0), np.repeat(s13, 8, 0)
+    Q2, S2 = np.repeat(q2, 8, 0), np.repeat(s2, 8, 0)
+    x = host_bf16_normal((dim,), 962, 0, 0, 1)
+    y0, _, sel0, g0 = _run(wq, x, np.zeros(8, np.float32), Q13, S13, Q2, S2, dim, f)
+    assert sel0 == (0, 1) and np.all(g0 == 0.5)
+    logits = np.array([0.5, 2.0, -1.0, 2.0, 2.0, 0.0, 1.0, 1.5], np.float32)
+    y1, _, sel1, _ = _run(wq, x, logits, Q13, S13, Q2, S2, dim, f)
+    assert sel1 == (1, 3)
+    ref, _, _ = moe_top2(x, logits, Q13, S13, Q2, S2)
+    _check(y1, round_f32_to_bf16(y1), ref)
+    assert rel_err(y1, y0) <= 1e-5
+
+
+def test_moe_full_mixtral_shape_unselected_not_read(wq):
+    import torch
+    dim, f, e = 4096, 14336, 8
+    say("moe full mixtral shape")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(963)
+    q13 = torch.randint(-127, 128, (e, 2 * f, dim), generator=g, device="cuda", dtype=torch.int32).to(torch.int8)
+    q2 = torch.randint(-127, 128, (e, dim, f), generator=g, device="cuda", dtype=torch.int32).to(torch.int8)
+    s13 = (torch.rand((e, 2 * f), generator=g, device="cuda") + 0.5) * 1.5e-4
+    s2 = (torch.rand((e, dim), generator=g, device="cuda") + 0.5) * 1.5e-4
+    s13b = s13.to(torch.bfloat16).view(torch.int16).contiguous()
+    s2b = s2.to(torch.bfloat16).view(torch.int16).contiguous()
+    x = host_bf16_normal((dim,), 963, 0, 0, 1)
+    logits = host_logits(8, 963, 0, 0, 2)
+    (a, b), _ = route_top2(logits)
+    # unselected experts: codes that would change y if read
+    for i in range(e):
+        if i not in (a, b):
+            q13[i].fill_(127)
+            q2[i].fill_(-127)
+    work = torch.empty(2 * f, dtype=torch.float32, device="cuda")
+    y32 = torch.empty(dim, dtype=torch.float32, device="cuda")
+    sel = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    wq.moe_top2_gemv(dev(x), dev(logits), e, q13, s13b, q2, s2b, dim, f, work, y32, None, sel, None)
+    got = host(y32)
+    assert tuple(host(sel).tolist()) == (a, b)
+    # oracle on the two selected experts only (the others are zero-filled on the host)
+    Q13 = np.zeros((e, 2 * f, dim), np.int8)
+    Q2 = np.zeros((e, dim, f), np.int8)
+    S13 = host_u16(s13b)
+    S2 = host_u16(s2b)
+    for i in (a, b):
+        Q13[i] = host(q13[i])
+        Q2[i] = host(q2[i])
+    ref, sel_ref, _ = moe_top2(x, logits, Q13, S13, Q2, S2)
+    assert tuple(sel_ref) == (a, b)
+    e32 = rel_err(got, ref)
+    say(f"  sel={(a, b)} err f32={e32:.2e}")
+    assert e32 <= TOL_F32
+    # deterministic
+    y2 = torch.empty(dim, dtype=torch.float32, device="cuda")
+    wq.moe_top2_gemv(dev(x), dev(logits), e, q13, s13b, q2, s2b, dim, f, work, y2, None, None, None)
+    assert np.array_equal(host(y2), got)
+
+
+def test_moe_argument_errors(wq):
+    import torch
+    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    with pytest.raises(wq.WQError) as ei:
+        wq.moe_top2_gemv(buf, buf, 4, buf, buf, buf, buf, 64, 64, buf, y)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.moe_top2_gemv(buf.data_ptr() + 2, buf, 8, buf, buf, buf, buf, 64, 64, buf, y)
+    assert ei.value.status == 3
+    with pytest.raises(wq.WQError) as ei:
+        wq.moe_top2_gemv(buf, buf, 8, buf, buf, buf, buf, 64, 40, buf, y)
+    assert ei.value.status == 2

@@ -1,0 +1,130 @@
+"""ctypes binding of libwq (argument marshalling only).
+
+Each function has the name and argument order of the C entry point declared
+in include/wq.h.  Buffers are torch tensors on the GPU (or raw device
+addresses as ints, or None for a nullable pointer); sizes are ints; `stream`
+defaults to torch's current stream on the current device.  Every step of the
+computation runs in the HIP library; a non-OK status raises WQError.
+
+The library is loaded from this package directory (built in-tree by
+``weight_only_quantized_wq_amd.build``).  Loading fails loudly if it is
+missing: there is no fallback implementation.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "wq_quantize_int8": [_P, _I64, _I64, _P, _P, _P],
+    "wq_quantize_int4g32": [_P, _I64, _I64, _P, _P, _P],
+    "wq_gemv_bf16": [_P, _P, _I64, _I64, _P, _P, _P],
+    "wq_gemv_int8": [_P, _P, _P, _I64, _I64, _P, _P, _P],
+    "wq_gemv_int4g32": [_P, _P, _P, _I64, _I64, _P, _P, _P],
+    "wq_gemm_smallM": [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P],
+    "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
+}
+
+WQ_STATUS = {0: "WQ_OK", 1: "WQ_ERR_NULL", 2: "WQ_ERR_SHAPE", 3: "WQ_ERR_ALIGN", 4: "WQ_ERR_DEVICE",
+             5: "WQ_ERR_LAUNCH"}
+
+
+class WQError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.fn = fn
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{fn}: {WQ_STATUS.get(status, status)}: {detail}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libwq.so not found at {LIB_PATH}; build it first with "
+            "`python -m weight_only_quantized_wq_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.wq_status_string.argtypes = [ctypes.c_int]
+    lib.wq_status_string.restype = ctypes.c_char_p
+    lib.wq_last_error.argtypes = []
+    lib.wq_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def _ptr(t):
+    """Device address of a tensor (or None / int passthrough)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("libwq buffers must be GPU tensors (device memory)")
+    if not t.is_contiguous():
+        raise ValueError("libwq buffers must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(name, *args):
+    rc = getattr(lib, name)(*args)
+    if rc != 0:
+        raise WQError(name, rc, lib.wq_last_error().decode(errors="replace"))
+
+
+def status_string(status):
+    return lib.wq_status_string(int(status)).decode()
+
+
+def last_error():
+    return lib.wq_last_error().decode(errors="replace")
+
+
+def wq_quantize_int8(w, n, k, q, scale, stream=None):
+    _call("wq_quantize_int8", _ptr(w), n, k, _ptr(q), _ptr(scale), _stream(stream))
+
+
+def wq_quantize_int4g32(w, n, k, qpacked, sz, stream=None):
+    _call("wq_quantize_int4g32", _ptr(w), n, k, _ptr(qpacked), _ptr(sz), _stream(stream))
+
+
+def wq_gemv_bf16(x, w, n, k, y_f32=None, y_bf16=None, stream=None):
+    _call("wq_gemv_bf16", _ptr(x), _ptr(w), n, k, _ptr(y_f32), _ptr(y_bf16), _stream(stream))
+
+
+def wq_gemv_int8(x, q, scale, n, k, y_f32=None, y_bf16=None, stream=None):
+    _call("wq_gemv_int8", _ptr(x), _ptr(q), _ptr(scale), n, k, _ptr(y_f32), _ptr(y_bf16), _stream(stream))
+
+
+def wq_gemv_int4g32(x, qpacked, sz, n, k, y_f32=None, y_bf16=None, stream=None):
+    _call("wq_gemv_int4g32", _ptr(x), _ptr(qpacked), _ptr(sz), n, k, _ptr(y_f32), _ptr(y_bf16),
+          _stream(stream))
+
+
+def wq_gemm_smallM(x, m, qpacked, sz, n, k, y_f32=None, y_bf16=None, stream=None):
+    _call("wq_gemm_smallM", _ptr(x), m, _ptr(qpacked), _ptr(sz), n, k, _ptr(y_f32), _ptr(y_bf16),
+          _stream(stream))
+
+
+def moe_top2_gemv(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32=None, y_bf16=None, sel=None,
+                  gates=None, stream=None):
+    _call("moe_top2_gemv", _ptr(x), _ptr(logits), e, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), dim, f,
+          _ptr(work), _ptr(y_f32), _ptr(y_bf16), _ptr(sel), _ptr(gates), _stream(stream))

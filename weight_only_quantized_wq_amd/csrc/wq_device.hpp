@@ -1,0 +1,86 @@
+// Device helpers shared by the libwq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t pair) {
+  return __uint_as_float(pair & 0xFFFF0000u);
+}
+
+// fp32 -> bf16, round to nearest, ties to even.  Adding 0x7FFF plus the kept
+// part's lowest bit and truncating rounds the dropped half correctly; a
+// carry into the exponent is the correctly rounded result.  NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming loads: weights are read exactly once per product, so they are
+// fetched with the nontemporal hint and do not displace x or other data.
+
+__device__ __forceinline__ u32x4 load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ uint32_t load_stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Packed bf16 dot: a.lo*b.lo + a.hi*b.hi + c in fp32 (v_dot2_f32_bf16).
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                         false);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide sum with DPP.  Quad butterflies, then the half-row and row
+// mirrors make every lane hold its 16-lane row's sum; two row broadcasts
+// fold rows 0+1 and 2+3 and then the halves; lane 63 ends with the total,
+// which is read back as a wave-uniform value.  The order of additions is
+// fixed, so the result is deterministic.
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);          // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);          // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);         // row_half_mirror
+  v += dpp_f<0x140>(v);         // row_mirror
+  v += dpp_f<0x142, 0xA>(v);    // row_bcast15 into rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);    // row_bcast31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wave-wide maximum of non-negative values (rows the broadcasts skip see 0).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  v = fmaxf(v, dpp_f<0x142, 0xA>(v));
+  v = fmaxf(v, dpp_f<0x143, 0xC>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+}  // namespace wq

@@ -1,0 +1,188 @@
+// Streaming matvec kernel template shared by every weight format.
+//
+// Work decomposition (one launch per weight matrix):
+//   * a row of W is `chunks` 16-byte chunks; lane l of a wave owns chunks
+//     (ks * CPL + j) * 64 + l, j < CPL, of every row it visits, so each
+//     wave-wide load is 1 KiB of one row, contiguous;
+//   * `split` waves (ks = 0 .. split-1) cover one row together when a row has
+//     more chunks than one wave can hold activations for (split-K); their
+//     partial sums meet in LDS in a fixed order;
+//   * a workgroup holds `groups` such wave teams; each team takes U rows per
+//     batch, and workgroups stride over batches;
+//   * the activations of a lane's chunks are loaded once into registers and
+//     reused for every row (they are the same for all rows of W);
+//   * with PF, the next batch's weights are requested before the current one
+//     is reduced (two register buffers), and the first batch is requested
+//     before the activations are staged, so HBM requests stay in flight
+//     through the arithmetic;
+//   * per row: fp32 accumulation per lane, a DPP wave reduction, the split-K
+//     sum through LDS, then the epilogue (row scale for int8, fp32 and/or
+//     bf16 stores).
+// No atomics: every output is reduced in one fixed order, so results are
+// bitwise reproducible.
+#pragma once
+
+#include <stdint.h>
+
+#include "wq_formats.hpp"
+
+namespace wq {
+
+struct GemvArgs {
+  const uint16_t* x;      // [m][k] bf16
+  const uint8_t* w;       // n rows of row_bytes
+  const uint16_t* scale;  // int8: [n] bf16 row scales
+  const uint32_t* sz;     // int4: [n][chunks] (scale | zero << 16)
+  float* y32;             // [m][n] or null
+  uint16_t* y16;          // [m][n] or null
+  int64_t n;
+  int64_t k;
+  int64_t row_bytes;
+  int64_t batches;
+  int32_t chunks;
+  int32_t split;
+  int32_t groups;
+};
+
+template <class F, int U, int CPL>
+struct Batch {
+  u32x4 w[U][CPL];
+  uint32_t aux[U][CPL];
+};
+
+// Requests batch b's weights (rows past n and chunks past the row are not
+// loaded and read as zero).
+template <class F, int U, int CPL>
+__device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg, const int (&cidx)[CPL],
+                                           const bool (&cok)[CPL], Batch<F, U, CPL>& bt) {
+  const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = r0 + u;
+    const bool row_ok = r < a.n;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const bool ok = row_ok && cok[j];
+      bt.w[u][j] = ok ? load_stream16(a.w + r * a.row_bytes + (int64_t)cidx[j] * 16) : u32x4{0, 0, 0, 0};
+      if constexpr (F::kGroupAux) bt.aux[u][j] = ok ? load_stream4(a.sz + r * a.chunks + cidx[j]) : 0u;
+      else bt.aux[u][j] = 0u;
+    }
+  }
+}
+
+// Reduces batch b (already loaded) and writes its outputs.
+template <class F, int M, int CPL, int U, int WAVES>
+__device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int lane, int wave, int ks, int rg,
+                                             const Batch<F, U, CPL>& bt, const typename F::X (&xr)[M][CPL],
+                                             const float (&bias)[M], float (&red)[2][WAVES][U * M], int& buf) {
+  const int S = a.split;
+  const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
+  float acc[U][M];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[u][m] = bias[m];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      typename F::D d;
+      F::decode(bt.w[u][j], d);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[u][m] = F::dot(d, bt.aux[u][j], xr[m][j], acc[u][m]);
+    }
+  }
+
+  float tot[U * M];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int m = 0; m < M; ++m) tot[u * M + m] = wave_sum(acc[u][m]);
+
+  if (S > 1) {
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < U * M; ++i) red[buf][wave][i] = tot[i];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int i = 0; i < U * M; ++i) {
+        float v = red[buf][rg * S][i];
+        for (int s = 1; s < S; ++s) v += red[buf][rg * S + s][i];
+        tot[i] = v;
+      }
+    }
+    buf ^= 1;
+  }
+
+  if (ks == 0 && lane < U * M) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < U * M; ++i)
+      if (lane == i) v = tot[i];
+    const int u = lane / M;
+    const int m = lane - u * M;
+    const int64_t r = r0 + u;
+    if (r < a.n) {
+      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)a.scale[r] << 16);
+      if (a.y32) a.y32[m * a.n + r] = v;
+      if (a.y16) a.y16[m * a.n + r] = f32_to_bf16(v);
+    }
+  }
+}
+
+template <class F, int M, int CPL, int U, int WAVES, bool PF>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int ks = wave % a.split;
+  const int rg = wave / a.split;
+
+  int cidx[CPL];
+  bool cok[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    cidx[j] = (ks * CPL + j) * kWave + lane;
+    cok[j] = cidx[j] < a.chunks;
+  }
+
+  int64_t b = blockIdx.x;
+  const int64_t step = gridDim.x;
+  Batch<F, U, CPL> A;
+  load_batch<F, U, CPL>(a, b, rg, cidx, cok, A);
+
+  typename F::X xr[M][CPL];
+  float bias[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    bias[m] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      xr[m][j] = F::load_x(a.x + m * a.k, cidx[j], cok[j]);
+      bias[m] += F::lane_bias(xr[m][j]);
+    }
+  }
+
+  __shared__ float red[2][WAVES][U * M];
+  int buf = 0;
+
+  if constexpr (PF) {
+    Batch<F, U, CPL> B;
+    while (b < a.batches) {
+      load_batch<F, U, CPL>(a, b + step, rg, cidx, cok, B);
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, red, buf);
+      b += step;
+      if (b >= a.batches) break;
+      load_batch<F, U, CPL>(a, b + step, rg, cidx, cok, A);
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, red, buf);
+      b += step;
+    }
+  } else {
+    while (b < a.batches) {
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, red, buf);
+      b += step;
+      if (b < a.batches) load_batch<F, U, CPL>(a, b, rg, cidx, cok, A);
+    }
+  }
+}
+
+}  // namespace wq

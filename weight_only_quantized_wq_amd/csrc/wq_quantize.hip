@@ -1,0 +1,185 @@
+// Offline quantizers: fp32 weights -> int8 per-row / int4 G=32 codes.
+//
+// Codes are round-half-even of the EXACT real quotient, so the device must
+// take the same decision as exact arithmetic even when an fp32 quotient
+// lands within rounding of a half-integer.  A candidate code c comes from an
+// fp64 quotient; it is then confirmed or moved by exact comparisons of w
+// against the decision boundaries z + (c +- 1/2) s:
+//   * (c +- 1/2) s is exact in fp64 (a <= 8-bit integer-and-a-half times an
+//     8-bit bf16 significand);
+//   * w - z is formed with TwoSum, so d + e == w - z exactly; rounding is
+//     monotone, hence d > p implies w - z > p, d < p implies w - z < p, and
+//     when d == p the sign of (w - z) - p is the sign of e.
+// An exact tie goes to the even code.
+#include <stdint.h>
+
+#include "wq_device.hpp"
+#include "wq_host.hpp"
+
+namespace wq {
+
+// sign((w - z) - p) computed exactly (w, z, p are exact fp64 values)
+__device__ __forceinline__ int cmp_diff(double w, double z, double p) {
+  double d = w - z;
+  double bb = d - w;
+  double e = (w - (d - bb)) + (-z - bb);
+  if (d > p) return 1;
+  if (d < p) return -1;
+  return (e > 0.0) - (e < 0.0);
+}
+
+// round-half-even of the exact (w - z) / s for s > 0, starting from a
+// candidate within a few units of the answer.
+__device__ __forceinline__ int rne_code(double w, double z, double s, int c) {
+  for (int it = 0; it < 6; ++it) {
+    int up = cmp_diff(w, z, ((double)c + 0.5) * s);
+    if (up > 0 || (up == 0 && (c & 1))) {
+      ++c;
+      continue;
+    }
+    int dn = cmp_diff(w, z, ((double)c - 0.5) * s);
+    if (dn < 0 || (dn == 0 && (c & 1))) {
+      --c;
+      continue;
+    }
+    break;
+  }
+  return c;
+}
+
+__device__ __forceinline__ int candidate(double w, double z, double s, int lo, int hi) {
+  double r = rint((w - z) / s);
+  if (!(r >= (double)lo)) r = (double)lo;   // also catches NaN
+  if (r > (double)hi) r = (double)hi;
+  return (int)r;
+}
+
+// ---------------------------------------------------------------------------
+// int8: one wave per row.
+
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                            int8_t* __restrict__ q, uint16_t* __restrict__ scale) {
+  const int lane = lane_id();
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  const int64_t k4 = k / 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < n; r += waves) {
+    const float4* row = reinterpret_cast<const float4*>(w + r * k);
+    float m = 0.0f;
+    for (int64_t i = lane; i < k4; i += kWave) {
+      float4 v = row[i];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    m = wave_max_nonneg(m);
+    const uint16_t sb = f32_to_bf16(__fdiv_rn(m, 127.0f));
+    const double s = (double)__uint_as_float((uint32_t)sb << 16);
+    if (lane == 0) scale[r] = sb;
+    uint32_t* qrow = reinterpret_cast<uint32_t*>(q + r * k);
+    for (int64_t i = lane; i < k4; i += kWave) {
+      float4 v = row[i];
+      float e[4] = {v.x, v.y, v.z, v.w};
+      uint32_t packed = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        int c = 0;
+        if (s > 0.0) {
+          double wd = (double)e[t];
+          c = rne_code(wd, 0.0, s, candidate(wd, 0.0, s, -200, 200));
+          c = c < -127 ? -127 : (c > 127 ? 127 : c);
+        }
+        packed |= ((uint32_t)(uint8_t)(int8_t)c) << (8 * t);
+      }
+      qrow[i] = packed;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// int4 G=32: one lane per group of 32 consecutive inputs.
+
+__global__ __launch_bounds__(256) void quantize_int4g32_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                               uint8_t* __restrict__ qpacked,
+                                                               uint32_t* __restrict__ sz) {
+  const int64_t groups_per_row = k / 32;
+  const int64_t total = n * groups_per_row;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total; gidx += stride) {
+    const int64_t r = gidx / groups_per_row;
+    const int64_t g = gidx - r * groups_per_row;
+    const float4* src = reinterpret_cast<const float4*>(w + r * k + g * 32);
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float4 t = src[i];
+      v[4 * i] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+    const uint16_t zb = f32_to_bf16(mn);
+    const float zf = __uint_as_float((uint32_t)zb << 16);
+    const float t = __fsub_rn(mx, zf);
+    const uint16_t sb = t > 0.0f ? f32_to_bf16(__fdiv_rn(t, 15.0f)) : (uint16_t)0;
+    const double s = (double)__uint_as_float((uint32_t)sb << 16);
+    const double z = (double)zf;
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    if (s > 0.0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double wd = (double)v[i];
+        int c = rne_code(wd, z, s, candidate(wd, z, s, -64, 64));
+        c = c < 0 ? 0 : (c > 15 ? 15 : c);
+        words[i >> 3] |= (uint32_t)c << (4 * (i & 7));
+      }
+    }
+    u32x4 out = {words[0], words[1], words[2], words[3]};
+    *reinterpret_cast<u32x4*>(qpacked + r * (k / 2) + g * 16) = out;
+    sz[gidx] = (uint32_t)sb | ((uint32_t)zb << 16);
+  }
+}
+
+}  // namespace wq
+
+using namespace wq;
+
+extern "C" int wq_quantize_int8(const float* w, int64_t n, int64_t k, int8_t* q, uint16_t* scale, void* stream) {
+  const char* name = "wq_quantize_int8";
+  if (!w || !q || !scale) return fail(WQ_ERR_NULL, "%s: w, q and scale must be non-null", name);
+  if (n < 0 || k < 0 || k % 4) return fail(WQ_ERR_SHAPE, "%s: need n, k >= 0 and k %% 4 == 0 (n = %lld, k = %lld)", name, (long long)n, (long long)k);
+  if (!aligned16(w) || (reinterpret_cast<uintptr_t>(q) & 3u) || (reinterpret_cast<uintptr_t>(scale) & 1u))
+    return fail(WQ_ERR_ALIGN, "%s: w must be 16-byte, q 4-byte and scale 2-byte aligned", name);
+  if (n == 0) return WQ_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  static int resident = 0;
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int8_kernel), 256);
+  int64_t grid = balanced_grid((n + 3) / 4, resident);
+  hipLaunchKernelGGL(quantize_int8_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, n, k, q,
+                     scale);
+  return launch_status(name);
+}
+
+extern "C" int wq_quantize_int4g32(const float* w, int64_t n, int64_t k, uint8_t* qpacked, uint16_t* sz,
+                                   void* stream) {
+  const char* name = "wq_quantize_int4g32";
+  if (!w || !qpacked || !sz) return fail(WQ_ERR_NULL, "%s: w, qpacked and sz must be non-null", name);
+  if (n < 0 || k < 0 || k % 32)
+    return fail(WQ_ERR_SHAPE, "%s: need n, k >= 0 and k %% 32 == 0 (n = %lld, k = %lld)", name, (long long)n, (long long)k);
+  if (!aligned16(w) || !aligned16(qpacked) || (reinterpret_cast<uintptr_t>(sz) & 3u))
+    return fail(WQ_ERR_ALIGN, "%s: w and qpacked must be 16-byte and sz 4-byte aligned", name);
+  if (n == 0 || k == 0) return WQ_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  static int resident = 0;
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int4g32_kernel), 256);
+  int64_t blocks = (n * (k / 32) + 255) / 256;
+  int64_t grid = balanced_grid(blocks, resident);
+  hipLaunchKernelGGL(quantize_int4g32_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, n, k,
+                     qpacked, reinterpret_cast<uint32_t*>(sz));
+  return launch_status(name);
+}

@@ -40,6 +40,29 @@ __device__ __forceinline__ uint32_t load_stream4(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
 }
 
+// Buffer resource over [base, base + bytes): loads at offsets past `bytes`
+// return zero instead of touching memory, so ragged rows and chunks need no
+// branches.  Dword 3 selects 32-bit data format (raw, untyped loads).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// cache policy 2 = nontemporal (streamed once)
+__device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ uint32_t buffer_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2);
+}
+
+// A constant held in a VGPR.  gfx9 VOP3 instructions cannot take two
+// literal/SGPR operands, so a mask used with a second constant (as in
+// v_and_or_b32) must live in a vector register for the three-operand form.
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "i"(c));
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Packed bf16 dot: a.lo*b.lo + a.hi*b.hi + c in fp32 (v_dot2_f32_bf16).
 
@@ -82,5 +105,8 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 }  // namespace wq

@@ -45,11 +45,13 @@ struct FmtBf16 {
   }
   __device__ static float lane_bias(const X&) { return 0.0f; }
 
+  struct K {};
+  __device__ static K consts() { return K{}; }
   // decoded chunk: the bf16 pairs as loaded
   struct D {
     uint32_t p[4];
   };
-  __device__ static void decode(const u32x4& w, D& d) {
+  __device__ static void decode(const u32x4& w, D& d, const K&) {
     d.p[0] = w[0];
     d.p[1] = w[1];
     d.p[2] = w[2];
@@ -108,11 +110,13 @@ struct FmtInt8 {
     return -128.0f * s;
   }
 
+  struct K {};
+  __device__ static K consts() { return K{}; }
   // decoded chunk: u = q + 128 as fp32, one per weight
   struct D {
     float u[16];
   };
-  __device__ static void decode(const u32x4& w, D& d) {
+  __device__ static void decode(const u32x4& w, D& d, const K&) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       uint32_t u = w[t] ^ 0x80808080u;
@@ -171,18 +175,24 @@ struct FmtInt4 {
   }
   __device__ static float lane_bias(const X&) { return 0.0f; }
 
+  // the nibble mask sits in a VGPR so that each pair decodes with one
+  // v_and_or_b32 (mask, then OR the bf16 128.0 exponent pattern)
+  struct K {
+    uint32_t mask;
+  };
+  __device__ static K consts() { return K{vgpr_const(0x000F000Fu)}; }
   // decoded chunk: bf16 pairs (128 + q_k, 128 + q_{k+4})
   struct D {
     uint32_t t[16];
   };
-  __device__ static void decode(const u32x4& w, D& d) {
+  __device__ static void decode(const u32x4& w, D& d, const K& k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t v = w[i];
-      d.t[4 * i + 0] = (v & 0x000F000Fu) | kMagic;
-      d.t[4 * i + 1] = ((v >> 4) & 0x000F000Fu) | kMagic;
-      d.t[4 * i + 2] = ((v >> 8) & 0x000F000Fu) | kMagic;
-      d.t[4 * i + 3] = ((v >> 12) & 0x000F000Fu) | kMagic;
+      d.t[4 * i + 0] = (v & k.mask) | kMagic;
+      d.t[4 * i + 1] = ((v >> 4) & k.mask) | kMagic;
+      d.t[4 * i + 2] = ((v >> 8) & k.mask) | kMagic;
+      d.t[4 * i + 3] = ((v >> 12) & k.mask) | kMagic;
     }
   }
   // adds the group's sum_k (z + q_k s) x_k to acc; sz word: low half =

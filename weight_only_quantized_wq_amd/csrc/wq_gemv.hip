@@ -11,61 +11,70 @@ namespace wq {
 // ---------------------------------------------------------------------------
 // Host side: plan selection and launch.
 
-using LaunchFn = int (*)(const GemvArgs&, int threads, hipStream_t);
+using LaunchFn = int (*)(const GemvArgs&, int split, hipStream_t);
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
-int launch_one(const GemvArgs& a0, int threads, hipStream_t stream) {
-  static int resident = 0;
+int launch_one(const GemvArgs& a0, int split, hipStream_t stream) {
+  static int resident_by_split[WAVES + 1] = {0};
   auto kern = gemv_kernel<F, M, CPL, U, WAVES, PF>;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
   GemvArgs a = a0;
+  a.split = split;
+  a.groups = WAVES / split;
+  const int threads = split * a.groups * kWave;
+  int& resident = resident_by_split[split];
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
+  const int64_t rows_per_batch = (int64_t)a.groups * U;
+  a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
   int64_t grid = balanced_grid(a.batches, resident);
   if (grid <= 0) return WQ_OK;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, stream, a);
   return launch_status("gemv");
 }
 
-constexpr int kU = 2;
-
-// Candidate (chunks-per-lane, waves-per-workgroup) plans per format.  A lane
-// holds CPL chunks of activations in registers; split = ceil(chunks / (64
-// CPL)) waves share a row.
-template <class F, int M>
-struct Plans;
-
-#define WQ_PLAN(CPL, WAVES) {CPL, WAVES, &launch_one<F, M, CPL, kU, WAVES, false>}
+// Launch plans.  A plan fixes the chunks of activations each lane holds
+// (CPL), the waves per workgroup, the rows per wave per batch (U) and whether
+// the next batch is prefetched (PF); the split (waves per row) follows from
+// the row length.  Each format lists its plans in order with the largest row
+// (in chunks) each should serve; the first that covers the row is used.  The
+// table was chosen by timing every candidate on the Llama-2-7B,
+// Llama-3.1-8B and Llama-3.1-70B linear shapes on MI355X.  A 4-wave
+// workgroup may use up to 512 VGPRs per lane, an 8-wave one 256 and a
+// 16-wave one 128; every plan fits its size without spilling.
 struct PlanEntry {
+  int max_chunks;
   int cpl;
   int waves;
   LaunchFn fn;
 };
 
-// A workgroup of 4 waves may use up to 512 VGPRs per lane, one of 8 waves
-// 256 and one of 16 waves 128; plans are listed only where the kernel fits
-// its workgroup size without spilling.
+#define WQ_PLAN(MAXC, CPL, WAVES, U, PF) {MAXC, CPL, WAVES, &launch_one<F, M, CPL, U, WAVES, PF>}
+
+template <class F, int M>
+struct Plans;
+
 template <>
 struct Plans<FmtBf16, 1> {
   using F = FmtBf16;
   static constexpr int M = 1;
-  static constexpr PlanEntry list[] = {WQ_PLAN(8, 4), WQ_PLAN(7, 4), WQ_PLAN(6, 4), WQ_PLAN(4, 4),
-                                       WQ_PLAN(2, 4), WQ_PLAN(8, 8), WQ_PLAN(7, 8), WQ_PLAN(6, 8),
-                                       WQ_PLAN(8, 16)};
+  static constexpr PlanEntry list[] = {WQ_PLAN(128, 2, 4, 2, true), WQ_PLAN(512, 8, 4, 1, true),
+                                       WQ_PLAN(1792, 7, 4, 1, true), WQ_PLAN(4096, 8, 8, 1, true),
+                                       WQ_PLAN(8192, 8, 16, 1, false)};
 };
 template <>
 struct Plans<FmtInt8, 1> {
   using F = FmtInt8;
   static constexpr int M = 1;
-  static constexpr PlanEntry list[] = {WQ_PLAN(4, 4), WQ_PLAN(6, 4), WQ_PLAN(7, 4), WQ_PLAN(2, 4),
-                                       WQ_PLAN(1, 4), WQ_PLAN(4, 8), WQ_PLAN(6, 8), WQ_PLAN(7, 8),
-                                       WQ_PLAN(4, 16)};
+  static constexpr PlanEntry list[] = {WQ_PLAN(64, 1, 4, 4, true), WQ_PLAN(256, 4, 4, 2, false),
+                                       WQ_PLAN(896, 7, 4, 1, true), WQ_PLAN(3584, 7, 8, 1, true),
+                                       WQ_PLAN(4096, 4, 16, 1, false)};
 };
 template <>
 struct Plans<FmtInt4, 1> {
   using F = FmtInt4;
   static constexpr int M = 1;
-  static constexpr PlanEntry list[] = {WQ_PLAN(2, 4), WQ_PLAN(4, 4), WQ_PLAN(6, 4), WQ_PLAN(7, 4),
-                                       WQ_PLAN(1, 4), WQ_PLAN(4, 8), WQ_PLAN(7, 8), WQ_PLAN(8, 8),
-                                       WQ_PLAN(2, 16)};
+  static constexpr PlanEntry list[] = {WQ_PLAN(128, 2, 4, 2, false), WQ_PLAN(384, 3, 4, 2, true),
+                                       WQ_PLAN(896, 7, 4, 1, true), WQ_PLAN(3584, 7, 8, 1, true),
+                                       WQ_PLAN(4096, 8, 8, 1, false)};
 };
 // speculative-verify rows: the activations of all M tokens stay in registers
 #define WQ_SMALLM_PLANS(MM, ...)                                             \
@@ -75,40 +84,28 @@ struct Plans<FmtInt4, 1> {
     static constexpr int M = MM;                                             \
     static constexpr PlanEntry list[] = {__VA_ARGS__};                       \
   };
-WQ_SMALLM_PLANS(2, WQ_PLAN(1, 4), WQ_PLAN(2, 4), WQ_PLAN(2, 8), WQ_PLAN(4, 8), WQ_PLAN(1, 16))
-WQ_SMALLM_PLANS(3, WQ_PLAN(1, 4), WQ_PLAN(2, 4), WQ_PLAN(2, 8), WQ_PLAN(1, 16))
-WQ_SMALLM_PLANS(4, WQ_PLAN(1, 4), WQ_PLAN(2, 4), WQ_PLAN(2, 8), WQ_PLAN(1, 16))
-WQ_SMALLM_PLANS(5, WQ_PLAN(1, 4), WQ_PLAN(1, 8), WQ_PLAN(2, 8))
-WQ_SMALLM_PLANS(6, WQ_PLAN(1, 4), WQ_PLAN(1, 8))
-WQ_SMALLM_PLANS(7, WQ_PLAN(1, 4), WQ_PLAN(1, 8))
-WQ_SMALLM_PLANS(8, WQ_PLAN(1, 4), WQ_PLAN(1, 8))
+WQ_SMALLM_PLANS(2, WQ_PLAN(1024, 2, 8, 2, false))
+WQ_SMALLM_PLANS(3, WQ_PLAN(1024, 2, 8, 2, false))
+WQ_SMALLM_PLANS(4, WQ_PLAN(1024, 2, 8, 2, false))
+WQ_SMALLM_PLANS(5, WQ_PLAN(1024, 2, 8, 2, false))
+WQ_SMALLM_PLANS(6, WQ_PLAN(512, 1, 8, 2, false))
+WQ_SMALLM_PLANS(7, WQ_PLAN(512, 1, 8, 2, false))
+WQ_SMALLM_PLANS(8, WQ_PLAN(512, 1, 8, 2, false))
 #undef WQ_SMALLM_PLANS
 #undef WQ_PLAN
 
-// Picks the plan covering `chunks` with the fewest idle lanes; ties go to the
-// plan with fewer waves per row (less cross-wave reduction), then to fewer
-// registers.  Returns false when no plan covers the row.
 template <class F, int M>
 bool choose_plan(int64_t chunks, PlanEntry& best, int& split) {
-  bool found = false;
-  int64_t best_waste = 0;
-  int best_split = 0;
   for (const PlanEntry& p : Plans<F, M>::list) {
-    int64_t per_wave = (int64_t)kWave * p.cpl;
+    if (chunks > p.max_chunks) continue;
+    const int64_t per_wave = (int64_t)kWave * p.cpl;
     int64_t s = chunks == 0 ? 1 : (chunks + per_wave - 1) / per_wave;
     if (s > p.waves) continue;
-    int64_t waste = s * per_wave - chunks;
-    bool better = !found || waste < best_waste ||
-                  (waste == best_waste && (s < best_split || (s == best_split && p.cpl < best.cpl)));
-    if (better) {
-      found = true;
-      best = p;
-      best_waste = waste;
-      best_split = (int)s;
-    }
+    best = p;
+    split = (int)s;
+    return true;
   }
-  split = best_split;
-  return found;
+  return false;
 }
 
 template <class F, int M>
@@ -117,12 +114,7 @@ int run_gemv(GemvArgs a, hipStream_t stream, const char* name) {
   int split = 0;
   if (!choose_plan<F, M>(a.chunks, p, split))
     return fail(WQ_ERR_SHAPE, "%s: k = %lld is larger than the largest supported row", name, (long long)a.k);
-  int groups = p.waves / split;
-  a.split = split;
-  a.groups = groups;
-  int64_t rows_per_batch = (int64_t)groups * kU;
-  a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
-  return p.fn(a, split * groups * kWave, stream);
+  return p.fn(a, split, stream);
 }
 
 // Host checks in a fixed order -- null pointers, then sizes, then alignment --

@@ -11,6 +11,8 @@
 //     batch, and workgroups stride over batches;
 //   * the activations of a lane's chunks are loaded once into registers and
 //     reused for every row (they are the same for all rows of W);
+//   * weights are read with buffer loads through per-row resources, so rows
+//     past n and chunks past a row's end read as zero with no branches;
 //   * with PF, the next batch's weights are requested before the current one
 //     is reduced (two register buffers), and the first batch is requested
 //     before the activations are staged, so HBM requests stay in flight
@@ -50,22 +52,28 @@ struct Batch {
   uint32_t aux[U][CPL];
 };
 
-// Requests batch b's weights (rows past n and chunks past the row are not
-// loaded and read as zero).
+// Requests batch b's weights through per-row buffer resources: a row past
+// n gets an empty resource and a chunk past the row lies past the resource's
+// end, so both read as zero without a branch.  off[j] = 16 * chunk index.
 template <class F, int U, int CPL>
-__device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg, const int (&cidx)[CPL],
-                                           const bool (&cok)[CPL], Batch<F, U, CPL>& bt) {
+__device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg, const uint32_t (&off)[CPL],
+                                           Batch<F, U, CPL>& bt) {
   const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = r0 + u;
     const bool row_ok = r < a.n;
+    const int64_t rr = row_ok ? r : 0;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rr * a.row_bytes, row_ok ? (uint32_t)a.row_bytes : 0u);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const bool ok = row_ok && cok[j];
-      bt.w[u][j] = ok ? load_stream16(a.w + r * a.row_bytes + (int64_t)cidx[j] * 16) : u32x4{0, 0, 0, 0};
-      if constexpr (F::kGroupAux) bt.aux[u][j] = ok ? load_stream4(a.sz + r * a.chunks + cidx[j]) : 0u;
-      else bt.aux[u][j] = 0u;
+    for (int j = 0; j < CPL; ++j) bt.w[u][j] = buffer_load16_nt(rw, off[j]);
+    if constexpr (F::kGroupAux) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * a.chunks, row_ok ? (uint32_t)a.chunks * 4u : 0u);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = buffer_load4_nt(rs, off[j] >> 2);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;
     }
   }
 }
@@ -74,7 +82,8 @@ __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg,
 template <class F, int M, int CPL, int U, int WAVES>
 __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int lane, int wave, int ks, int rg,
                                              const Batch<F, U, CPL>& bt, const typename F::X (&xr)[M][CPL],
-                                             const float (&bias)[M], float (&red)[2][WAVES][U * M], int& buf) {
+                                             const float (&bias)[M], const typename F::K& kc,
+                                             float (&red)[2][WAVES][U * M], int& buf) {
   const int S = a.split;
   const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
   float acc[U][M];
@@ -85,7 +94,7 @@ __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int l
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       typename F::D d;
-      F::decode(bt.w[u][j], d);
+      F::decode(bt.w[u][j], d, kc);
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[u][m] = F::dot(d, bt.aux[u][j], xr[m][j], acc[u][m]);
     }
@@ -133,22 +142,22 @@ __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int l
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int ks = wave % a.split;
   const int rg = wave / a.split;
 
   int cidx[CPL];
-  bool cok[CPL];
+  uint32_t off[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     cidx[j] = (ks * CPL + j) * kWave + lane;
-    cok[j] = cidx[j] < a.chunks;
+    off[j] = (uint32_t)cidx[j] * 16u;
   }
 
   int64_t b = blockIdx.x;
   const int64_t step = gridDim.x;
   Batch<F, U, CPL> A;
-  load_batch<F, U, CPL>(a, b, rg, cidx, cok, A);
+  load_batch<F, U, CPL>(a, b, rg, off, A);
 
   typename F::X xr[M][CPL];
   float bias[M];
@@ -157,10 +166,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
     bias[m] = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-      xr[m][j] = F::load_x(a.x + m * a.k, cidx[j], cok[j]);
+      xr[m][j] = F::load_x(a.x + m * a.k, cidx[j], cidx[j] < a.chunks);
       bias[m] += F::lane_bias(xr[m][j]);
     }
   }
+  const typename F::K kc = F::consts();
 
   __shared__ float red[2][WAVES][U * M];
   int buf = 0;
@@ -168,19 +178,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
   if constexpr (PF) {
     Batch<F, U, CPL> B;
     while (b < a.batches) {
-      load_batch<F, U, CPL>(a, b + step, rg, cidx, cok, B);
-      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, red, buf);
+      load_batch<F, U, CPL>(a, b + step, rg, off, B);
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf);
       b += step;
       if (b >= a.batches) break;
-      load_batch<F, U, CPL>(a, b + step, rg, cidx, cok, A);
-      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, red, buf);
+      load_batch<F, U, CPL>(a, b + step, rg, off, A);
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, kc, red, buf);
       b += step;
     }
   } else {
     while (b < a.batches) {
-      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, red, buf);
+      finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf);
       b += step;
-      if (b < a.batches) load_batch<F, U, CPL>(a, b, rg, cidx, cok, A);
+      if (b < a.batches) load_batch<F, U, CPL>(a, b, rg, off, A);
     }
   }
 }

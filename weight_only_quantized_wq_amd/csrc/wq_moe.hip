@@ -119,7 +119,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_kernel(MoeArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         F::D d;
-        F::decode(wv[u][j], d);
+        F::decode(wv[u][j], d, F::K{});
         acc = F::dot(d, 0u, xr[j], acc);
       }
       tot[u] = wave_sum(acc);
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_kernel(MoeArgs a) {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         F::D d;
-        F::decode(wv[u][j], d);
+        F::decode(wv[u][j], d, F::K{});
         acc = F::dot(d, 0u, xr[j], acc);
       }
       float t = wave_sum(acc);

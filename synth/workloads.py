@@ -4,7 +4,8 @@ Each workload is one batch-1 decode step (or one speculative-verify pass) of
 a model family the pages benchmark, with synthetic N(0, sigma) weights and
 N(0, 1) bf16 activations standing in for trained checkpoints:
 
-  int8-4096        one int8 per-row GEMV, W [4096, 4096] N(0, 0.02), seed 0
+  int8-4096        one int8 per-row GEMV, W [4096, 4096] N(0, 0.02), seed 0;
+                   a step sweeps 64 resident copies of it
   llama2-7b-int4   Llama-2-7B linear set, int4 G=32          (129 matvecs)
   llama2-7b-bf16 / llama2-7b-int8 / llama3.1-8b-bf16 / llama3.1-8b-int8
   llama3.1-70b-int4-m5  Llama-3.1-70B set, int4 G=32, 5 tokens per pass,
@@ -21,6 +22,9 @@ from .configs import LLAMA2_7B, LLAMA31_8B, LLAMA31_70B, MIXTRAL_8X7B, Matrix, l
 from .gen import ROLE_W, ROLE_X, ROLE_LOGITS, device_normal, device_bf16_normal, host_normal, host_bf16_normal
 
 
+COPIES = 64
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -33,7 +37,11 @@ class Workload:
 
     def matrices(self, layers=None):
         if self.model is None:
-            return [Matrix("w", 0, 0, 4096, 4096)]
+            # 64 resident copies of the one seed-0 matrix (same values, distinct
+            # addresses): 1.07 GB per sweep, so the 256 MB Infinity Cache cannot
+            # serve a repeat and every launch streams from HBM
+            n = COPIES if layers is None else 1
+            return [Matrix("w", 0, 0, 4096, 4096) for _ in range(n)]
         return linear_set(self.model, layers)
 
 

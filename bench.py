@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="llama2-7b-int4")
+    p.add_argument("--launch", choices=("fused", "per-matrix"), default="fused",
+                   help="linear sets: one persistent launch per step (default) or one launch per matrix")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-calibration", action="store_true", help="skip the 1 GiB copy used to scale PMC counters")
@@ -54,7 +56,7 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def build_workload(name):
+def build_workload(name, launch="fused"):
     import torch
     from synth.workloads import WORKLOADS, gen_w_device, gen_x_device, expert_key, logits_key, moe_x_key
     from synth.gen import device_normal, device_bf16_normal
@@ -73,9 +75,8 @@ def build_workload(name):
             return device_normal((e,), 1.0, "cuda", *logits_key(wl, layer))
         ls = MoELayerSet(mm.dim, mm.ffn, mm.experts, mm.layers, gw, gx, gl)
         launches = [("moe_top2_gemv", mm.dim, ls.bytes / mm.layers)] * mm.layers
-        return wl, ls, launches
+        return wl, ls, launches, ls.launch_layer, ls.step
     ls = LayerSet(wl.matrices(), wl.fmt, gen_w_device(wl), gen_x_device(wl), m=wl.m)
-    launches = [(f"{wl.fmt} m={q.m} k={q.k}", q.k, q.bytes) for q in ls.mats]
     if wl.model is None:
         # every copy holds the same seed-0 weights
         for q in ls.mats[1:]:
@@ -83,7 +84,12 @@ def build_workload(name):
             q.aux.copy_(ls.mats[0].aux)
             q.x.copy_(ls.mats[0].x)
     torch.cuda.synchronize()
-    return wl, ls, launches
+    if launch == "fused":
+        ls.prepare_fused()
+        launches = [(f"decode step kernel {wl.fmt} m={wl.m} ({len(ls.mats)} matrices)", 0, ls.bytes)]
+        return wl, ls, launches, lambda i: ls.step_fused(), ls.step_fused
+    launches = [(f"{wl.fmt} m={q.m} k={q.k}", q.k, q.bytes) for q in ls.mats]
+    return wl, ls, launches, lambda i: ls.mats[i].launch(), ls.step
 
 
 def copy_calibration():
@@ -121,7 +127,7 @@ def timed_steps(step, steps):
     return time.perf_counter() - t0
 
 
-def kernel_durations(ls, launches, steps):
+def kernel_durations(launch_one, launches, steps):
     """Average duration (ms) of one launch of each launch class, from HIP events.
 
     A class is one kernel configuration (format, tokens per pass, K).  The
@@ -134,7 +140,6 @@ def kernel_durations(ls, launches, steps):
     small kernels are bound by the host, not the GPU.
     """
     import torch
-    mats = getattr(ls, "mats", None)
     classes = {}
     for i, (cls, _, _) in enumerate(launches):
         classes.setdefault(cls, []).append(i)
@@ -142,10 +147,7 @@ def kernel_durations(ls, launches, steps):
     def runner(idx):
         def run():
             for i in idx:
-                if mats is not None:
-                    mats[i].launch()
-                else:
-                    ls.launch_layer(i)
+                launch_one(i)
         return run
     graphs = {c: capture(runner(idx)) for c, idx in classes.items()}
     out = {}
@@ -283,20 +285,19 @@ def main():
         sys.exit(3)
     torch.cuda.set_device(0)
     t_build = time.perf_counter()
-    wl, ls, launches = build_workload(args.workload)
+    wl, ls, launches, launch_one, step = build_workload(args.workload, args.launch)
     print(f"[bench] built {args.workload}: {len(launches)} launches, {ls.bytes / 1e9:.4f} GB/step "
           f"in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
     if not args.no_calibration:
         copy_calibration()
 
     for _ in range(args.warmup):
-        ls.step()
+        step()
     torch.cuda.synchronize()
-    eager = timed_steps(ls.step, args.steps)
-    print(f"[bench] eager launches: {eager / args.steps * 1e3:.3f} ms/step (host-bound reference)", file=sys.stderr,
-          flush=True)
+    eager = timed_steps(step, args.steps)
+    print(f"[bench] eager launches: {eager / args.steps * 1e3:.3f} ms/step", file=sys.stderr, flush=True)
 
-    graph = capture(ls.step)
+    graph = capture(step)
     for _ in range(args.warmup):
         graph.replay()
     wall = timed_steps(graph.replay, args.steps)
@@ -305,7 +306,7 @@ def main():
     print(f"[bench] timed {args.steps} graph-replayed steps: {ms_per_step:.3f} ms/step, {gbs:.1f} GB/s",
           file=sys.stderr, flush=True)
 
-    dur = kernel_durations(ls, launches, args.steps)
+    dur = kernel_durations(launch_one, launches, args.steps)
     dom, roof = roofline(launches, dur)
     sha = source_sha()
     roof["traffic"] = traffic_for(dom, sha)
@@ -337,10 +338,11 @@ def main():
             "weights": wl.fmt,
             "tokens_per_pass": wl.m,
             "launches_per_step": len(launches),
-            "copies_per_step": len(launches) if wl.model is None else None,
+            "copies_per_step": len(ls.mats) if wl.model is None else None,
             "bytes_per_step": int(ls.bytes),
             "batch": 1,
-            "launch": "one HIP graph replay per step",
+            "launch": ("one persistent launch per step" if hasattr(ls, "plan") else "one launch per matrix")
+                      + ", replayed from a HIP graph",
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -159,6 +159,63 @@ int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, const int8_
                   int64_t f, float* work, float* y_f32, uint16_t* y_bf16, int32_t* sel,
                   float* gates, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* A whole decode step in one launch -- [README] "基准测试" (tokens/s of a  */
+/* batch-1 step is the time to stream every linear layer once).             */
+/* ------------------------------------------------------------------------ */
+
+enum { WQ_FORMAT_BF16 = 1, WQ_FORMAT_INT8 = 2, WQ_FORMAT_INT4G32 = 3 };
+
+/* One linear layer of a step, in the layout of the single-matrix calls:
+ *   x    bf16 [m][k]   (16-byte aligned)
+ *   w    bf16 [n][k] | int8 [n][k] | int4 packed [n][k/2]   (16-byte aligned)
+ *   aux  NULL (bf16) | bf16 scale [n] (int8) | sz [n][k/32][2] (int4, 4-byte aligned)
+ *   y_f32 / y_bf16  [m][n], either may be NULL but not both. */
+typedef struct {
+  const void* x;
+  const void* w;
+  const void* aux;
+  int64_t n;
+  int64_t k;
+  float* y_f32;
+  uint16_t* y_bf16;
+} wq_matrix;
+
+/* Filled by wq_decode_step_prepare; pass it unchanged to wq_decode_step_run. */
+typedef struct {
+  int32_t format;
+  int32_t m;
+  int32_t count;
+  int32_t groups;
+  int64_t total_batches;
+  const void* workspace;
+} wq_step_plan;
+
+/* Upper bound of the device workspace a plan of `count` matrices needs. */
+int64_t wq_decode_step_workspace_bytes(int32_t count);
+
+/*
+ * Plans `count` independent matvecs of one format (m token rows each: m = 1
+ * for bf16/int8, 1 <= m <= 8 for int4 G=32) as ONE persistent launch: every
+ * workgroup streams an equal share of the step's weight bytes as a contiguous
+ * range of row batches across the matrices, so no matrix pays its own
+ * launch, ramp-up and drain.  Results equal the single-matrix calls' to fp32
+ * rounding (the per-row reduction order may differ).
+ * Validates every matrix on the host (null -> sizes -> alignment; k must be a
+ * positive multiple of 8 / 16 / 32 per format and within the kernel's row
+ * limit), then writes the launch description into `workspace` (device
+ * memory, 16-byte aligned, `workspace_bytes` long, caller-owned; it must
+ * stay allocated and unmodified while the plan is used).  This copy is
+ * synchronous: prepare once, outside any graph capture.  The matrices'
+ * buffers must stay where they are for as long as the plan is run.
+ */
+int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int32_t count,
+                           void* workspace, int64_t workspace_bytes, wq_step_plan* plan);
+
+/* Launches a prepared step on `stream` (asynchronous; may be captured into a
+ * HIP graph).  Concurrent runs of plans that share output buffers race. */
+int wq_decode_step_run(const wq_step_plan* plan, void* stream);
+
 /* Static text for a wq_status value ("unknown status" otherwise). */
 const char* wq_status_string(int status);
 

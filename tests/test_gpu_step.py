@@ -1,0 +1,116 @@
+"""Whole decode step in one persistent launch (wq_decode_step_*) vs the oracle.
+
+Each case mixes shapes that take different wave roles in the step kernel
+(one wave per row, split-K across 2..7 waves, idle waves), ragged row counts
+and N = 1, with oracle-quantized weights.  Every matrix's fp32 and bf16
+outputs must meet the tolerances; runs are bitwise reproducible and graph
+replays reproduce the eager run.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_util import dev, host, host_u16, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say
+from oracle.bf16 import round_f32_to_bf16
+from oracle.quant import quantize_int8, quantize_int4g32
+from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
+from synth.gen import host_normal, host_bf16_normal
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8)],
+    ("int8", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 16)],
+    ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32)],
+    ("int4g32", 5): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32)],
+    ("int4g32", 2): [(45, 4096), (9, 16384)],
+    ("int4g32", 8): [(45, 4096), (9, 16384)],
+}
+
+
+def _build(fmt, m, seed):
+    import torch
+    mats, refs = [], []
+    for i, (n, k) in enumerate(SHAPES[(fmt, m)]):
+        w = host_normal((n, k), 0.02, 980, seed, i, 0)
+        x = host_bf16_normal((m, k) if m > 1 else (k,), 980, seed, i, 1)
+        if fmt == "bf16":
+            wb = round_f32_to_bf16(w)
+            ref = gemv_bf16(x, wb)
+            W, A = dev(wb), None
+        elif fmt == "int8":
+            q, s = quantize_int8(w)
+            ref = gemv_int8(x, q, s)
+            W, A = dev(q), dev(s)
+        else:
+            p, sz = quantize_int4g32(w)
+            ref = gemm_small_m(x, p, sz) if m > 1 else gemv_int4g32(x, p, sz)
+            W, A = dev(p), dev(sz)
+        y32 = torch.full((m * n,), -7.0, dtype=torch.float32, device="cuda")
+        y16 = torch.full((m * n,), 0x7BAD, dtype=torch.int16, device="cuda")
+        mats.append((dev(x), W, A, n, k, y32, y16))
+        refs.append(ref.reshape(m, n) if m > 1 else ref.reshape(1, n))
+    return mats, refs
+
+
+@pytest.mark.parametrize("fmt,m", list(SHAPES))
+def test_step_matches_oracle(fmt, m):
+    import torch
+    import weight_only_quantized_wq_amd as wq
+    say(f"decode step {fmt} m={m}")
+    mats, refs = _build(fmt, m, 1)
+    ws = torch.empty(wq.wq_decode_step_workspace_bytes(len(mats)), dtype=torch.uint8, device="cuda")
+    plan = wq.wq_decode_step_prepare(fmt, m, mats, ws)
+    wq.wq_decode_step_run(plan)
+    torch.cuda.synchronize()
+    first = []
+    for (x, W, A, n, k, y32, y16), ref in zip(mats, refs):
+        g32 = host(y32).reshape(m, n)
+        g16 = host_u16(y16)
+        e32 = rel_err(g32, ref)
+        e16 = rel_err(bf16_bits_to_f64(g16).reshape(m, n), ref)
+        say(f"  n={n} k={k}: err f32={e32:.2e} bf16={e16:.2e}")
+        assert e32 <= TOL_F32 and e16 <= TOL_BF16
+        assert np.array_equal(g16, round_f32_to_bf16(host(y32)))
+        first.append(host(y32).copy())
+    # bitwise reproducible, also from a captured graph
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.wq_decode_step_run(plan)
+    for rep in range(3):
+        for mt in mats:
+            mt[5].fill_(-7.0)
+        torch.cuda.synchronize()
+        if rep == 0:
+            wq.wq_decode_step_run(plan)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        for mt, f in zip(mats, first):
+            assert np.array_equal(host(mt[5]), f), f"run {rep} differs"
+
+
+def test_step_argument_errors():
+    import torch
+    import weight_only_quantized_wq_amd as wq
+    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    ws = torch.empty(wq.wq_decode_step_workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    good = (buf, buf, buf, 4, 64, buf, None)
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 9, [good], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 48, buf, None)], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, None, 4, 64, buf, None)], ws)
+    assert ei.value.status == 1
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf.data_ptr() + 2, buf, buf, 4, 64, buf, None)], ws)
+    assert ei.value.status == 3
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [good], ws, 64)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 2 ** 20, buf, None)], ws)
+    assert ei.value.status == 2

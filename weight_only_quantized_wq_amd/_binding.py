@@ -30,6 +30,19 @@ _SIGNATURES = {
     "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
 }
 
+WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3}
+
+
+class wq_matrix(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("w", ctypes.c_void_p), ("aux", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("y_f32", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p)]
+
+
+class wq_step_plan(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("m", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("total_batches", ctypes.c_int64), ("workspace", ctypes.c_void_p)]
+
+
 WQ_STATUS = {0: "WQ_OK", 1: "WQ_ERR_NULL", 2: "WQ_ERR_SHAPE", 3: "WQ_ERR_ALIGN", 4: "WQ_ERR_DEVICE",
              5: "WQ_ERR_LAUNCH"}
 
@@ -52,6 +65,13 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.wq_decode_step_workspace_bytes.argtypes = [ctypes.c_int32]
+    lib.wq_decode_step_workspace_bytes.restype = ctypes.c_int64
+    lib.wq_decode_step_prepare.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(wq_matrix), ctypes.c_int32,
+                                           _P, _I64, ctypes.POINTER(wq_step_plan)]
+    lib.wq_decode_step_prepare.restype = ctypes.c_int
+    lib.wq_decode_step_run.argtypes = [ctypes.POINTER(wq_step_plan), _P]
+    lib.wq_decode_step_run.restype = ctypes.c_int
     lib.wq_status_string.argtypes = [ctypes.c_int]
     lib.wq_status_string.restype = ctypes.c_char_p
     lib.wq_last_error.argtypes = []
@@ -128,3 +148,29 @@ def moe_top2_gemv(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32=None, y_bf
                   gates=None, stream=None):
     _call("moe_top2_gemv", _ptr(x), _ptr(logits), e, _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), dim, f,
           _ptr(work), _ptr(y_f32), _ptr(y_bf16), _ptr(sel), _ptr(gates), _stream(stream))
+
+
+def wq_decode_step_workspace_bytes(count):
+    return int(lib.wq_decode_step_workspace_bytes(count))
+
+
+def wq_decode_step_prepare(format, m, mats, workspace, workspace_bytes=None):
+    """mats: sequence of (x, w, aux, n, k, y_f32, y_bf16) with tensors (or None).
+    `format` is 1/2/3 or "bf16"/"int8"/"int4g32".  Returns the wq_step_plan."""
+    fmt = WQ_FORMAT.get(format, format)
+    arr = (wq_matrix * len(mats))()
+    for i, (x, w, aux, n, k, y32, y16) in enumerate(mats):
+        arr[i] = wq_matrix(_ptr(x), _ptr(w), _ptr(aux), n, k, _ptr(y32), _ptr(y16))
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    plan = wq_step_plan()
+    rc = lib.wq_decode_step_prepare(fmt, m, arr, len(mats), _ptr(workspace), workspace_bytes, ctypes.byref(plan))
+    if rc != 0:
+        raise WQError("wq_decode_step_prepare", rc, lib.wq_last_error().decode(errors="replace"))
+    return plan
+
+
+def wq_decode_step_run(plan, stream=None):
+    rc = lib.wq_decode_step_run(ctypes.byref(plan), _stream(stream))
+    if rc != 0:
+        raise WQError("wq_decode_step_run", rc, lib.wq_last_error().decode(errors="replace"))

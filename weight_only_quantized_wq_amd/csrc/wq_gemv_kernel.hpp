@@ -41,9 +41,11 @@ struct GemvArgs {
   int64_t k;
   int64_t row_bytes;
   int64_t batches;
+  int64_t batch_begin;    // multi-matrix launches: first global batch of this matrix
   int32_t chunks;
   int32_t split;
   int32_t groups;
+  int32_t cpl;            // multi-matrix launches: chunks per lane used (<= CPL)
 };
 
 template <class F, int U, int CPL>
@@ -57,7 +59,7 @@ struct Batch {
 // end, so both read as zero without a branch.  off[j] = 16 * chunk index.
 template <class F, int U, int CPL>
 __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg, const uint32_t (&off)[CPL],
-                                           Batch<F, U, CPL>& bt) {
+                                           Batch<F, U, CPL>& bt, int cpl = CPL) {
   const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -66,11 +68,11 @@ __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg,
     const int64_t rr = row_ok ? r : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rr * a.row_bytes, row_ok ? (uint32_t)a.row_bytes : 0u);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) bt.w[u][j] = buffer_load16_nt(rw, off[j]);
+    for (int j = 0; j < CPL; ++j) bt.w[u][j] = j < cpl ? buffer_load16_nt(rw, off[j]) : u32x4{0, 0, 0, 0};
     if constexpr (F::kGroupAux) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * a.chunks, row_ok ? (uint32_t)a.chunks * 4u : 0u);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = buffer_load4_nt(rs, off[j] >> 2);
+      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = j < cpl ? buffer_load4_nt(rs, off[j] >> 2) : 0u;
     } else {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;
@@ -83,8 +85,16 @@ template <class F, int M, int CPL, int U, int WAVES>
 __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int lane, int wave, int ks, int rg,
                                              const Batch<F, U, CPL>& bt, const typename F::X (&xr)[M][CPL],
                                              const float (&bias)[M], const typename F::K& kc,
-                                             float (&red)[2][WAVES][U * M], int& buf) {
+                                             float (&red)[2][WAVES][U * M], int& buf, int cpl = CPL,
+                                             bool active = true) {
   const int S = a.split;
+  if (!active) {            // a wave with no row group in this matrix: barrier only
+    if (S > 1) {
+      __syncthreads();
+      buf ^= 1;
+    }
+    return;
+  }
   const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
   float acc[U][M];
 #pragma unroll
@@ -93,6 +103,7 @@ __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int l
     for (int m = 0; m < M; ++m) acc[u][m] = bias[m];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
+      if (j >= cpl) break;
       typename F::D d;
       F::decode(bt.w[u][j], d, kc);
 #pragma unroll
@@ -192,6 +203,82 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
       b += step;
       if (b < a.batches) load_batch<F, U, CPL>(a, b, rg, off, A);
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole decode step in one launch: a workgroup walks a contiguous range of
+// global row batches across the step's matrices (ranges are cut so that every
+// workgroup streams the same number of weight bytes).  Per matrix it reads the
+// descriptor, takes its wave roles (split, row groups, chunks per lane <=
+// CPL), stages that matrix's activations, and streams its batches; waves
+// without a row group in a matrix only join the split-K barriers.  There is no
+// per-matrix launch, ramp-up or drain: the step is one stream of weight bytes.
+template <class F, int M, int CPL, int U, int WAVES, bool PF>
+__global__ __launch_bounds__(WAVES * 64) void gemv_step_kernel(const GemvArgs* __restrict__ mats,
+                                                               const int64_t* __restrict__ wg_begin,
+                                                               const int32_t* __restrict__ wg_mat) {
+  const int lane = lane_id();
+  const int wave = wave_id();
+  int64_t gb = wg_begin[blockIdx.x];
+  const int64_t gend = wg_begin[blockIdx.x + 1];
+  int mi = wg_mat[blockIdx.x];
+  __shared__ float red[2][WAVES][U * M];
+  int buf = 0;
+
+  while (gb < gend) {
+    const GemvArgs a = mats[mi];
+    const int cpl = a.cpl;
+    const int ks = wave % a.split;
+    const int rg = wave / a.split;
+    const bool active = rg < a.groups;
+    int cidx[CPL];
+    uint32_t off[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      cidx[j] = (ks * cpl + j) * kWave + lane;
+      off[j] = (uint32_t)cidx[j] * 16u;
+    }
+    int64_t b = gb - a.batch_begin;
+    const int64_t mend = a.batch_begin + a.batches;
+    const int64_t bend = (gend < mend ? gend : mend) - a.batch_begin;
+
+    Batch<F, U, CPL> A;
+    if (active) load_batch<F, U, CPL>(a, b, rg, off, A, cpl);
+
+    typename F::X xr[M][CPL];
+    float bias[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      bias[m] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        xr[m][j] = F::load_x(a.x + m * a.k, cidx[j], active && j < cpl && cidx[j] < a.chunks);
+        bias[m] += F::lane_bias(xr[m][j]);
+      }
+    }
+    const typename F::K kc = F::consts();
+
+    if constexpr (PF) {
+      Batch<F, U, CPL> B;
+      while (b < bend) {
+        if (active && b + 1 < bend) load_batch<F, U, CPL>(a, b + 1, rg, off, B, cpl);
+        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf, cpl, active);
+        ++b;
+        if (b >= bend) break;
+        if (active && b + 1 < bend) load_batch<F, U, CPL>(a, b + 1, rg, off, A, cpl);
+        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, kc, red, buf, cpl, active);
+        ++b;
+      }
+    } else {
+      while (b < bend) {
+        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf, cpl, active);
+        ++b;
+        if (active && b < bend) load_batch<F, U, CPL>(a, b, rg, off, A, cpl);
+      }
+    }
+    gb = a.batch_begin + bend;
+    ++mi;
   }
 }
 

@@ -1,0 +1,223 @@
+// Whole decode step in one launch: plan once on the host, then launch the
+// persistent step kernel (wq_gemv_kernel.hpp) as often as needed.
+#include <stdint.h>
+#include <string.h>
+
+#include <vector>
+
+#include "wq_gemv_kernel.hpp"
+#include "wq_host.hpp"
+
+namespace wq {
+
+// One persistent kernel configuration per (format, tokens per pass): the
+// largest chunks-per-lane any matrix may use (registers are sized for it),
+// waves per workgroup, rows per wave per batch and prefetch.
+struct StepVariant {
+  int cpl_max;
+  int waves;
+  int u;
+  const void* kernel;
+  void (*launch)(int grid, const GemvArgs*, const int64_t*, const int32_t*, hipStream_t);
+};
+
+template <class F, int M, int CPL, int U, int WAVES, bool PF>
+static void step_launch(int grid, const GemvArgs* mats, const int64_t* begin, const int32_t* mat,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+                     stream, mats, begin, mat);
+}
+
+template <class F, int M, int CPL, int U, int WAVES, bool PF>
+static StepVariant variant() {
+  return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
+                     &step_launch<F, M, CPL, U, WAVES, PF>};
+}
+
+static bool pick_variant(int format, int m, StepVariant& v) {
+  if (format == WQ_FORMAT_BF16 && m == 1) {
+    v = variant<FmtBf16, 1, 8, 1, 12, true>();
+  } else if (format == WQ_FORMAT_INT8 && m == 1) {
+    v = variant<FmtInt8, 1, 4, 2, 12, false>();
+  } else if (format == WQ_FORMAT_INT4G32) {
+    switch (m) {
+      case 1: v = variant<FmtInt4, 1, 3, 2, 4, true>(); break;
+      case 2: v = variant<FmtInt4, 2, 2, 2, 8, false>(); break;
+      case 3: v = variant<FmtInt4, 3, 2, 2, 8, false>(); break;
+      case 4: v = variant<FmtInt4, 4, 2, 2, 8, false>(); break;
+      case 5: v = variant<FmtInt4, 5, 2, 2, 8, false>(); break;
+      case 6: v = variant<FmtInt4, 6, 1, 2, 8, false>(); break;
+      case 7: v = variant<FmtInt4, 7, 1, 2, 8, false>(); break;
+      case 8: v = variant<FmtInt4, 8, 1, 2, 8, false>(); break;
+      default: return false;
+    }
+  } else {
+    return false;
+  }
+  return true;
+}
+
+static int weights_per_chunk(int format) {
+  return format == WQ_FORMAT_BF16 ? 8 : (format == WQ_FORMAT_INT8 ? 16 : 32);
+}
+
+static int64_t row_bytes_of(int format, int64_t k) {
+  return format == WQ_FORMAT_BF16 ? 2 * k : (format == WQ_FORMAT_INT8 ? k : k / 2);
+}
+
+constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
+
+static int64_t workspace_need(int64_t count, int64_t groups) {
+  return count * (int64_t)sizeof(GemvArgs) + (groups + 1) * 8 + groups * 4 + 64;
+}
+
+}  // namespace wq
+
+using namespace wq;
+
+extern "C" int64_t wq_decode_step_workspace_bytes(int32_t count) {
+  if (count < 0) return 0;
+  return workspace_need(count, kMaxGroups);
+}
+
+extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int32_t count,
+                                      void* workspace, int64_t workspace_bytes, wq_step_plan* plan) {
+  const char* name = "wq_decode_step_prepare";
+  if (!mats || !workspace || !plan) return fail(WQ_ERR_NULL, "%s: mats, workspace and plan must be non-null", name);
+  if (count < 1) return fail(WQ_ERR_SHAPE, "%s: count = %d must be >= 1", name, count);
+  StepVariant v{};
+  if (!pick_variant(format, m, v))
+    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16/int8, 1..8 for int4)", name,
+                format, m);
+  const int wpc = weights_per_chunk(format);
+  std::vector<GemvArgs> desc((size_t)count);
+  std::vector<double> batch_bytes((size_t)count);
+  int64_t total_batches = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const wq_matrix& mt = mats[i];
+    if (!mt.x || !mt.w || (format != WQ_FORMAT_BF16 && !mt.aux))
+      return fail(WQ_ERR_NULL, "%s: matrix %d: x, w (and scales) must be non-null", name, i);
+    if (!mt.y_f32 && !mt.y_bf16)
+      return fail(WQ_ERR_NULL, "%s: matrix %d: at least one of y_f32 / y_bf16 must be non-null", name, i);
+    if (mt.n < 1 || mt.k < wpc || mt.k % wpc || mt.n > ((int64_t)1 << 31))
+      return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
+                  name, i, (long long)mt.n, (long long)mt.k, wpc);
+    const int64_t chunks = mt.k / wpc;
+    const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
+    const int64_t split = (chunks + per_wave_max - 1) / per_wave_max;
+    if (split > v.waves)
+      return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
+                  (long long)mt.k);
+    if (!aligned16(mt.x) || !aligned16(mt.w) ||
+        (format == WQ_FORMAT_INT4G32 && (reinterpret_cast<uintptr_t>(mt.aux) & 3u)))
+      return fail(WQ_ERR_ALIGN, "%s: matrix %d: x and w must be 16-byte aligned (sz 4-byte)", name, i);
+    GemvArgs& a = desc[(size_t)i];
+    a = GemvArgs{};
+    a.x = reinterpret_cast<const uint16_t*>(mt.x);
+    a.w = reinterpret_cast<const uint8_t*>(mt.w);
+    if (format == WQ_FORMAT_INT8) a.scale = reinterpret_cast<const uint16_t*>(mt.aux);
+    if (format == WQ_FORMAT_INT4G32) a.sz = reinterpret_cast<const uint32_t*>(mt.aux);
+    a.y32 = mt.y_f32;
+    a.y16 = mt.y_bf16;
+    a.n = mt.n;
+    a.k = mt.k;
+    a.row_bytes = row_bytes_of(format, mt.k);
+    a.chunks = (int32_t)chunks;
+    a.split = (int32_t)split;
+    a.groups = v.waves / (int32_t)split;
+    a.cpl = (int32_t)((chunks + split * kWave - 1) / (split * kWave));
+    const int64_t rows_per_batch = (int64_t)a.groups * v.u;
+    a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
+    a.batch_begin = total_batches;
+    total_batches += a.batches;
+    const double aux_bytes = format == WQ_FORMAT_INT4G32 ? (double)chunks * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
+    batch_bytes[(size_t)i] = (double)rows_per_batch * ((double)a.row_bytes + aux_bytes);
+  }
+  int rc = check_device();
+  if (rc) return rc;
+
+  int groups = resident_groups(v.kernel, v.waves * kWave);
+  if (groups > kMaxGroups) groups = kMaxGroups;
+  if (groups > total_batches) groups = (int)total_batches;
+  if (groups < 1) groups = 1;
+  const int64_t need = workspace_need(count, groups);
+  if (workspace_bytes < need)
+    return fail(WQ_ERR_SHAPE, "%s: workspace of %lld bytes is smaller than the %lld needed", name,
+                (long long)workspace_bytes, (long long)need);
+  if (!aligned16(workspace)) return fail(WQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", name);
+
+  // Cut the step's weight bytes into `groups` equal contiguous ranges of row
+  // batches (a batch goes to the range its first byte falls in).
+  std::vector<int64_t> begin((size_t)groups + 1);
+  std::vector<int32_t> first((size_t)groups);
+  double total = 0;
+  for (int32_t i = 0; i < count; ++i) total += batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
+  int32_t mi = 0;
+  double acc = 0;   // bytes before matrix mi
+  for (int g = 0; g <= groups; ++g) {
+    const double target = total * (double)g / (double)groups;
+    while (mi < count && acc + batch_bytes[(size_t)mi] * (double)desc[(size_t)mi].batches <= target) {
+      acc += batch_bytes[(size_t)mi] * (double)desc[(size_t)mi].batches;
+      ++mi;
+    }
+    int64_t gb;
+    if (g == groups || mi >= count) {
+      gb = total_batches;
+    } else {
+      const GemvArgs& a = desc[(size_t)mi];
+      int64_t local = (int64_t)((target - acc) / batch_bytes[(size_t)mi] + 0.999999);
+      if (local > a.batches) local = a.batches;
+      gb = a.batch_begin + local;
+    }
+    if (g > 0 && gb < begin[(size_t)g - 1]) gb = begin[(size_t)g - 1];
+    begin[(size_t)g] = gb;
+  }
+  for (int g = 0; g < groups; ++g) {
+    // matrix holding the range's first batch
+    int32_t lo = 0, hi = count - 1;
+    const int64_t gb = begin[(size_t)g] < total_batches ? begin[(size_t)g] : total_batches - 1;
+    while (lo < hi) {
+      int32_t mid = (lo + hi + 1) / 2;
+      if (desc[(size_t)mid].batch_begin <= gb) lo = mid;
+      else hi = mid - 1;
+    }
+    first[(size_t)g] = lo;
+  }
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  const size_t off_begin = (size_t)count * sizeof(GemvArgs);
+  const size_t off_first = off_begin + ((size_t)groups + 1) * 8;
+  std::vector<char> host(off_first + (size_t)groups * 4);
+  memcpy(host.data(), desc.data(), off_begin);
+  memcpy(host.data() + off_begin, begin.data(), ((size_t)groups + 1) * 8);
+  memcpy(host.data() + off_first, first.data(), (size_t)groups * 4);
+  hipError_t e = hipMemcpy(ws, host.data(), host.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(WQ_ERR_LAUNCH, "%s: copying the plan to the workspace failed: %s", name, hipGetErrorString(e));
+  }
+  memset(plan, 0, sizeof(*plan));
+  plan->format = format;
+  plan->m = m;
+  plan->count = count;
+  plan->groups = groups;
+  plan->workspace = workspace;
+  plan->total_batches = total_batches;
+  return WQ_OK;
+}
+
+extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
+  const char* name = "wq_decode_step_run";
+  if (!plan || !plan->workspace) return fail(WQ_ERR_NULL, "%s: plan and its workspace must be non-null", name);
+  StepVariant v{};
+  if (!pick_variant(plan->format, plan->m, v) || plan->count < 1 || plan->groups < 1 || plan->groups > kMaxGroups)
+    return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_decode_step_prepare", name);
+  int rc = check_device();
+  if (rc) return rc;
+  const char* ws = reinterpret_cast<const char*>(plan->workspace);
+  const size_t off_begin = (size_t)plan->count * sizeof(GemvArgs);
+  const size_t off_first = off_begin + ((size_t)plan->groups + 1) * 8;
+  v.launch(plan->groups, reinterpret_cast<const GemvArgs*>(ws), reinterpret_cast<const int64_t*>(ws + off_begin),
+           reinterpret_cast<const int32_t*>(ws + off_first), (hipStream_t)stream);
+  return launch_status(name);
+}

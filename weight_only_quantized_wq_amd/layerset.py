@@ -93,8 +93,26 @@ class LayerSet:
         self.bytes = sum(q.bytes for q in self.mats)
 
     def step(self, stream=None):
+        """One decode step as one launch per matrix."""
         for q in self.mats:
             q.launch(stream)
+
+    def prepare_fused(self, with_f32=False):
+        """Plans the whole step as one persistent launch (wq_decode_step_*)."""
+        dev = self.mats[0].w.device
+        if with_f32:
+            for q in self.mats:
+                if q.y32 is None:
+                    q.y32 = torch.empty((q.m, q.n), dtype=torch.float32, device=dev)
+        nbytes = wq.wq_decode_step_workspace_bytes(len(self.mats))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        mats = [(q.x, q.w, q.aux, q.n, q.k, q.y32, q.y16) for q in self.mats]
+        self.plan = wq.wq_decode_step_prepare(self.fmt, self.m, mats, self.workspace)
+        return self.plan
+
+    def step_fused(self, stream=None):
+        """One decode step as one persistent launch (call prepare_fused first)."""
+        wq.wq_decode_step_run(self.plan, stream)
 
 
 def moe_layer_bytes(dim, f, top=2):

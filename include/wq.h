@@ -129,8 +129,8 @@ int wq_gemv_int4g32(const uint16_t* x, const uint8_t* qpacked, const uint16_t* s
  * through one int4 G=32 linear in one pass, each weight read once:
  *   x bf16 [m][k], 1 <= m <= 8; y [m][n]; row i of y equals
  *   wq_gemv_int4g32 applied to row i of x (to fp32 rounding).
- * k % 32 == 0; k <= 131072 for m == 1, 32768 for 2 <= m <= 5, 16384 for
- * m >= 6.
+ * k % 32 == 0; k <= 131072 for m == 1, 32768 for m == 2, 131072 for
+ * m >= 3 (from three tokens on the matrix cores).
  */
 int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
                    int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);

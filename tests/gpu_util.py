@@ -68,3 +68,13 @@ def rel_err(y, ref):
 
 def say(*a):
     print(*a, flush=True)
+
+
+def assert_same(got, want, what="repeat run"):
+    """Bitwise equality, naming the differing positions when it fails."""
+    got = np.asarray(got)
+    want = np.asarray(want)
+    if not np.array_equal(got, want):
+        idx = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
+        pairs = [(int(i), float(got.reshape(-1)[i]), float(want.reshape(-1)[i])) for i in idx[:8]]
+        raise AssertionError(f"{what}: {idx.size} of {got.size} values differ, first (index, got, want): {pairs}")

@@ -12,7 +12,7 @@ must not write outside the output.
 import numpy as np
 import pytest
 
-from gpu_util import (dev, host, host_u16, guarded, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say)
+from gpu_util import (assert_same, dev, host, host_u16, guarded, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say)
 from oracle.bf16 import round_f32_to_bf16
 from oracle.quant import quantize_int8, quantize_int4g32
 from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
@@ -79,7 +79,7 @@ def test_gemv_bf16(wq, n, k):
     _check_guards(b32, b16, n)
     first = host(y32).copy()
     wq.wq_gemv_bf16(xd, wd, n, k, y32, y16)
-    assert np.array_equal(host(y32), first)
+    assert_same(host(y32), first)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 
 
@@ -101,7 +101,7 @@ def test_gemv_int8(wq, n, k):
     _check_guards(b32, b16, n)
     first = host(y32).copy()
     wq.wq_gemv_int8(xd, qd, sd, n, k, y32, None)
-    assert np.array_equal(host(y32), first)
+    assert_same(host(y32), first)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 
 
@@ -123,12 +123,15 @@ def test_gemv_int4g32(wq, n, k):
     _check_guards(b32, b16, n)
     first = host(y32).copy()
     wq.wq_gemv_int4g32(xd, pd, szd, n, k, y32, None)
-    assert np.array_equal(host(y32), first)
+    assert_same(host(y32), first)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 
 
+# m >= 3 runs on the matrix cores with K windows of 256 groups: the cases
+# cover one window, several, and a ragged last window (k = 8288, 12352)
 SMALLM_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 32), (70, 8192)]] + \
-    [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 4, 5)] + [(5, 8, 32768), (1, 10, 131072)]
+    [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 3, 4, 5, 7, 8)] + \
+    [(5, 8, 32768), (1, 10, 131072), (5, 6, 131072), (5, 50, 8288), (7, 37, 12352), (3, 100, 8224)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALLM_CASES)

@@ -24,7 +24,11 @@ SHAPES = {
     ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32)],
     ("int4g32", 5): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32)],
     ("int4g32", 2): [(45, 4096), (9, 16384)],
-    ("int4g32", 8): [(45, 4096), (9, 16384)],
+    ("int4g32", 8): [(45, 4096), (9, 16384), (3, 28672)],
+    ("int4g32", 3): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32), (40, 8288)],
+    ("int4g32", 4): [(45, 4096), (9, 16384), (77, 12352)],
+    ("int4g32", 6): [(45, 4096), (9, 16384)],
+    ("int4g32", 7): [(45, 4096), (31, 8192), (2, 32)],
 }
 
 

@@ -5,6 +5,7 @@
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
+#include "wq_mfma.hpp"
 
 namespace wq {
 
@@ -76,22 +77,14 @@ struct Plans<FmtInt4, 1> {
                                        WQ_PLAN(896, 7, 4, 1, true), WQ_PLAN(3584, 7, 8, 1, true),
                                        WQ_PLAN(4096, 8, 8, 1, false)};
 };
-// speculative-verify rows: the activations of all M tokens stay in registers
-#define WQ_SMALLM_PLANS(MM, ...)                                             \
-  template <>                                                                \
-  struct Plans<FmtInt4, MM> {                                                \
-    using F = FmtInt4;                                                       \
-    static constexpr int M = MM;                                             \
-    static constexpr PlanEntry list[] = {__VA_ARGS__};                       \
-  };
-WQ_SMALLM_PLANS(2, WQ_PLAN(1024, 2, 8, 2, false))
-WQ_SMALLM_PLANS(3, WQ_PLAN(1024, 2, 8, 2, false))
-WQ_SMALLM_PLANS(4, WQ_PLAN(1024, 2, 8, 2, false))
-WQ_SMALLM_PLANS(5, WQ_PLAN(1024, 2, 8, 2, false))
-WQ_SMALLM_PLANS(6, WQ_PLAN(512, 1, 8, 2, false))
-WQ_SMALLM_PLANS(7, WQ_PLAN(512, 1, 8, 2, false))
-WQ_SMALLM_PLANS(8, WQ_PLAN(512, 1, 8, 2, false))
-#undef WQ_SMALLM_PLANS
+// two-token verify rows: the activations of both tokens stay in registers
+// (from three tokens on the matrix-core kernel of wq_mfma.hpp is faster)
+template <>
+struct Plans<FmtInt4, 2> {
+  using F = FmtInt4;
+  static constexpr int M = 2;
+  static constexpr PlanEntry list[] = {WQ_PLAN(1024, 2, 8, 2, false)};
+};
 #undef WQ_PLAN
 
 template <class F, int M>
@@ -203,6 +196,36 @@ extern "C" int wq_gemv_int4g32(const uint16_t* x, const uint8_t* qpacked, const 
   return run_gemv<FmtInt4, 1>(a, (hipStream_t)stream, "wq_gemv_int4g32");
 }
 
+namespace wq {
+
+// Verify product on the matrix cores (3 <= m <= 8): workgroups of 12 waves
+// over blocks of 32 rows, activations staged in LDS 256 groups (8192
+// inputs) at a time, work items of 8 groups, one item prefetched.
+template <int M>
+int launch_mfma(const GemvArgs& g, hipStream_t stream) {
+  constexpr int RT = kMfmaRT, KW = kMfmaKW, WAVES = kMfmaWaves, PF = kMfmaPF, OCT = kMfmaOct;
+  static int resident = 0;
+  auto kern = gemm_mfma_kernel<M, RT, KW, WAVES, PF, OCT>;
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
+  MfmaArgs a{};
+  a.x = g.x;
+  a.w = g.w;
+  a.sz = g.sz;
+  a.y32 = g.y32;
+  a.y16 = g.y16;
+  a.n = g.n;
+  a.k = g.k;
+  a.groups = (int32_t)(g.k / 32);
+  a.blocks = (g.n + 16 * RT - 1) / (16 * RT);
+  a.block_begin = 0;
+  const int64_t grid = balanced_grid(a.blocks, resident);
+  if (grid <= 0) return WQ_OK;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * kWave), 0, stream, a);
+  return launch_status("wq_gemm_smallM");
+}
+
+}  // namespace wq
+
 extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
                               int64_t k, float* y_f32, uint16_t* y_bf16, void* stream) {
   GemvArgs a;
@@ -211,14 +234,18 @@ extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpack
   if (n == 0) return WQ_OK;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  switch (m) {
-    case 1: return run_gemv<FmtInt4, 1>(a, s, "wq_gemm_smallM");
-    case 2: return run_gemv<FmtInt4, 2>(a, s, "wq_gemm_smallM");
-    case 3: return run_gemv<FmtInt4, 3>(a, s, "wq_gemm_smallM");
-    case 4: return run_gemv<FmtInt4, 4>(a, s, "wq_gemm_smallM");
-    case 5: return run_gemv<FmtInt4, 5>(a, s, "wq_gemm_smallM");
-    case 6: return run_gemv<FmtInt4, 6>(a, s, "wq_gemm_smallM");
-    case 7: return run_gemv<FmtInt4, 7>(a, s, "wq_gemm_smallM");
-    default: return run_gemv<FmtInt4, 8>(a, s, "wq_gemm_smallM");
+  if (m >= 3) {
+    if (k > kMfmaMaxK)
+      return fail(WQ_ERR_SHAPE, "wq_gemm_smallM: k = %lld is larger than %d", (long long)k, kMfmaMaxK);
+    switch (m) {
+      case 3: return launch_mfma<3>(a, s);
+      case 4: return launch_mfma<4>(a, s);
+      case 5: return launch_mfma<5>(a, s);
+      case 6: return launch_mfma<6>(a, s);
+      case 7: return launch_mfma<7>(a, s);
+      default: return launch_mfma<8>(a, s);
+    }
   }
+  if (m == 2) return run_gemv<FmtInt4, 2>(a, s, "wq_gemm_smallM");
+  return run_gemv<FmtInt4, 1>(a, s, "wq_gemm_smallM");
 }

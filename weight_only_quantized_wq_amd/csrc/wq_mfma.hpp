@@ -1,0 +1,324 @@
+// Speculative-verify product (int4 G=32 weights, 2 <= M <= 8 token rows) on
+// the matrix cores: v_mfma_f32_16x16x32_bf16.
+//
+// One MFMA multiplies a 16 x 32 A tile by a 32 x 16 B tile.  Here a "quad"
+// is 16 weight rows x 4 consecutive groups (128 inputs):
+//   * A: lane l holds 8 k-values of row (l % 16) in k-slot (l / 16); the quad
+//     is decoded so that lane l's 16 loaded bytes -- group (l / 16) of its row
+//     -- feed k-slot (l / 16) of four MFMAs (word j of the chunk -> MFMA j).
+//     Codes become exact bf16 (128 + q) as in the VALU path.
+//   * B is block diagonal: output column c = 4 * slot + token (tokens 0..3 in
+//     the first column set, 4..7 in the second), and lane (slot q', column c)
+//     holds that token's activations of group q' only when c belongs to slot
+//     q'; every other B element is zero.  So D[row][c] is the sum over ONE
+//     group, and the group's scale and zero are applied exactly afterwards:
+//     y += s * D + (z - 128 s) * (sum of the group's activations).
+//   * D: lane l holds rows 4 * (l / 16) + r (r < 4) of column l % 16.
+// Activations are staged in LDS per K-window (pre-permuted bf16 pairs and
+// per-group sums; once per matrix when a window holds all of K).  The waves of
+// a workgroup take the window's work items in turn for the workgroup's block
+// of 16 * RT rows, and their totals meet in LDS in a fixed order at the end
+// of the block.  No atomics: results are bitwise reproducible.
+#pragma once
+
+#include <stdint.h>
+
+#include "wq_formats.hpp"
+
+namespace wq {
+
+// The configuration used by both entry points (chosen by timing the
+// Llama-3.1-70B verify shapes at 3..8 tokens): blocks of 2 row tiles (32
+// rows), K windows of 256 groups, 12 waves, one item prefetched, items of 2
+// quads (32 contiguous code bytes per lane).
+constexpr int kMfmaRT = 2, kMfmaKW = 256, kMfmaWaves = 12, kMfmaPF = 1, kMfmaOct = 2;
+constexpr int kMfmaMaxK = 131072;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct MfmaArgs {
+  const uint16_t* x;     // [m][k] bf16
+  const uint8_t* w;      // [n][k/2]
+  const uint32_t* sz;    // [n][k/32]
+  float* y32;            // [m][n] or null
+  uint16_t* y16;         // [m][n] or null
+  int64_t n;
+  int64_t k;
+  int64_t blocks;        // ceil(n / (16 * RT))
+  int64_t block_begin;   // first global block of this matrix (decode step)
+  int32_t groups;        // k / 32
+};
+
+template <int M, int RT, int KW, int WAVES>
+struct alignas(16) MfmaShared {
+  static constexpr int kSets = (M + 3) / 4;
+  // permuted activation pairs per (token, group); each token's row is padded
+  // by 16 bytes so the four tokens read by one k-slot sit in different banks
+  static constexpr int kRow = KW * 16 + 4;
+  uint32_t xs[M][kRow];
+  float gs[M][KW];                          // per-group activation sums
+  alignas(16) uint32_t zero[16];            // B operand of columns outside a slot
+  float red[WAVES][RT][kSets][4][16];       // per-wave totals (lanes with column < 4)
+};
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint32_t (&a)[4], const uint32_t (&b)[4], f32x4 c) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 av = {a[0], a[1], a[2], a[3]};
+  u4 bv = {b[0], b[1], b[2], b[3]};
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), c,
+                                                 0, 0, 0);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Stages activations of groups [g0, g0 + kw) for all M tokens into LDS.
+template <int M, int RT, int KW, int WAVES>
+__device__ __forceinline__ void stage_window(const MfmaArgs& a, int g0, int kw, MfmaShared<M, RT, KW, WAVES>& sh) {
+  for (int it = threadIdx.x; it < M * kw; it += WAVES * 64) {
+    const int t = it / kw;
+    const int g = it - t * kw;
+    FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, g0 + g, true);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sh.xs[t][16 * g + i] = xv.p[i];
+    sh.gs[t][g] = xv.gsum;
+  }
+}
+
+// One work item: OCT quads of a block's RT row tiles.  Lane (rq, col) loads
+// the 16 * OCT contiguous code bytes of groups gb + OCT rq + o (o < OCT) of
+// row col, so quad o is made of groups gb + OCT rq' + o over the four k-slots;
+// and for each quad the (scale, zero) words of its D rows 4 rq + r for the
+// group of its D column, gb + OCT slot + o.  Rows past n and groups past k/32
+// read as zero.
+template <int RT, int OCT>
+struct ItemData {
+  u32x4 w[RT][OCT];
+  uint32_t sz[RT][OCT][4];
+};
+
+template <int RT, int OCT>
+__device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t gb, int rq, int col, int slot,
+                                          ItemData<RT, OCT>& q) {
+  const uint32_t row_bytes = (uint32_t)(a.k / 2);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int64_t rbase = n0 + 16 * rt;
+    const int64_t rows_left = a.n - rbase;
+    const uint32_t rows_ok = rows_left <= 0 ? 0u : (rows_left >= 16 ? 16u : (uint32_t)rows_left);
+    const int64_t rb = rows_left > 0 ? rbase : 0;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * (a.k / 2), rows_ok * row_bytes);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.groups, rows_ok * (uint32_t)a.groups * 4u);
+#pragma unroll
+    for (int o = 0; o < OCT; ++o) {
+      const int64_t g = gb + OCT * rq + o;
+      q.w[rt][o] = buffer_load16_nt(rw, g < a.groups ? (uint32_t)col * row_bytes + (uint32_t)g * 16u : 0x80000000u);
+    }
+#pragma unroll
+    for (int o = 0; o < OCT; ++o) {
+      const int64_t ge = gb + OCT * slot + o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t offs =
+            ge < a.groups ? ((uint32_t)(4 * rq + r) * (uint32_t)a.groups + (uint32_t)ge) * 4u : 0x80000000u;
+        q.sz[rt][o][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)offs, 0, 0);
+      }
+    }
+  }
+}
+
+// Next item of this wave's sequence (block, window start, item) after the
+// given one: items wave, wave + WAVES, ... of each window, windows in order,
+// then the next block of the range.  False when the wave has no more work.
+template <int KW, int WAVES, int OCT>
+__device__ __forceinline__ bool next_item(const MfmaArgs& a, int64_t b_end, int64_t b_step, int wave, int64_t& blk,
+                                          int& g0, int& it) {
+  it += WAVES;
+  for (;;) {
+    const int kw = (a.groups - g0) < KW ? (a.groups - g0) : KW;
+    if (4 * OCT * it < kw) return true;
+    g0 += KW;
+    it = wave;
+    if (g0 >= a.groups) {
+      g0 = 0;
+      blk += b_step;
+      if (blk >= b_end) return false;
+    }
+  }
+}
+
+// One workgroup's share of a matrix: blocks b_first, b_first + b_step, ...
+// below b_end, each of 16 * RT rows.  The block's K range is walked in
+// windows of KW groups whose activations are staged in LDS (once per call
+// when one window holds all of K), and the WAVES waves take the window's
+// items in turn.  PF = 1 keeps the next item's loads in flight while one
+// computes.  Every thread of the workgroup must make the same call.
+template <int M, int RT, int KW, int WAVES, int PF, int OCT>
+__device__ __forceinline__ void mfma_blocks(const MfmaArgs& a, int64_t b_first, int64_t b_end, int64_t b_step,
+                                            MfmaShared<M, RT, KW, WAVES>& sh) {
+  constexpr int SETS = (M + 3) / 4;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int rq = lane >> 4;          // k-slot of A, row quarter of D
+  const int col = lane & 15;         // row of A, column of D
+  const int slot = col >> 2;         // group slot of this D column
+  const int tok0 = col & 3;          // token of this D column in set 0
+  const FmtInt4::K kc = FmtInt4::consts();
+  const bool single = a.groups <= KW;   // one window: stage it once
+
+  ItemData<RT, OCT> nxt;
+  int64_t pblk = b_first;
+  int pg0 = 0, pit = wave - WAVES;
+  bool pending = false;
+  if (PF && pblk < b_end) {
+    pending = next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
+    if (pending) load_item<RT, OCT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
+  }
+  bool staged = false;
+  uint32_t bop[SETS][4][4];          // B operands of the current quad (see below)
+#pragma unroll
+  for (int st = 0; st < SETS; ++st)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bop[st][j][e] = 0u;
+
+  for (int64_t blk = b_first; blk < b_end; blk += b_step) {
+    const int64_t n0 = blk * 16 * RT;
+    float tot[RT][SETS][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int s = 0; s < SETS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) tot[rt][s][r] = 0.0f;
+
+    for (int g0 = 0; g0 < a.groups; g0 += KW) {
+      const int kw = (a.groups - g0) < KW ? (a.groups - g0) : KW;
+      if (!single || !staged) {
+        __syncthreads();                     // previous window fully consumed
+        stage_window<M, RT, KW, WAVES>(a, g0, kw, sh);
+        __syncthreads();
+        staged = true;
+      }
+      const int items = (kw + 4 * OCT - 1) / (4 * OCT);
+      for (int it = wave; it < items; it += WAVES) {
+        const int64_t gb = g0 + 4 * OCT * it;
+        ItemData<RT, OCT> cur;
+        if (PF) {
+          cur = nxt;
+          pending = next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
+          if (pending) load_item<RT, OCT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
+        } else {
+          load_item<RT, OCT>(a, n0, gb, rq, col, slot, cur);
+        }
+#pragma unroll
+        for (int o = 0; o < OCT; ++o) {
+          // B operands of quad o.  Only the lanes whose column slot equals
+          // their k-slot (and whose token exists) ever hold data: the others
+          // keep the zeros they started with, so they read no LDS at all.
+          float xsum[SETS];
+          const int gl = 4 * OCT * it + OCT * rq + o;     // this lane's B group (window-local)
+          const int ge = 4 * OCT * it + OCT * slot + o;   // the group of this lane's D column
+#pragma unroll
+          for (int s = 0; s < SETS; ++s) {
+            const int t = 4 * s + tok0;
+            if (slot == rq && t < M) {
+              const uint32_t* src = gl < kw ? &sh.xs[t][16 * gl] : &sh.zero[0];
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bop[s][j][e] = src[4 * j + e];
+            }
+            xsum[s] = (t < M && ge < kw) ? sh.gs[t < M ? t : 0][ge < kw ? ge : 0] : 0.0f;
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            FmtInt4::D d;
+            FmtInt4::decode(cur.w[rt][o], d, kc);
+#pragma unroll
+            for (int s = 0; s < SETS; ++s) {
+              f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const uint32_t av[4] = {d.t[4 * j], d.t[4 * j + 1], d.t[4 * j + 2], d.t[4 * j + 3]};
+                acc = mfma_bf16(av, bop[s][j], acc);
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float sc = __uint_as_float(cur.sz[rt][o][r] << 16);
+                const float zc = __uint_as_float(cur.sz[rt][o][r] & 0xFFFF0000u);
+                float v = fmaf(sc, acc[r], tot[rt][s][r]);
+                tot[rt][s][r] = fmaf(fmaf(-128.0f, sc, zc), xsum[s], v);
+              }
+            }
+          }
+        }
+      }
+    }
+
+    // sum the four group slots of each token (columns c, c+4, c+8, c+12 of a
+    // 16-lane row), then the waves in a fixed order, then store
+    if (single) __syncthreads();             // the previous block's totals are read
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int s = 0; s < SETS; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = tot[rt][s][r];
+          v += dpp_row<0x124>(v);     // row_ror:4
+          v += dpp_row<0x128>(v);     // row_ror:8
+          if (col < 4) sh.red[wave][rt][s][r][4 * rq + col] = v;
+        }
+    __syncthreads();
+    for (int i = threadIdx.x; i < RT * SETS * 4 * 16; i += WAVES * 64) {
+      const int c16 = i & 15;
+      const int r = (i >> 4) & 3;
+      const int s = (i >> 6) % SETS;
+      const int rt = (i >> 6) / SETS;
+      const int t = 4 * s + (c16 & 3);
+      const int64_t row = n0 + 16 * rt + 4 * (c16 >> 2) + r;
+      if (t < M && row < a.n) {
+        float v = sh.red[0][rt][s][r][c16];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) v += sh.red[w][rt][s][r][c16];
+        if (a.y32) a.y32[(int64_t)t * a.n + row] = v;
+        if (a.y16) a.y16[(int64_t)t * a.n + row] = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+// One matrix: workgroups take blocks blockIdx.x, blockIdx.x + gridDim.x, ...
+template <int M, int RT, int KW, int WAVES, int PF, int OCT>
+__global__ __launch_bounds__(WAVES * 64) void gemm_mfma_kernel(MfmaArgs a) {
+  __shared__ MfmaShared<M, RT, KW, WAVES> sh;
+  if (threadIdx.x < 16) sh.zero[threadIdx.x] = 0u;
+  mfma_blocks<M, RT, KW, WAVES, PF, OCT>(a, blockIdx.x, a.blocks, gridDim.x, sh);
+}
+
+// A whole decode step: the blocks of all matrices in one global order
+// (matrix by matrix), workgroup g taking the contiguous range
+// [wg_begin[g], wg_begin[g + 1]) that starts in matrix wg_mat[g].
+template <int M, int RT, int KW, int WAVES, int PF, int OCT>
+__global__ __launch_bounds__(WAVES * 64) void gemm_mfma_step_kernel(const MfmaArgs* __restrict__ mats,
+                                                                    const int64_t* __restrict__ wg_begin,
+                                                                    const int32_t* __restrict__ wg_mat) {
+  __shared__ MfmaShared<M, RT, KW, WAVES> sh;
+  if (threadIdx.x < 16) sh.zero[threadIdx.x] = 0u;
+  const int64_t b0 = wg_begin[blockIdx.x];
+  const int64_t b1 = wg_begin[blockIdx.x + 1];
+  int mi = wg_mat[blockIdx.x];
+  for (int64_t b = b0; b < b1; ++mi) {
+    const MfmaArgs a = mats[mi];
+    const int64_t hi = (a.block_begin + a.blocks) < b1 ? (a.block_begin + a.blocks) : b1;
+    if (hi > b) mfma_blocks<M, RT, KW, WAVES, PF, OCT>(a, b - a.block_begin, hi - a.block_begin, 1, sh);
+    b = hi > b ? hi : b;
+  }
+}
+
+}  // namespace wq

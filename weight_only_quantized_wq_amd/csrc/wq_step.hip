@@ -7,31 +7,49 @@
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
+#include "wq_mfma.hpp"
 
 namespace wq {
 
 // One persistent kernel configuration per (format, tokens per pass): the
 // largest chunks-per-lane any matrix may use (registers are sized for it),
-// waves per workgroup, rows per wave per batch and prefetch.
+// waves per workgroup, rows per wave per batch and prefetch; or, for int4
+// with 3..8 tokens, the matrix-core kernel (batch = one block of rows).
 struct StepVariant {
   int cpl_max;
   int waves;
   int u;
   const void* kernel;
-  void (*launch)(int grid, const GemvArgs*, const int64_t*, const int32_t*, hipStream_t);
+  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, hipStream_t);
+  bool mfma;   // int4 with 3..8 tokens: the matrix-core step kernel
 };
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static void step_launch(int grid, const GemvArgs* mats, const int64_t* begin, const int32_t* mat,
-                        hipStream_t stream) {
+static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, mats, begin, mat);
+                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
 }
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 static StepVariant variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>};
+                     &step_launch<F, M, CPL, U, WAVES, PF>, false};
+}
+
+template <int M>
+static void mfma_step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
+                     dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream, reinterpret_cast<const MfmaArgs*>(mats),
+                     begin, mat);
+}
+
+template <int M>
+static StepVariant mfma_variant() {
+  return StepVariant{0, kMfmaWaves, 16 * kMfmaRT,
+                     reinterpret_cast<const void*>(
+                         gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
+                     &mfma_step_launch<M>, true};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -44,12 +62,12 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     switch (m) {
       case 1: v = variant<FmtInt4, 1, 3, 2, 4, false>(); break;
       case 2: v = variant<FmtInt4, 2, 2, 2, 8, false>(); break;
-      case 3: v = variant<FmtInt4, 3, 2, 2, 8, false>(); break;
-      case 4: v = variant<FmtInt4, 4, 2, 2, 8, false>(); break;
-      case 5: v = variant<FmtInt4, 5, 2, 2, 8, false>(); break;
-      case 6: v = variant<FmtInt4, 6, 1, 2, 8, false>(); break;
-      case 7: v = variant<FmtInt4, 7, 1, 2, 8, false>(); break;
-      case 8: v = variant<FmtInt4, 8, 1, 2, 8, false>(); break;
+      case 3: v = mfma_variant<3>(); break;
+      case 4: v = mfma_variant<4>(); break;
+      case 5: v = mfma_variant<5>(); break;
+      case 6: v = mfma_variant<6>(); break;
+      case 7: v = mfma_variant<7>(); break;
+      case 8: v = mfma_variant<8>(); break;
       default: return false;
     }
   } else {
@@ -68,8 +86,11 @@ static int64_t row_bytes_of(int format, int64_t k) {
 
 constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
 
+// per-matrix descriptor slot: large enough for either kernel's descriptor
+constexpr size_t kDescBytes = ((sizeof(GemvArgs) > sizeof(MfmaArgs) ? sizeof(GemvArgs) : sizeof(MfmaArgs)) + 15) / 16 * 16;
+
 static int64_t workspace_need(int64_t count, int64_t groups) {
-  return count * (int64_t)sizeof(GemvArgs) + (groups + 1) * 8 + groups * 4 + 64;
+  return count * (int64_t)kDescBytes + (groups + 1) * 8 + groups * 4 + 64;
 }
 
 }  // namespace wq
@@ -104,9 +125,9 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
                   name, i, (long long)mt.n, (long long)mt.k, wpc);
     const int64_t chunks = mt.k / wpc;
-    const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
-    const int64_t split = (chunks + per_wave_max - 1) / per_wave_max;
-    if (split > v.waves)
+    const int64_t per_wave_max = (int64_t)kWave * (v.mfma ? 1 : v.cpl_max);
+    const int64_t split = v.mfma ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
+    if (split > v.waves || (v.mfma && mt.k > kMfmaMaxK))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -127,7 +148,8 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.split = (int32_t)split;
     a.groups = v.waves / (int32_t)split;
     a.cpl = (int32_t)((chunks + split * kWave - 1) / (split * kWave));
-    const int64_t rows_per_batch = (int64_t)a.groups * v.u;
+    // the matrix-core kernel's batch is one block of 16 * RT rows
+    const int64_t rows_per_batch = v.mfma ? (int64_t)v.u : (int64_t)a.groups * v.u;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -186,10 +208,30 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   }
 
   char* ws = reinterpret_cast<char*>(workspace);
-  const size_t off_begin = (size_t)count * sizeof(GemvArgs);
+  const size_t off_begin = (size_t)count * (v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs));
   const size_t off_first = off_begin + ((size_t)groups + 1) * 8;
   std::vector<char> host(off_first + (size_t)groups * 4);
-  memcpy(host.data(), desc.data(), off_begin);
+  if (v.mfma) {
+    std::vector<MfmaArgs> md((size_t)count);
+    for (int32_t i = 0; i < count; ++i) {
+      const GemvArgs& g = desc[(size_t)i];
+      MfmaArgs& a = md[(size_t)i];
+      a = MfmaArgs{};
+      a.x = g.x;
+      a.w = g.w;
+      a.sz = g.sz;
+      a.y32 = g.y32;
+      a.y16 = g.y16;
+      a.n = g.n;
+      a.k = g.k;
+      a.groups = (int32_t)(g.k / 32);
+      a.blocks = g.batches;
+      a.block_begin = g.batch_begin;
+    }
+    memcpy(host.data(), md.data(), off_begin);
+  } else {
+    memcpy(host.data(), desc.data(), off_begin);
+  }
   memcpy(host.data() + off_begin, begin.data(), ((size_t)groups + 1) * 8);
   memcpy(host.data() + off_first, first.data(), (size_t)groups * 4);
   hipError_t e = hipMemcpy(ws, host.data(), host.size(), hipMemcpyHostToDevice);
@@ -216,9 +258,9 @@ extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
   int rc = check_device();
   if (rc) return rc;
   const char* ws = reinterpret_cast<const char*>(plan->workspace);
-  const size_t off_begin = (size_t)plan->count * sizeof(GemvArgs);
+  const size_t off_begin = (size_t)plan->count * (v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs));
   const size_t off_first = off_begin + ((size_t)plan->groups + 1) * 8;
-  v.launch(plan->groups, reinterpret_cast<const GemvArgs*>(ws), reinterpret_cast<const int64_t*>(ws + off_begin),
+  v.launch(plan->groups, ws, reinterpret_cast<const int64_t*>(ws + off_begin),
            reinterpret_cast<const int32_t*>(ws + off_first), (hipStream_t)stream);
   return launch_status(name);
 }

@@ -156,10 +156,43 @@ __device__ __forceinline__ bool next_item(const MfmaArgs& a, int64_t b_end, int6
 // when one window holds all of K), and the WAVES waves take the window's
 // items in turn.  PF = 1 keeps the next item's loads in flight while one
 // computes.  Every thread of the workgroup must make the same call.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  return reinterpret_cast<T*>(uniform64(reinterpret_cast<int64_t>(p)));
+}
+
+// A descriptor whose fields the compiler can keep in scalar registers: the
+// buffer resources built from them must be wave-uniform, or every buffer
+// load turns into a loop over the distinct values.
+__device__ __forceinline__ MfmaArgs uniform_args(const MfmaArgs& a) {
+  MfmaArgs u;
+  u.x = uniform_ptr(a.x);
+  u.w = uniform_ptr(a.w);
+  u.sz = uniform_ptr(a.sz);
+  u.y32 = uniform_ptr(a.y32);
+  u.y16 = uniform_ptr(a.y16);
+  u.n = uniform64(a.n);
+  u.k = uniform64(a.k);
+  u.blocks = uniform64(a.blocks);
+  u.block_begin = uniform64(a.block_begin);
+  u.groups = __builtin_amdgcn_readfirstlane(a.groups);
+  return u;
+}
+
 template <int M, int RT, int KW, int WAVES, int PF, int OCT>
-__device__ __forceinline__ void mfma_blocks(const MfmaArgs& a, int64_t b_first, int64_t b_end, int64_t b_step,
+__device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_first, int64_t b_end, int64_t b_step,
                                             MfmaShared<M, RT, KW, WAVES>& sh) {
   constexpr int SETS = (M + 3) / 4;
+  const MfmaArgs a = uniform_args(a_in);
+  b_first = uniform64(b_first);
+  b_end = uniform64(b_end);
+  b_step = uniform64(b_step);
   const int lane = lane_id();
   const int wave = wave_id();
   const int rq = lane >> 4;          // k-slot of A, row quarter of D

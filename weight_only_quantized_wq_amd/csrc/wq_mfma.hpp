@@ -57,7 +57,8 @@ struct alignas(16) MfmaShared {
   // by 16 bytes so the four tokens read by one k-slot sit in different banks
   static constexpr int kRow = KW * 16 + 4;
   uint32_t xs[M][kRow];
-  float gs[M][KW];                          // per-group activation sums
+  float gs[M][KW + 1];                      // per-group activation sums; rows padded so the
+                                            // tokens one lane quad reads sit in different banks
   alignas(16) uint32_t zero[16];            // B operand of columns outside a slot
   float red[WAVES][RT][kSets][4][16];       // per-wave totals (lanes with column < 4)
 };

@@ -20,24 +20,29 @@ struct StepVariant {
   int waves;
   int u;
   const void* kernel;
-  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, hipStream_t);
+  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, StepTail*, hipStream_t);
   bool mfma;   // int4 with 3..8 tokens: the matrix-core step kernel
+  // dynamic tail (VALU kernel): fraction of the step's bytes handed out in
+  // units of about `unit_bytes`; 0 = all static
+  double tail_frac;
+  double unit_bytes;
 };
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
+static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail* tail,
+                        hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat, tail);
 }
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 static StepVariant variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>, false};
+                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0.0, 0.0};
 }
 
 template <int M>
-static void mfma_step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat,
+static void mfma_step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
                              hipStream_t stream) {
   hipLaunchKernelGGL((gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
                      dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream, reinterpret_cast<const MfmaArgs*>(mats),
@@ -49,7 +54,7 @@ static StepVariant mfma_variant() {
   return StepVariant{0, kMfmaWaves, 16 * kMfmaRT,
                      reinterpret_cast<const void*>(
                          gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
-                     &mfma_step_launch<M>, true};
+                     &mfma_step_launch<M>, true, 0.0, 0.0};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -58,6 +63,11 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     v = variant<FmtBf16, 1, 4, 2, 12, true>();
   } else if (format == WQ_FORMAT_INT8 && m == 1) {
     v = variant<FmtInt8, 1, 4, 4, 12, false>();
+    // on steps that mix row lengths its equal-byte static shares finish up
+    // to ~15% apart: hand out the last 15% of the bytes dynamically (timed;
+    // the bf16 and int4 kernels gain nothing from it)
+    v.tail_frac = 0.15;
+    v.unit_bytes = 64.0 * 1024;
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
       case 1: v = variant<FmtInt4, 1, 3, 2, 4, false>(); break;
@@ -89,8 +99,19 @@ constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound
 // per-matrix descriptor slot: large enough for either kernel's descriptor
 constexpr size_t kDescBytes = ((sizeof(GemvArgs) > sizeof(MfmaArgs) ? sizeof(GemvArgs) : sizeof(MfmaArgs)) + 15) / 16 * 16;
 
+// Units of the dynamic tail (at most kMaxUnits per plan).
+constexpr int64_t kMaxUnits = 65536;
+
+// Workspace layout: descriptors, static range starts (groups + 1), first
+// matrix per range (groups), then at a 16-byte boundary the tail header and
+// the matrix of each tail unit.
+static size_t tail_offset(size_t desc_bytes, int64_t count, int64_t groups) {
+  const size_t off_first = (size_t)count * desc_bytes + ((size_t)groups + 1) * 8;
+  return (off_first + (size_t)groups * 4 + 15) / 16 * 16;
+}
+
 static int64_t workspace_need(int64_t count, int64_t groups) {
-  return count * (int64_t)kDescBytes + (groups + 1) * 8 + groups * 4 + 64;
+  return (int64_t)tail_offset(kDescBytes, count, groups) + (int64_t)sizeof(StepTail) + 4 * kMaxUnits + 64;
 }
 
 }  // namespace wq
@@ -169,48 +190,76 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
                 (long long)workspace_bytes, (long long)need);
   if (!aligned16(workspace)) return fail(WQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", name);
 
-  // Cut the step's weight bytes into `groups` equal contiguous ranges of row
-  // batches (a batch goes to the range its first byte falls in).
-  std::vector<int64_t> begin((size_t)groups + 1);
-  std::vector<int32_t> first((size_t)groups);
+  // The first global batch at or after byte offset `target` of the step
+  // (a batch belongs to the range its first byte falls in).
   double total = 0;
   for (int32_t i = 0; i < count; ++i) total += batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
-  int32_t mi = 0;
-  double acc = 0;   // bytes before matrix mi
-  for (int g = 0; g <= groups; ++g) {
-    const double target = total * (double)g / (double)groups;
-    while (mi < count && acc + batch_bytes[(size_t)mi] * (double)desc[(size_t)mi].batches <= target) {
-      acc += batch_bytes[(size_t)mi] * (double)desc[(size_t)mi].batches;
-      ++mi;
+  auto batch_at = [&](double target) -> int64_t {
+    double acc = 0;   // bytes before matrix i
+    for (int32_t i = 0; i < count; ++i) {
+      const double mb = batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
+      if (acc + mb > target) {
+        int64_t local = (int64_t)((target - acc) / batch_bytes[(size_t)i] + 0.999999);
+        if (local > desc[(size_t)i].batches) local = desc[(size_t)i].batches;
+        return desc[(size_t)i].batch_begin + local;
+      }
+      acc += mb;
     }
-    int64_t gb;
-    if (g == groups || mi >= count) {
-      gb = total_batches;
-    } else {
-      const GemvArgs& a = desc[(size_t)mi];
-      int64_t local = (int64_t)((target - acc) / batch_bytes[(size_t)mi] + 0.999999);
-      if (local > a.batches) local = a.batches;
-      gb = a.batch_begin + local;
-    }
-    if (g > 0 && gb < begin[(size_t)g - 1]) gb = begin[(size_t)g - 1];
-    begin[(size_t)g] = gb;
-  }
-  for (int g = 0; g < groups; ++g) {
-    // matrix holding the range's first batch
+    return total_batches;
+  };
+  auto matrix_of = [&](int64_t gb) -> int32_t {
+    if (gb >= total_batches) gb = total_batches - 1;
     int32_t lo = 0, hi = count - 1;
-    const int64_t gb = begin[(size_t)g] < total_batches ? begin[(size_t)g] : total_batches - 1;
     while (lo < hi) {
-      int32_t mid = (lo + hi + 1) / 2;
+      const int32_t mid = (lo + hi + 1) / 2;
       if (desc[(size_t)mid].batch_begin <= gb) lo = mid;
       else hi = mid - 1;
     }
-    first[(size_t)g] = lo;
+    return lo;
+  };
+
+  // Static part: [0, static_end) cut into `groups` equal-byte ranges; the
+  // rest (for variants with a dynamic tail) is handed out in units.
+  // Equal bytes take equal time only when the matrices share a shape; a
+  // step that mixes row lengths streams them at different rates, so part of
+  // it is handed out dynamically (variants with a tail only).
+  bool mixed = false;
+  for (int32_t i = 1; i < count; ++i) mixed = mixed || desc[(size_t)i].k != desc[0].k;
+  const bool dynamic = !v.mfma && groups > 1 && v.tail_frac > 0.0 && mixed;
+  const double static_bytes = dynamic ? total * (1.0 - v.tail_frac) : total;
+  const int64_t static_end = dynamic ? batch_at(static_bytes) : total_batches;
+  std::vector<int64_t> begin((size_t)groups + 1);
+  std::vector<int32_t> first((size_t)groups);
+  for (int g = 0; g <= groups; ++g) {
+    int64_t gb = g == groups ? static_end : batch_at(static_bytes * (double)g / (double)groups);
+    if (gb > static_end) gb = static_end;
+    if (g > 0 && gb < begin[(size_t)g - 1]) gb = begin[(size_t)g - 1];
+    begin[(size_t)g] = gb;
+  }
+  for (int g = 0; g < groups; ++g) first[(size_t)g] = matrix_of(begin[(size_t)g]);
+
+  StepTail tail{};
+  std::vector<int32_t> unit_mat;
+  if (dynamic && static_end < total_batches) {
+    const int64_t left = total_batches - static_end;
+    const double avg = (total - static_bytes) / (double)left;   // bytes per tail batch
+    int64_t ub = (int64_t)(v.unit_bytes / avg + 0.5);
+    if (ub < 1) ub = 1;
+    if ((left + ub - 1) / ub > kMaxUnits) ub = (left + kMaxUnits - 1) / kMaxUnits;
+    tail.units = (int32_t)((left + ub - 1) / ub);
+    tail.start = static_end;
+    tail.unit_batches = ub;
+    tail.total = total_batches;
+    unit_mat.resize((size_t)tail.units);
+    for (int32_t u = 0; u < tail.units; ++u) unit_mat[(size_t)u] = matrix_of(static_end + (int64_t)u * ub);
   }
 
   char* ws = reinterpret_cast<char*>(workspace);
-  const size_t off_begin = (size_t)count * (v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs));
+  const size_t desc_bytes = v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs);
+  const size_t off_begin = (size_t)count * desc_bytes;
   const size_t off_first = off_begin + ((size_t)groups + 1) * 8;
-  std::vector<char> host(off_first + (size_t)groups * 4);
+  const size_t off_tail = tail_offset(desc_bytes, count, groups);
+  std::vector<char> host(off_tail + sizeof(StepTail) + unit_mat.size() * 4, 0);
   if (v.mfma) {
     std::vector<MfmaArgs> md((size_t)count);
     for (int32_t i = 0; i < count; ++i) {
@@ -234,6 +283,8 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   }
   memcpy(host.data() + off_begin, begin.data(), ((size_t)groups + 1) * 8);
   memcpy(host.data() + off_first, first.data(), (size_t)groups * 4);
+  memcpy(host.data() + off_tail, &tail, sizeof(StepTail));
+  if (!unit_mat.empty()) memcpy(host.data() + off_tail + sizeof(StepTail), unit_mat.data(), unit_mat.size() * 4);
   hipError_t e = hipMemcpy(ws, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -257,10 +308,13 @@ extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
     return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_decode_step_prepare", name);
   int rc = check_device();
   if (rc) return rc;
-  const char* ws = reinterpret_cast<const char*>(plan->workspace);
-  const size_t off_begin = (size_t)plan->count * (v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs));
+  char* ws = reinterpret_cast<char*>(const_cast<void*>(plan->workspace));
+  const size_t desc_bytes = v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs);
+  const size_t off_begin = (size_t)plan->count * desc_bytes;
   const size_t off_first = off_begin + ((size_t)plan->groups + 1) * 8;
+  const size_t off_tail = tail_offset(desc_bytes, plan->count, plan->groups);
   v.launch(plan->groups, ws, reinterpret_cast<const int64_t*>(ws + off_begin),
-           reinterpret_cast<const int32_t*>(ws + off_first), (hipStream_t)stream);
+           reinterpret_cast<const int32_t*>(ws + off_first), reinterpret_cast<StepTail*>(ws + off_tail),
+           (hipStream_t)stream);
   return launch_status(name);
 }

@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = {
     ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8)],
     ("int8", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 16)],
-    ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32)],
+    ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32), (3, 28672),
+                     (70, 4160)],
     ("int4g32", 5): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32)],
     ("int4g32", 2): [(45, 4096), (9, 16384)],
     ("int4g32", 8): [(45, 4096), (9, 16384), (3, 28672)],
@@ -117,4 +118,8 @@ def test_step_argument_errors():
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 2 ** 20, buf, None)], ws)
+    assert ei.value.status == 2
+    # one past the longest int4 row the single-token step kernel stages
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
     assert ei.value.status == 2

@@ -30,6 +30,7 @@ struct FmtBf16 {
   static constexpr int kWeightsPerChunk = 8;
   static constexpr bool kGroupAux = false;
   static constexpr bool kRowScale = false;
+  static constexpr bool kLaneBias = false;
   struct X {
     uint32_t p[4];
   };
@@ -71,6 +72,7 @@ struct FmtInt8 {
   static constexpr int kWeightsPerChunk = 16;
   static constexpr bool kGroupAux = false;
   static constexpr bool kRowScale = true;
+  static constexpr bool kLaneBias = true;
   struct X {
     float v[16];
   };
@@ -138,6 +140,7 @@ struct FmtInt4 {
   static constexpr int kWeightsPerChunk = 32;
   static constexpr bool kGroupAux = true;   // one (scale, zero) word per chunk
   static constexpr bool kRowScale = false;
+  static constexpr bool kLaneBias = false;
   static constexpr uint32_t kMagic = 0x43004300u;   // bf16 128.0 in both halves
   struct X {
     uint32_t p[16];   // p[4i + j] = (x[8i + j], x[8i + j + 4]) as a bf16 pair
@@ -174,6 +177,33 @@ struct FmtInt4 {
     return r;
   }
   __device__ static float lane_bias(const X&) { return 0.0f; }
+
+  // Activations staged in LDS for a whole workgroup (decode-step kernel):
+  // 17 words per chunk, laid out over `cmax` chunks as four 16-byte planes
+  // (plane h of chunk c at word 4 * (h * cmax + c), so consecutive lanes read
+  // consecutive 16-byte slots) followed by the group sums (word 16 * cmax + c).
+  static constexpr int kLdsWordsPerChunk = 17;
+  __device__ static void stage(const uint16_t* x, int chunks, int c, uint32_t* xs, int cmax) {
+    const X r = load_x(x, c, c < chunks);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<u32x4*>(xs + 4 * (h * cmax + c)) = u32x4{r.p[4 * h], r.p[4 * h + 1], r.p[4 * h + 2],
+                                                                 r.p[4 * h + 3]};
+    xs[16 * cmax + c] = __float_as_uint(r.gsum);
+  }
+  __device__ static X lds_x(const uint32_t* xs, int cmax, int c) {
+    X r;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + 4 * (h * cmax + c));
+      r.p[4 * h] = v[0];
+      r.p[4 * h + 1] = v[1];
+      r.p[4 * h + 2] = v[2];
+      r.p[4 * h + 3] = v[3];
+    }
+    r.gsum = __uint_as_float(xs[16 * cmax + c]);
+    return r;
+  }
 
   // the nibble mask sits in a VGPR so that each pair decodes with one
   // v_and_or_b32 (mask, then OR the bf16 128.0 exponent pattern)

@@ -8,6 +8,7 @@
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
 #include "wq_mfma.hpp"
+#include "wq_step_shared.hpp"
 
 namespace wq {
 
@@ -22,6 +23,8 @@ struct StepVariant {
   const void* kernel;
   void (*launch)(int grid, const void*, const int64_t*, const int32_t*, StepTail*, hipStream_t);
   bool mfma;   // int4 with 3..8 tokens: the matrix-core step kernel
+  int cmax;    // > 0: the shared-activation kernel (batch = u rows of one wave),
+               // staging at most cmax chunks of a row
   // dynamic tail (VALU kernel): fraction of the step's bytes handed out in
   // units of about `unit_bytes`; 0 = all static
   double tail_frac;
@@ -38,7 +41,20 @@ static void step_launch(int grid, const void* mats, const int64_t* begin, const 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 static StepVariant variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0.0, 0.0};
+                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0, 0.0, 0.0};
+}
+
+template <class F, int U, int CPL, int WAVES, bool PF>
+static void shared_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_step_shared_kernel<F, U, CPL, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+}
+
+template <class F, int U, int CPL, int WAVES, bool PF>
+static StepVariant shared_variant() {
+  return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_shared_kernel<F, U, CPL, WAVES, PF>),
+                     &shared_launch<F, U, CPL, WAVES, PF>, false, shared_x_cmax<F, CPL>(), 0.0, 0.0};
 }
 
 template <int M>
@@ -54,7 +70,7 @@ static StepVariant mfma_variant() {
   return StepVariant{0, kMfmaWaves, 16 * kMfmaRT,
                      reinterpret_cast<const void*>(
                          gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
-                     &mfma_step_launch<M>, true, 0.0, 0.0};
+                     &mfma_step_launch<M>, true, 0, 0.0, 0.0};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -70,7 +86,7 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     v.unit_bytes = 64.0 * 1024;
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
-      case 1: v = variant<FmtInt4, 1, 3, 2, 4, false>(); break;
+      case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
       case 2: v = variant<FmtInt4, 2, 2, 2, 8, false>(); break;
       case 3: v = mfma_variant<3>(); break;
       case 4: v = mfma_variant<4>(); break;
@@ -147,8 +163,9 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
                   name, i, (long long)mt.n, (long long)mt.k, wpc);
     const int64_t chunks = mt.k / wpc;
     const int64_t per_wave_max = (int64_t)kWave * (v.mfma ? 1 : v.cpl_max);
-    const int64_t split = v.mfma ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
-    if (split > v.waves || (v.mfma && mt.k > kMfmaMaxK))
+    const int64_t split = v.mfma || v.cmax ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
+    const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
+    if (split > v.waves || (v.mfma && mt.k > kMfmaMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -167,10 +184,13 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.row_bytes = row_bytes_of(format, mt.k);
     a.chunks = (int32_t)chunks;
     a.split = (int32_t)split;
-    a.groups = v.waves / (int32_t)split;
-    a.cpl = (int32_t)((chunks + split * kWave - 1) / (split * kWave));
-    // the matrix-core kernel's batch is one block of 16 * RT rows
-    const int64_t rows_per_batch = v.mfma ? (int64_t)v.u : (int64_t)a.groups * v.u;
+    a.groups = v.cmax ? 1 : v.waves / (int32_t)split;
+    // the shared-activation kernel streams a row in `passes` passes of cpl_max
+    // chunks per lane
+    a.cpl = v.cmax ? (int32_t)passes : (int32_t)((chunks + split * kWave - 1) / (split * kWave));
+    // the matrix-core kernel's batch is one block of 16 * RT rows; the
+    // shared-activation kernel's is u rows of one wave
+    const int64_t rows_per_batch = v.mfma || v.cmax ? (int64_t)v.u : (int64_t)a.groups * v.u;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -225,7 +245,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   // it is handed out dynamically (variants with a tail only).
   bool mixed = false;
   for (int32_t i = 1; i < count; ++i) mixed = mixed || desc[(size_t)i].k != desc[0].k;
-  const bool dynamic = !v.mfma && groups > 1 && v.tail_frac > 0.0 && mixed;
+  const bool dynamic = !v.mfma && !v.cmax && groups > 1 && v.tail_frac > 0.0 && mixed;
   const double static_bytes = dynamic ? total * (1.0 - v.tail_frac) : total;
   const int64_t static_end = dynamic ? batch_at(static_bytes) : total_batches;
   std::vector<int64_t> begin((size_t)groups + 1);

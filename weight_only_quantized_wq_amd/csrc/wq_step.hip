@@ -9,6 +9,7 @@
 #include "wq_host.hpp"
 #include "wq_mfma.hpp"
 #include "wq_step_shared.hpp"
+#include "wq_verify.hpp"
 
 namespace wq {
 
@@ -25,6 +26,8 @@ struct StepVariant {
   bool mfma;   // int4 with 3..8 tokens: the matrix-core step kernel
   int cmax;    // > 0: the shared-activation kernel (batch = u rows of one wave),
                // staging at most cmax chunks of a row
+  bool verify; // int4 with 2..8 tokens on the matrix cores, weights as the B
+               // operand (batch = one 16-row tile)
   // dynamic tail (VALU kernel): fraction of the step's bytes handed out in
   // units of about `unit_bytes`; 0 = all static
   double tail_frac;
@@ -41,7 +44,7 @@ static void step_launch(int grid, const void* mats, const int64_t* begin, const 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 static StepVariant variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0, 0.0, 0.0};
+                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0, false, 0.0, 0.0};
 }
 
 template <class F, int U, int CPL, int WAVES, bool PF>
@@ -54,7 +57,7 @@ static void shared_launch(int grid, const void* mats, const int64_t* begin, cons
 template <class F, int U, int CPL, int WAVES, bool PF>
 static StepVariant shared_variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_shared_kernel<F, U, CPL, WAVES, PF>),
-                     &shared_launch<F, U, CPL, WAVES, PF>, false, shared_x_cmax<F, CPL>(), 0.0, 0.0};
+                     &shared_launch<F, U, CPL, WAVES, PF>, false, shared_x_cmax<F, CPL>(), false, 0.0, 0.0};
 }
 
 template <int M>
@@ -70,7 +73,23 @@ static StepVariant mfma_variant() {
   return StepVariant{0, kMfmaWaves, 16 * kMfmaRT,
                      reinterpret_cast<const void*>(
                          gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
-                     &mfma_step_launch<M>, true, 0, 0.0, 0.0};
+                     &mfma_step_launch<M>, true, 0, false, 0.0, 0.0};
+}
+
+constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
+
+template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL>
+static void verify_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>), dim3((unsigned)grid),
+                     dim3(WAVES * 64), 0, stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+}
+
+template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool QL = true>
+static StepVariant verify_variant() {
+  return StepVariant{1, WAVES, 16 * RT,
+                     reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>),
+                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL>, false, 0, true, 0.0, 0.0};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -88,12 +107,12 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
       case 2: v = variant<FmtInt4, 2, 2, 2, 8, false>(); break;
-      case 3: v = mfma_variant<3>(); break;
-      case 4: v = mfma_variant<4>(); break;
-      case 5: v = mfma_variant<5>(); break;
-      case 6: v = mfma_variant<6>(); break;
-      case 7: v = mfma_variant<7>(); break;
-      case 8: v = mfma_variant<8>(); break;
+      case 3: v = verify_variant<3, 12, true>(); break;
+      case 4: v = verify_variant<4, 12, true>(); break;
+      case 5: v = verify_variant<5, 8, true>(); break;
+      case 6: v = verify_variant<6, 8, true, 2, 2, 128>(); break;
+      case 7: v = verify_variant<7, 8, true, 2, 2, 128>(); break;
+      case 8: v = verify_variant<8, 8, true, 2, 2, 128>(); break;
       default: return false;
     }
   } else {
@@ -163,9 +182,9 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
                   name, i, (long long)mt.n, (long long)mt.k, wpc);
     const int64_t chunks = mt.k / wpc;
     const int64_t per_wave_max = (int64_t)kWave * (v.mfma ? 1 : v.cpl_max);
-    const int64_t split = v.mfma || v.cmax ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
+    const int64_t split = v.mfma || v.cmax || v.verify ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
-    if (split > v.waves || (v.mfma && mt.k > kMfmaMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
+    if (split > v.waves || ((v.mfma || v.verify) && mt.k > kMfmaMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -184,18 +203,23 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.row_bytes = row_bytes_of(format, mt.k);
     a.chunks = (int32_t)chunks;
     a.split = (int32_t)split;
-    a.groups = v.cmax ? 1 : v.waves / (int32_t)split;
+    a.groups = v.cmax || v.verify ? 1 : v.waves / (int32_t)split;
     // the shared-activation kernel streams a row in `passes` passes of cpl_max
     // chunks per lane
     a.cpl = v.cmax ? (int32_t)passes : (int32_t)((chunks + split * kWave - 1) / (split * kWave));
     // the matrix-core kernel's batch is one block of 16 * RT rows; the
     // shared-activation kernel's is u rows of one wave
-    const int64_t rows_per_batch = v.mfma || v.cmax ? (int64_t)v.u : (int64_t)a.groups * v.u;
+    const int64_t rows_per_batch = v.mfma || v.cmax || v.verify ? (int64_t)v.u : (int64_t)a.groups * v.u;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
     const double aux_bytes = format == WQ_FORMAT_INT4G32 ? (double)chunks * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
     batch_bytes[(size_t)i] = (double)rows_per_batch * ((double)a.row_bytes + aux_bytes);
+    // the shared-activation kernel spends arithmetic on every lane of a pass,
+    // including the lanes past a row's end in its last pass: weigh a batch by
+    // its padded length so that rows whose length is not a multiple of a
+    // pass (e.g. k = 11008) get proportionally shorter ranges
+    if (v.cmax) batch_bytes[(size_t)i] *= (double)(passes * per_wave_max) / (double)chunks;
   }
   int rc = check_device();
   if (rc) return rc;
@@ -245,7 +269,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   // it is handed out dynamically (variants with a tail only).
   bool mixed = false;
   for (int32_t i = 1; i < count; ++i) mixed = mixed || desc[(size_t)i].k != desc[0].k;
-  const bool dynamic = !v.mfma && !v.cmax && groups > 1 && v.tail_frac > 0.0 && mixed;
+  const bool dynamic = !v.mfma && !v.cmax && !v.verify && groups > 1 && v.tail_frac > 0.0 && mixed;
   const double static_bytes = dynamic ? total * (1.0 - v.tail_frac) : total;
   const int64_t static_end = dynamic ? batch_at(static_bytes) : total_batches;
   std::vector<int64_t> begin((size_t)groups + 1);

@@ -74,6 +74,10 @@ def build_workload(name, launch="fused"):
         def gl(e, layer):
             return device_normal((e,), 1.0, "cuda", *logits_key(wl, layer))
         ls = MoELayerSet(mm.dim, mm.ffn, mm.experts, mm.layers, gw, gx, gl)
+        if launch == "fused":
+            ls.prepare_fused()
+            launches = [(f"moe step kernels int8 top-2 ({mm.layers} layers: W13 pass + W2 pass)", 0, ls.bytes)]
+            return wl, ls, launches, lambda i: ls.step_fused(), ls.step_fused
         launches = [("moe_top2_gemv", mm.dim, ls.bytes / mm.layers)] * mm.layers
         return wl, ls, launches, ls.launch_layer, ls.step
     ls = LayerSet(wl.matrices(), wl.fmt, gen_w_device(wl), gen_x_device(wl), m=wl.m)
@@ -286,6 +290,7 @@ def main():
     torch.cuda.set_device(0)
     t_build = time.perf_counter()
     wl, ls, launches, launch_one, step = build_workload(args.workload, args.launch)
+    from weight_only_quantized_wq_amd.layerset import MoELayerSet
     print(f"[bench] built {args.workload}: {len(launches)} launches, {ls.bytes / 1e9:.4f} GB/step "
           f"in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
     if not args.no_calibration:
@@ -341,8 +346,9 @@ def main():
             "copies_per_step": len(ls.mats) if wl.model is None else None,
             "bytes_per_step": int(ls.bytes),
             "batch": 1,
-            "launch": ("one persistent launch per step" if hasattr(ls, "plan") else "one launch per matrix")
-                      + ", replayed from a HIP graph",
+            "launch": (("two persistent launches per step (all layers' W13, then all layers' W2)"
+                        if isinstance(ls, MoELayerSet) else "one persistent launch per step")
+                       if hasattr(ls, "plan") else "one launch per matrix") + ", replayed from a HIP graph",
         },
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -217,6 +217,59 @@ int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int
  * HIP graph).  Concurrent runs of plans that share output buffers race. */
 int wq_decode_step_run(const wq_step_plan* plan, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Top-2 MoE decode over many layers in two launches -- [README] "Mixtral   */
+/* 8x7B" (a token's MoE layers are streamed once per decode step).          */
+/* ------------------------------------------------------------------------ */
+
+/* One MoE layer, with the buffers and layouts of moe_top2_gemv. */
+typedef struct {
+  const void* x;          /* bf16 [dim], 16-byte aligned */
+  const float* logits;    /* fp32 [e] */
+  const int8_t* w13;      /* int8 [e][2f][dim], 16-byte aligned */
+  const uint16_t* s13;    /* bf16 [e][2f] */
+  const int8_t* w2;       /* int8 [e][dim][f], 16-byte aligned */
+  const uint16_t* s2;     /* bf16 [e][dim] */
+  float* work;            /* fp32 [2][f], 16-byte aligned; caller scratch (overwritten) */
+  float* y_f32;           /* [dim] or NULL */
+  uint16_t* y_bf16;       /* [dim] or NULL (not both NULL) */
+  int32_t* sel;           /* [2] or NULL */
+  float* gates;           /* [2] or NULL */
+} wq_moe_layer;
+
+/* Filled by wq_moe_step_prepare; pass it unchanged to wq_moe_step_run. */
+typedef struct {
+  int64_t dim;
+  int64_t f;
+  int32_t e;
+  int32_t count;
+  int32_t grid13;
+  int32_t grid2;
+  const void* workspace;
+} wq_moe_plan;
+
+/* Device workspace a plan of `count` layers needs (bytes). */
+int64_t wq_moe_step_workspace_bytes(int32_t count);
+
+/*
+ * Plans `count` independent MoE layers (each its own token, logits, experts,
+ * work buffer and output; every layer computes exactly what moe_top2_gemv
+ * computes for it, to fp32 rounding) as two persistent launches: the W13
+ * pass of every layer, then the W2 pass of every layer.  All layers share
+ * e == 8, dim and f, with dim % 16 == 0, f % 16 == 0, 16 <= dim <= 14336 and
+ * 16 <= f <= 16384 (a layer's activations are staged whole in LDS).
+ * Validates every layer on the host (null -> sizes -> alignment), then copies
+ * the layer descriptors into `workspace` (device memory, 16-byte aligned,
+ * caller-owned, unmodified while the plan is used).  The copy is
+ * synchronous: prepare once, outside any graph capture.
+ */
+int wq_moe_step_prepare(int64_t e, int64_t dim, int64_t f, const wq_moe_layer* layers, int32_t count,
+                        void* workspace, int64_t workspace_bytes, wq_moe_plan* plan);
+
+/* Launches a prepared MoE step on `stream` (asynchronous; may be captured
+ * into a HIP graph).  Runs of plans that share buffers must not overlap. */
+int wq_moe_step_run(const wq_moe_plan* plan, void* stream);
+
 /* Static text for a wq_status value ("unknown status" otherwise). */
 const char* wq_status_string(int status);
 

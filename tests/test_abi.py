@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32",
                  "wq_gemm_smallM", "moe_top2_gemv", "wq_status_string", "wq_last_error",
-                 "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run"]:
+                 "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
+                 "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run"]:
         assert want in names
 
 
@@ -134,3 +135,35 @@ def test_step_plan_errors_before_any_device_work(wq):
     junk = wq_step_plan(7, 1, 1, 1, 1, BAD)
     assert lib.wq_decode_step_run(ctypes.byref(junk), None) == 2
     assert wq.wq_decode_step_workspace_bytes(129) > 129 * 64
+
+
+def test_moe_step_plan_errors_before_any_device_work(wq):
+    import ctypes
+    from weight_only_quantized_wq_amd._binding import wq_moe_layer, wq_moe_plan
+    lib = wq._binding.lib
+    plan = wq_moe_plan()
+
+    def layers(**kw):
+        f = dict(x=BAD, logits=BAD, w13=BAD, s13=BAD, w2=BAD, s2=BAD, work=BAD, y_f32=BAD, y_bf16=None,
+                 sel=None, gates=None)
+        f.update(kw)
+        return (wq_moe_layer * 1)(wq_moe_layer(**f))
+    ok = layers()
+    # null arguments
+    assert lib.wq_moe_step_prepare(8, 64, 64, None, 1, BAD, 1 << 20, ctypes.byref(plan)) == 1
+    assert lib.wq_moe_step_prepare(8, 64, 64, ok, 1, None, 1 << 20, ctypes.byref(plan)) == 1
+    assert lib.wq_moe_step_prepare(8, 64, 64, layers(w2=None), 1, BAD, 1 << 20, ctypes.byref(plan)) == 1
+    assert lib.wq_moe_step_prepare(8, 64, 64, layers(y_f32=None), 1, BAD, 1 << 20, ctypes.byref(plan)) == 1
+    # sizes: expert count, dims not multiples of 16, beyond what LDS stages whole, no layers
+    assert lib.wq_moe_step_prepare(4, 64, 64, ok, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    assert lib.wq_moe_step_prepare(8, 40, 64, ok, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    assert lib.wq_moe_step_prepare(8, 64, 16400, ok, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    assert lib.wq_moe_step_prepare(8, 14352, 64, ok, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    assert lib.wq_moe_step_prepare(8, 64, 64, ok, 0, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    # misaligned pointers are rejected before the device is touched
+    assert lib.wq_moe_step_prepare(8, 64, 64, ok, 1, BAD, 1 << 20, ctypes.byref(plan)) == 3
+    # run rejects a plan it did not produce
+    assert lib.wq_moe_step_run(None, None) == 1
+    junk = wq_moe_plan(64, 64, 4, 1, 1, 1, BAD)
+    assert lib.wq_moe_step_run(ctypes.byref(junk), None) == 2
+    assert wq.wq_moe_step_workspace_bytes(32) >= 32 * 88

@@ -83,11 +83,14 @@ def test_workload_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
-def test_mixtral_full_size_layer0():
-    """Mixtral-8x7B MoE layer 0 as the bench builds it: the two selected
-    experts' fp32 weights are regenerated and quantized by the oracle, whose
-    codes must match the device's bit for bit, then the oracle's MoE output is
-    compared with the device output."""
+@pytest.mark.parametrize("launch", ["fused", "per-layer"])
+def test_mixtral_full_size_sampled(launch):
+    """Mixtral-8x7B MoE layers as the bench builds them (two layers; the bench
+    runs 32): the selected experts' fp32 weights are regenerated and quantized
+    by the oracle, whose codes must match the device's bit for bit, then the
+    oracle's MoE output is compared with the device output of each layer --
+    through the two-launch step (the bench's launch configuration) and
+    through the single-layer call."""
     import torch
     from synth.workloads import WORKLOADS, expert_key, logits_key, moe_x_key
     from synth.gen import device_normal, device_bf16_normal
@@ -101,27 +104,32 @@ def test_mixtral_full_size_layer0():
     ls = MoELayerSet(mm.dim, mm.ffn, mm.experts, 2, gw,
                      lambda d, l: device_bf16_normal((d,), "cuda", *moe_x_key(wl, l)),
                      lambda e, l: device_normal((e,), 1.0, "cuda", *logits_key(wl, l)))
-    y32 = torch.empty(mm.dim, dtype=torch.float32, device="cuda")
-    sel = torch.empty(2, dtype=torch.int32, device="cuda")
-    ls.launch_layer(0, y32=y32, sel=sel)
+    if launch == "fused":
+        ls.prepare_fused(with_f32=True, with_sel=True)
+        ls.step_fused()
+    else:
+        for li, L in enumerate(ls.layers):
+            L["y32"] = torch.empty(mm.dim, dtype=torch.float32, device="cuda")
+            L["sel"] = torch.empty(2, dtype=torch.int32, device="cuda")
+            ls.launch_layer(li, y32=L["y32"], sel=L["sel"])
     torch.cuda.synchronize()
-    L = ls.layers[0]
-    a, b = host(sel).tolist()
-    Q13 = np.zeros((8, 2 * mm.ffn, mm.dim), np.int8)
-    Q2 = np.zeros((8, mm.dim, mm.ffn), np.int8)
-    S13 = np.zeros((8, 2 * mm.ffn), np.uint16)
-    S2 = np.zeros((8, mm.dim), np.uint16)
-    for e in (a, b):
-        q13, s13 = quantize_int8(host(gw(2 * mm.ffn, mm.dim, (0, e, 0))))
-        q2, s2 = quantize_int8(host(gw(mm.dim, mm.ffn, (0, e, 1))))
-        assert np.array_equal(host(L["w13"][e]), q13) and np.array_equal(host_u16(L["s13"][e]), s13)
-        assert np.array_equal(host(L["w2"][e]), q2) and np.array_equal(host_u16(L["s2"][e]), s2)
-        Q13[e], S13[e], Q2[e], S2[e] = q13, s13, q2, s2
-    x = host_u16(L["x"].view(torch.int16))
-    logits = host(L["logits"])
-    ref, sel_ref, _ = moe_top2(x, logits, Q13, S13, Q2, S2)
-    assert tuple(sel_ref) == (a, b)
-    e32 = rel_err(host(y32), ref)
-    e16 = rel_err(bf16_bits_to_f64(host_u16(L["y16"])), ref)
-    say(f"  mixtral layer 0 experts {(a, b)}: err f32={e32:.2e} bf16={e16:.2e}")
-    assert e32 <= TOL_F32 and e16 <= TOL_BF16
+    for li, L in enumerate(ls.layers):
+        a, b = host(L["sel"]).tolist()
+        Q13 = np.zeros((8, 2 * mm.ffn, mm.dim), np.int8)
+        Q2 = np.zeros((8, mm.dim, mm.ffn), np.int8)
+        S13 = np.zeros((8, 2 * mm.ffn), np.uint16)
+        S2 = np.zeros((8, mm.dim), np.uint16)
+        for e in (a, b):
+            q13, s13 = quantize_int8(host(gw(2 * mm.ffn, mm.dim, (li, e, 0))))
+            q2, s2 = quantize_int8(host(gw(mm.dim, mm.ffn, (li, e, 1))))
+            assert np.array_equal(host(L["w13"][e]), q13) and np.array_equal(host_u16(L["s13"][e]), s13)
+            assert np.array_equal(host(L["w2"][e]), q2) and np.array_equal(host_u16(L["s2"][e]), s2)
+            Q13[e], S13[e], Q2[e], S2[e] = q13, s13, q2, s2
+        x = host_u16(L["x"].view(torch.int16))
+        logits = host(L["logits"])
+        ref, sel_ref, _ = moe_top2(x, logits, Q13, S13, Q2, S2)
+        assert tuple(sel_ref) == (a, b)
+        e32 = rel_err(host(L["y32"]), ref)
+        e16 = rel_err(bf16_bits_to_f64(host_u16(L["y16"])), ref)
+        say(f"  mixtral {launch} layer {li} experts {(a, b)}: err f32={e32:.2e} bf16={e16:.2e}")
+        assert e32 <= TOL_F32 and e16 <= TOL_BF16

@@ -143,3 +143,127 @@ def test_moe_argument_errors(wq):
     with pytest.raises(wq.WQError) as ei:
         wq.moe_top2_gemv(buf, buf, 8, buf, buf, buf, buf, 64, 40, buf, y)
     assert ei.value.status == 2
+
+
+def _step_layers(specs, dim, f):
+    """Host inputs for several MoE layers: (x, logits, q13, s13, q2, s2, reference, sel, gates)."""
+    out = []
+    for li, seed in enumerate(specs):
+        q13, s13, q2, s2 = _experts(8, dim, f, seed)
+        x = host_bf16_normal((dim,), 964, seed, li, 1)
+        logits = host_logits(8, 964, seed, li, 2)
+        ref, sel_ref, g_ref = moe_top2(x, logits, q13, s13, q2, s2)
+        out.append((x, logits, q13, s13, q2, s2, ref, tuple(sel_ref), g_ref))
+    return out
+
+
+@pytest.mark.parametrize("dim,f,seeds", [(64, 128, (10, 11, 12)), (1024, 2816, (13, 14)), (48, 4096, (15,)),
+                                         (4096, 512, (16, 17))])
+def test_moe_step_matches_oracle_and_single_layer_calls(wq, dim, f, seeds):
+    """All layers as two persistent launches: every layer's routing, gates and
+    output match the oracle, the single-layer call agrees, runs are bitwise
+    reproducible, also replayed from a captured graph."""
+    import torch
+    say(f"moe step dim={dim} f={f} layers={len(seeds)}")
+    hl = _step_layers(seeds, dim, f)
+    bufs = []
+    for (x, logits, q13, s13, q2, s2, _, _, _) in hl:
+        bufs.append(dict(x=dev(x), logits=dev(logits), w13=dev(q13), s13=dev(s13), w2=dev(q2), s2=dev(s2),
+                         work=torch.empty(2 * f, dtype=torch.float32, device="cuda"),
+                         y32=torch.full((dim,), -7.0, dtype=torch.float32, device="cuda"),
+                         y16=torch.full((dim,), 0x7BAD, dtype=torch.int16, device="cuda"),
+                         sel=torch.full((2,), -1, dtype=torch.int32, device="cuda"),
+                         gates=torch.zeros(2, dtype=torch.float32, device="cuda")))
+    layers = [(b["x"], b["logits"], b["w13"], b["s13"], b["w2"], b["s2"], b["work"], b["y32"], b["y16"], b["sel"],
+               b["gates"]) for b in bufs]
+    ws = torch.empty(max(16, wq.wq_moe_step_workspace_bytes(len(layers))), dtype=torch.uint8, device="cuda")
+    plan = wq.wq_moe_step_prepare(8, dim, f, layers, ws)
+    wq.wq_moe_step_run(plan)
+    torch.cuda.synchronize()
+    first = []
+    for li, (b, h) in enumerate(zip(bufs, hl)):
+        x, logits, q13, s13, q2, s2, ref, sel_ref, g_ref = h
+        assert tuple(host(b["sel"]).tolist()) == sel_ref
+        assert np.allclose(host(b["gates"]), g_ref, rtol=2e-6, atol=0)
+        e = _check(host(b["y32"]), host_u16(b["y16"]), ref)
+        y1, _, _, _ = _run(wq, x, logits, q13, s13, q2, s2, dim, f)
+        assert rel_err(host(b["y32"]), y1) <= 1e-5
+        say(f"  layer {li} sel={sel_ref} err f32={e[0]:.2e} bf16={e[1]:.2e}")
+        first.append(host(b["y32"]).copy())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        wq.wq_moe_step_run(plan)
+    for rep in range(3):
+        for b in bufs:
+            b["y32"].fill_(-7.0)
+        torch.cuda.synchronize()
+        if rep == 0:
+            wq.wq_moe_step_run(plan)
+        else:
+            g.replay()
+        torch.cuda.synchronize()
+        for b, f0 in zip(bufs, first):
+            assert np.array_equal(host(b["y32"]), f0), f"run {rep} differs"
+
+
+def test_moe_step_full_mixtral_shape_unselected_not_read(wq):
+    """Two Mixtral-8x7B-shaped layers through the two-launch step, the
+    unselected experts holding codes that would change the result."""
+    import torch
+    dim, f, e = 4096, 14336, 8
+    say("moe step full mixtral shape")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(965)
+    layers, refs, bufs = [], [], []
+    for li in range(2):
+        q13 = torch.randint(-127, 128, (e, 2 * f, dim), generator=g, device="cuda", dtype=torch.int32).to(torch.int8)
+        q2 = torch.randint(-127, 128, (e, dim, f), generator=g, device="cuda", dtype=torch.int32).to(torch.int8)
+        s13 = ((torch.rand((e, 2 * f), generator=g, device="cuda") + 0.5) * 1.5e-4).to(torch.bfloat16)
+        s2 = ((torch.rand((e, dim), generator=g, device="cuda") + 0.5) * 1.5e-4).to(torch.bfloat16)
+        s13 = s13.view(torch.int16).contiguous()
+        s2 = s2.view(torch.int16).contiguous()
+        x = host_bf16_normal((dim,), 965, li, 0, 1)
+        logits = host_logits(8, 965, li, 0, 2)
+        (a, b), _ = route_top2(logits)
+        Q13 = np.zeros((e, 2 * f, dim), np.int8)
+        Q2 = np.zeros((e, dim, f), np.int8)
+        for i in (a, b):
+            Q13[i] = host(q13[i])
+            Q2[i] = host(q2[i])
+        ref, sel_ref, _ = moe_top2(x, logits, Q13, host_u16(s13), Q2, host_u16(s2))
+        for i in range(e):
+            if i not in (a, b):
+                q13[i].fill_(127)
+                q2[i].fill_(-127)
+        y32 = torch.empty(dim, dtype=torch.float32, device="cuda")
+        sel = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+        work = torch.empty(2 * f, dtype=torch.float32, device="cuda")
+        bufs.append((q13, q2, s13, s2, y32, sel, work))
+        layers.append((dev(x), dev(logits), q13, s13, q2, s2, work, y32, None, sel, None))
+        refs.append((ref, tuple(sel_ref)))
+    ws = torch.empty(max(16, wq.wq_moe_step_workspace_bytes(2)), dtype=torch.uint8, device="cuda")
+    plan = wq.wq_moe_step_prepare(8, dim, f, layers, ws)
+    wq.wq_moe_step_run(plan)
+    torch.cuda.synchronize()
+    for li, ((ref, sel_ref), b) in enumerate(zip(refs, bufs)):
+        assert tuple(host(b[5]).tolist()) == sel_ref
+        e32 = rel_err(host(b[4]), ref)
+        say(f"  layer {li} sel={sel_ref} err f32={e32:.2e}")
+        assert e32 <= TOL_F32
+
+
+def test_moe_step_argument_errors(wq):
+    import torch
+    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    good = (buf, buf, buf, buf, buf, buf, buf, y, None, None, None)
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_moe_step_prepare(8, 64, 40, [good], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_moe_step_prepare(8, 64, 64, [(buf.data_ptr() + 2,) + good[1:]], ws)
+    assert ei.value.status == 3
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_moe_step_prepare(8, 64, 64, [good] * 100, ws, 16)
+    assert ei.value.status == 2

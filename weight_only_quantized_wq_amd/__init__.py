@@ -14,6 +14,7 @@ _EXPORTS = (
     "moe_top2_gemv",
     "WQ_FORMAT", "wq_matrix", "wq_step_plan",
     "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
+    "wq_moe_layer", "wq_moe_plan", "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run",
 )
 
 __all__ = list(_EXPORTS)

@@ -43,6 +43,18 @@ class wq_step_plan(ctypes.Structure):
                 ("groups", ctypes.c_int32), ("total_batches", ctypes.c_int64), ("workspace", ctypes.c_void_p)]
 
 
+class wq_moe_layer(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("w13", ctypes.c_void_p),
+                ("s13", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("s2", ctypes.c_void_p),
+                ("work", ctypes.c_void_p), ("y_f32", ctypes.c_void_p), ("y_bf16", ctypes.c_void_p),
+                ("sel", ctypes.c_void_p), ("gates", ctypes.c_void_p)]
+
+
+class wq_moe_plan(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int64), ("f", ctypes.c_int64), ("e", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("grid13", ctypes.c_int32), ("grid2", ctypes.c_int32), ("workspace", ctypes.c_void_p)]
+
+
 WQ_STATUS = {0: "WQ_OK", 1: "WQ_ERR_NULL", 2: "WQ_ERR_SHAPE", 3: "WQ_ERR_ALIGN", 4: "WQ_ERR_DEVICE",
              5: "WQ_ERR_LAUNCH"}
 
@@ -72,6 +84,13 @@ def _load():
     lib.wq_decode_step_prepare.restype = ctypes.c_int
     lib.wq_decode_step_run.argtypes = [ctypes.POINTER(wq_step_plan), _P]
     lib.wq_decode_step_run.restype = ctypes.c_int
+    lib.wq_moe_step_workspace_bytes.argtypes = [ctypes.c_int32]
+    lib.wq_moe_step_workspace_bytes.restype = ctypes.c_int64
+    lib.wq_moe_step_prepare.argtypes = [_I64, _I64, _I64, ctypes.POINTER(wq_moe_layer), ctypes.c_int32, _P, _I64,
+                                        ctypes.POINTER(wq_moe_plan)]
+    lib.wq_moe_step_prepare.restype = ctypes.c_int
+    lib.wq_moe_step_run.argtypes = [ctypes.POINTER(wq_moe_plan), _P]
+    lib.wq_moe_step_run.restype = ctypes.c_int
     lib.wq_status_string.argtypes = [ctypes.c_int]
     lib.wq_status_string.restype = ctypes.c_char_p
     lib.wq_last_error.argtypes = []
@@ -174,3 +193,28 @@ def wq_decode_step_run(plan, stream=None):
     rc = lib.wq_decode_step_run(ctypes.byref(plan), _stream(stream))
     if rc != 0:
         raise WQError("wq_decode_step_run", rc, lib.wq_last_error().decode(errors="replace"))
+
+
+def wq_moe_step_workspace_bytes(count):
+    return int(lib.wq_moe_step_workspace_bytes(count))
+
+
+def wq_moe_step_prepare(e, dim, f, layers, workspace, workspace_bytes=None):
+    """layers: sequence of (x, logits, w13, s13, w2, s2, work, y_f32, y_bf16, sel, gates) with tensors (or
+    None).  Returns the wq_moe_plan."""
+    arr = (wq_moe_layer * len(layers))()
+    for i, L in enumerate(layers):
+        arr[i] = wq_moe_layer(*[_ptr(t) for t in L])
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    plan = wq_moe_plan()
+    rc = lib.wq_moe_step_prepare(e, dim, f, arr, len(layers), _ptr(workspace), workspace_bytes, ctypes.byref(plan))
+    if rc != 0:
+        raise WQError("wq_moe_step_prepare", rc, lib.wq_last_error().decode(errors="replace"))
+    return plan
+
+
+def wq_moe_step_run(plan, stream=None):
+    rc = lib.wq_moe_step_run(ctypes.byref(plan), _stream(stream))
+    if rc != 0:
+        raise WQError("wq_moe_step_run", rc, lib.wq_last_error().decode(errors="replace"))

@@ -112,6 +112,36 @@ struct FmtInt8 {
     return -128.0f * s;
   }
 
+  // Activations staged in LDS for a whole workgroup: 17 words per chunk over
+  // `cmax` chunks, four 16-byte planes of fp32 values (plane h of chunk c at
+  // word 4 * (h * cmax + c)) followed by the chunk's bias, -128 times the sum
+  // of its 16 values (word 16 * cmax + c).  Chunks at or past `chunks` are
+  // zero.
+  static constexpr int kLdsWordsPerChunk = 17;
+  template <class T>
+  __device__ static void stage(const T* x, int chunks, int c, uint32_t* xs, int cmax) {
+    const X r = load_x(x, c, c < chunks);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<u32x4*>(xs + 4 * (h * cmax + c)) =
+          u32x4{__float_as_uint(r.v[4 * h]), __float_as_uint(r.v[4 * h + 1]), __float_as_uint(r.v[4 * h + 2]),
+                __float_as_uint(r.v[4 * h + 3])};
+    xs[16 * cmax + c] = __float_as_uint(lane_bias(r));
+  }
+  __device__ static X lds_x(const uint32_t* xs, int cmax, int c) {
+    X r;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + 4 * (h * cmax + c));
+      r.v[4 * h] = __uint_as_float(v[0]);
+      r.v[4 * h + 1] = __uint_as_float(v[1]);
+      r.v[4 * h + 2] = __uint_as_float(v[2]);
+      r.v[4 * h + 3] = __uint_as_float(v[3]);
+    }
+    return r;
+  }
+  __device__ static float lds_bias(const uint32_t* xs, int cmax, int c) { return __uint_as_float(xs[16 * cmax + c]); }
+
   struct K {};
   __device__ static K consts() { return K{}; }
   // decoded chunk: u = q + 128 as fp32, one per weight

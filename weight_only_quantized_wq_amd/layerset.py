@@ -161,5 +161,26 @@ class MoELayerSet:
                          L["work"], y32, L["y16"], sel, gates, stream)
 
     def step(self, stream=None):
+        """One decode step as one moe_top2_gemv call (two launches) per layer."""
         for i in range(len(self.layers)):
             self.launch_layer(i, stream)
+
+    def prepare_fused(self, with_f32=False, with_sel=False):
+        """Plans all layers as two persistent launches (wq_moe_step_*)."""
+        dev = self.layers[0]["x"].device
+        for L in self.layers:
+            if with_f32 and L.get("y32") is None:
+                L["y32"] = torch.empty(self.dim, dtype=torch.float32, device=dev)
+            if with_sel and L.get("sel") is None:
+                L["sel"] = torch.empty(2, dtype=torch.int32, device=dev)
+                L["gates"] = torch.empty(2, dtype=torch.float32, device=dev)
+        nbytes = wq.wq_moe_step_workspace_bytes(len(self.layers))
+        self.workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+        layers = [(L["x"], L["logits"], L["w13"], L["s13"], L["w2"], L["s2"], L["work"], L.get("y32"), L["y16"],
+                   L.get("sel"), L.get("gates")) for L in self.layers]
+        self.plan = wq.wq_moe_step_prepare(self.e, self.dim, self.f, layers, self.workspace)
+        return self.plan
+
+    def step_fused(self, stream=None):
+        """One decode step as two persistent launches (call prepare_fused first)."""
+        wq.wq_moe_step_run(self.plan, stream)

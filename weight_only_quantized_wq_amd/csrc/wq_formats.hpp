@@ -46,6 +46,19 @@ struct FmtBf16 {
   }
   __device__ static float lane_bias(const X&) { return 0.0f; }
 
+  // Activations staged in LDS for a whole workgroup: 4 words per chunk (the
+  // 8 bf16 values as loaded), chunk c at word 4 c; chunks at or past
+  // `chunks` are zero.
+  static constexpr int kLdsWordsPerChunk = 4;
+  __device__ static void stage(const uint16_t* x, int chunks, int c, uint32_t* xs, int) {
+    const X r = load_x(x, c, c < chunks);
+    *reinterpret_cast<u32x4*>(xs + 4 * c) = u32x4{r.p[0], r.p[1], r.p[2], r.p[3]};
+  }
+  __device__ static X lds_x(const uint32_t* xs, int, int c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xs + 4 * c);
+    return X{{v[0], v[1], v[2], v[3]}};
+  }
+
   struct K {};
   __device__ static K consts() { return K{}; }
   // decoded chunk: the bf16 pairs as loaded

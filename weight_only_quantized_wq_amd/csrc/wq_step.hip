@@ -95,14 +95,9 @@ static StepVariant verify_variant() {
 static bool pick_variant(int format, int m, StepVariant& v) {
   // chosen by timing candidates on the Llama-2-7B / Llama-3.1-8B / -70B sets
   if (format == WQ_FORMAT_BF16 && m == 1) {
-    v = variant<FmtBf16, 1, 4, 2, 12, true>();
+    v = shared_variant<FmtBf16, 4, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT8 && m == 1) {
-    v = variant<FmtInt8, 1, 4, 4, 12, false>();
-    // on steps that mix row lengths its equal-byte static shares finish up
-    // to ~15% apart: hand out the last 15% of the bytes dynamically (timed;
-    // the bf16 and int4 kernels gain nothing from it)
-    v.tail_frac = 0.15;
-    v.unit_bytes = 64.0 * 1024;
+    v = shared_variant<FmtInt8, 2, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;

@@ -203,8 +203,9 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
  * rounding (the per-row reduction order may differ).
  * Validates every matrix on the host (null -> sizes -> alignment; k must be a
  * positive multiple of 8 / 16 / 32 per format and within the kernel's row
- * limit: int4 with one token row k <= 28672, whose activations are staged
- * whole in LDS; int4 with 3..8 token rows k <= 131072), then writes the launch description into `workspace` (device
+ * limit: with one token row the activations are staged whole in LDS, so
+ * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with two token rows
+ * k <= 32768, with 3..8 token rows k <= 131072), then writes the launch description into `workspace` (device
  * memory, 16-byte aligned, `workspace_bytes` long, caller-owned; it must
  * stay allocated and unmodified while the plan is used).  This copy is
  * synchronous: prepare once, outside any graph capture.  The matrices'

@@ -119,7 +119,10 @@ def test_step_argument_errors():
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 2 ** 20, buf, None)], ws)
     assert ei.value.status == 2
-    # one past the longest int4 row the single-token step kernel stages
+    # one past the longest int8 / int4 rows the single-token step kernel stages
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int8", 1, [(buf, buf, buf, 4, 14352, buf, None)], ws)
+    assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
     assert ei.value.status == 2

@@ -217,7 +217,6 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   a.k = g.k;
   a.groups = (int32_t)(g.k / 32);
   a.blocks = (g.n + 16 * RT - 1) / (16 * RT);
-  a.block_begin = 0;
   const int64_t grid = balanced_grid(a.blocks, resident);
   if (grid <= 0) return WQ_OK;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * kWave), 0, stream, a);

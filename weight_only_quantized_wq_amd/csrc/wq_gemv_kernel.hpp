@@ -207,35 +207,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Whole decode step in one launch.  The step's row batches, matrix after
-// matrix, form one global sequence; the work is handed out in two parts:
-//
-//  * a static part: workgroup g walks the contiguous range
-//    [wg_begin[g], wg_begin[g + 1]) (cut so that every workgroup streams the
-//    same number of weight bytes), starting in matrix wg_mat[g];
-//  * a dynamic tail: the rest of the sequence in units of `unit_batches`
-//    batches, which workgroups claim one at a time from an atomic counter
-//    once their static range is done.  Workgroups that run slower (their
-//    CU's neighbours, their memory channels) claim fewer units, so the
-//    launch does not wait for the slowest static share.  The last workgroup
-//    to finish zeroes the counters for the next launch (no memset needed,
-//    also under graph replay).
-//
-// Per matrix segment a workgroup reads the descriptor, takes its wave roles
-// (split, row groups, chunks per lane <= CPL), loads that matrix's
+// Whole decode step in one launch (two-token rows).  The step's row batches,
+// matrix after matrix, form one global sequence; workgroup g walks the
+// contiguous range [wg_begin[g], wg_begin[g + 1]) (cut so that every
+// workgroup streams the same number of weight bytes), starting in matrix
+// wg_mat[g].  Per matrix segment a workgroup reads the descriptor, takes its
+// wave roles (split, row groups, chunks per lane <= CPL), loads that matrix's
 // activations and streams its batches; waves without a row group in a matrix
 // only join the split-K barriers.
-struct StepTail {
-  int32_t next;          // next unit to claim (reset to 0 by the last workgroup)
-  int32_t done;          // workgroups finished (reset to 0 by the last one)
-  int32_t units;         // units in the dynamic tail (0: none)
-  int32_t pad;
-  int64_t start;         // first global batch of the tail
-  int64_t unit_batches;  // batches per unit
-  int64_t total;         // batches in the step
-  // followed by int32 unit_mat[units]: the matrix holding each unit's first batch
-};
-
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 __device__ __forceinline__ void step_range(const GemvArgs* __restrict__ mats, int64_t gb, const int64_t gend, int mi,
                                            float (&red)[2][WAVES][U * M], int& buf) {
@@ -300,40 +279,11 @@ __device__ __forceinline__ void step_range(const GemvArgs* __restrict__ mats, in
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 __global__ __launch_bounds__(WAVES * 64) void gemv_step_kernel(const GemvArgs* __restrict__ mats,
                                                                const int64_t* __restrict__ wg_begin,
-                                                               const int32_t* __restrict__ wg_mat,
-                                                               StepTail* __restrict__ tail) {
+                                                               const int32_t* __restrict__ wg_mat) {
   __shared__ float red[2][WAVES][U * M];
-  __shared__ int32_t claimed;
   int buf = 0;
   step_range<F, M, CPL, U, WAVES, PF>(mats, wg_begin[blockIdx.x], wg_begin[blockIdx.x + 1], wg_mat[blockIdx.x], red,
                                       buf);
-  const int32_t units = tail->units;
-  if (units > 0) {
-    const int32_t* unit_mat = reinterpret_cast<const int32_t*>(tail + 1);
-    // thread 0 claims the following unit as soon as it starts on one, so the
-    // claim's round trip overlaps the unit's own loads
-    int32_t next_claim = 0;
-    if (threadIdx.x == 0) next_claim = atomicAdd(&tail->next, 1);
-    for (;;) {
-      if (threadIdx.x == 0) claimed = next_claim;
-      __syncthreads();
-      const int32_t u = claimed;
-      __syncthreads();                   // every wave has read `claimed`
-      if (u >= units) break;
-      if (threadIdx.x == 0) next_claim = atomicAdd(&tail->next, 1);
-      const int64_t ub = tail->start + (int64_t)u * tail->unit_batches;
-      const int64_t ue = ub + tail->unit_batches < tail->total ? ub + tail->unit_batches : tail->total;
-      step_range<F, M, CPL, U, WAVES, PF>(mats, ub, ue, unit_mat[u], red, buf);
-    }
-  }
-  if (threadIdx.x == 0) {
-    // every claim of this workgroup has returned; the last workgroup to get
-    // here knows all claims of the launch are over
-    if (atomicAdd(&tail->done, 1) == (int32_t)gridDim.x - 1) {
-      atomicExch(&tail->next, 0);
-      atomicExch(&tail->done, 0);
-    }
-  }
 }
 
 }  // namespace wq

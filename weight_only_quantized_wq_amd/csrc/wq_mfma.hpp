@@ -46,7 +46,6 @@ struct MfmaArgs {
   int64_t n;
   int64_t k;
   int64_t blocks;        // ceil(n / (16 * RT))
-  int64_t block_begin;   // first global block of this matrix (decode step)
   int32_t groups;        // k / 32
 };
 
@@ -181,7 +180,6 @@ __device__ __forceinline__ MfmaArgs uniform_args(const MfmaArgs& a) {
   u.n = uniform64(a.n);
   u.k = uniform64(a.k);
   u.blocks = uniform64(a.blocks);
-  u.block_begin = uniform64(a.block_begin);
   u.groups = __builtin_amdgcn_readfirstlane(a.groups);
   return u;
 }
@@ -333,26 +331,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_mfma_kernel(MfmaArgs a) {
   __shared__ MfmaShared<M, RT, KW, WAVES> sh;
   if (threadIdx.x < 16) sh.zero[threadIdx.x] = 0u;
   mfma_blocks<M, RT, KW, WAVES, PF, OCT>(a, blockIdx.x, a.blocks, gridDim.x, sh);
-}
-
-// A whole decode step: the blocks of all matrices in one global order
-// (matrix by matrix), workgroup g taking the contiguous range
-// [wg_begin[g], wg_begin[g + 1]) that starts in matrix wg_mat[g].
-template <int M, int RT, int KW, int WAVES, int PF, int OCT>
-__global__ __launch_bounds__(WAVES * 64) void gemm_mfma_step_kernel(const MfmaArgs* __restrict__ mats,
-                                                                    const int64_t* __restrict__ wg_begin,
-                                                                    const int32_t* __restrict__ wg_mat) {
-  __shared__ MfmaShared<M, RT, KW, WAVES> sh;
-  if (threadIdx.x < 16) sh.zero[threadIdx.x] = 0u;
-  const int64_t b0 = wg_begin[blockIdx.x];
-  const int64_t b1 = wg_begin[blockIdx.x + 1];
-  int mi = wg_mat[blockIdx.x];
-  for (int64_t b = b0; b < b1; ++mi) {
-    const MfmaArgs a = mats[mi];
-    const int64_t hi = (a.block_begin + a.blocks) < b1 ? (a.block_begin + a.blocks) : b1;
-    if (hi > b) mfma_blocks<M, RT, KW, WAVES, PF, OCT>(a, b - a.block_begin, hi - a.block_begin, 1, sh);
-    b = hi > b ? hi : b;
-  }
 }
 
 }  // namespace wq

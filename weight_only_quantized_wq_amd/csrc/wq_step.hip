@@ -7,49 +7,41 @@
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
-#include "wq_mfma.hpp"
 #include "wq_step_shared.hpp"
 #include "wq_verify.hpp"
 
 namespace wq {
 
 // One persistent kernel configuration per (format, tokens per pass): the
-// largest chunks-per-lane any matrix may use (registers are sized for it),
-// waves per workgroup, rows per wave per batch and prefetch; or, for int4
-// with 3..8 tokens, the matrix-core kernel (batch = one block of rows).
+// largest chunks per lane a pass uses, waves per workgroup and rows per wave
+// per batch, and which kernel: the shared-activation kernel (one format,
+// one token row; batch = u rows of one wave), the matrix-core verify kernel
+// (int4, 3..8 token rows; batch = u rows in 16-row tiles) or the register
+// kernel (int4, two token rows; batch = u rows per row group).
 struct StepVariant {
   int cpl_max;
   int waves;
   int u;
   const void* kernel;
-  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, StepTail*, hipStream_t);
-  bool mfma;   // int4 with 3..8 tokens: the matrix-core step kernel
-  int cmax;    // > 0: the shared-activation kernel (batch = u rows of one wave),
-               // staging at most cmax chunks of a row
-  bool verify; // int4 with 2..8 tokens on the matrix cores, weights as the B
-               // operand (batch = one 16-row tile)
-  // dynamic tail (VALU kernel): fraction of the step's bytes handed out in
-  // units of about `unit_bytes`; 0 = all static
-  double tail_frac;
-  double unit_bytes;
+  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, hipStream_t);
+  int cmax;    // > 0: the shared-activation kernel, staging at most cmax chunks of a row
+  bool verify; // the matrix-core verify kernel
 };
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail* tail,
-                        hipStream_t stream) {
+static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat, tail);
+                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
 }
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 static StepVariant variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>, false, 0, false, 0.0, 0.0};
+                     &step_launch<F, M, CPL, U, WAVES, PF>, 0, false};
 }
 
 template <class F, int U, int CPL, int WAVES, bool PF>
-static void shared_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
-                          hipStream_t stream) {
+static void shared_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_shared_kernel<F, U, CPL, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                      stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
 }
@@ -57,30 +49,13 @@ static void shared_launch(int grid, const void* mats, const int64_t* begin, cons
 template <class F, int U, int CPL, int WAVES, bool PF>
 static StepVariant shared_variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_shared_kernel<F, U, CPL, WAVES, PF>),
-                     &shared_launch<F, U, CPL, WAVES, PF>, false, shared_x_cmax<F, CPL>(), false, 0.0, 0.0};
-}
-
-template <int M>
-static void mfma_step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
-                     dim3((unsigned)grid), dim3(kMfmaWaves * 64), 0, stream, reinterpret_cast<const MfmaArgs*>(mats),
-                     begin, mat);
-}
-
-template <int M>
-static StepVariant mfma_variant() {
-  return StepVariant{0, kMfmaWaves, 16 * kMfmaRT,
-                     reinterpret_cast<const void*>(
-                         gemm_mfma_step_kernel<M, kMfmaRT, kMfmaKW, kMfmaWaves, kMfmaPF, kMfmaOct>),
-                     &mfma_step_launch<M>, true, 0, false, 0.0, 0.0};
+                     &shared_launch<F, U, CPL, WAVES, PF>, shared_x_cmax<F, CPL>(), false};
 }
 
 constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 
 template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL>
-static void verify_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, StepTail*,
-                          hipStream_t stream) {
+static void verify_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>), dim3((unsigned)grid),
                      dim3(WAVES * 64), 0, stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
 }
@@ -89,7 +64,7 @@ template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, i
 static StepVariant verify_variant() {
   return StepVariant{1, WAVES, 16 * RT,
                      reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>),
-                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL>, false, 0, true, 0.0, 0.0};
+                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL>, 0, true};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -126,22 +101,10 @@ static int64_t row_bytes_of(int format, int64_t k) {
 
 constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
 
-// per-matrix descriptor slot: large enough for either kernel's descriptor
-constexpr size_t kDescBytes = ((sizeof(GemvArgs) > sizeof(MfmaArgs) ? sizeof(GemvArgs) : sizeof(MfmaArgs)) + 15) / 16 * 16;
-
-// Units of the dynamic tail (at most kMaxUnits per plan).
-constexpr int64_t kMaxUnits = 65536;
-
-// Workspace layout: descriptors, static range starts (groups + 1), first
-// matrix per range (groups), then at a 16-byte boundary the tail header and
-// the matrix of each tail unit.
-static size_t tail_offset(size_t desc_bytes, int64_t count, int64_t groups) {
-  const size_t off_first = (size_t)count * desc_bytes + ((size_t)groups + 1) * 8;
-  return (off_first + (size_t)groups * 4 + 15) / 16 * 16;
-}
-
+// Workspace layout: per-matrix descriptors, then the range starts of the
+// workgroups (groups + 1) and the first matrix of each range (groups).
 static int64_t workspace_need(int64_t count, int64_t groups) {
-  return (int64_t)tail_offset(kDescBytes, count, groups) + (int64_t)sizeof(StepTail) + 4 * kMaxUnits + 64;
+  return count * (int64_t)sizeof(GemvArgs) + (groups + 1) * 8 + groups * 4 + 16;
 }
 
 }  // namespace wq
@@ -176,10 +139,10 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
                   name, i, (long long)mt.n, (long long)mt.k, wpc);
     const int64_t chunks = mt.k / wpc;
-    const int64_t per_wave_max = (int64_t)kWave * (v.mfma ? 1 : v.cpl_max);
-    const int64_t split = v.mfma || v.cmax || v.verify ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
+    const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
+    const int64_t split = v.cmax || v.verify ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
-    if (split > v.waves || ((v.mfma || v.verify) && mt.k > kMfmaMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
+    if (split > v.waves || (v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -202,9 +165,9 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     // the shared-activation kernel streams a row in `passes` passes of cpl_max
     // chunks per lane
     a.cpl = v.cmax ? (int32_t)passes : (int32_t)((chunks + split * kWave - 1) / (split * kWave));
-    // the matrix-core kernel's batch is one block of 16 * RT rows; the
-    // shared-activation kernel's is u rows of one wave
-    const int64_t rows_per_batch = v.mfma || v.cmax || v.verify ? (int64_t)v.u : (int64_t)a.groups * v.u;
+    // the verify kernel's batch is a block of 16-row tiles, the
+    // shared-activation kernel's u rows of one wave
+    const int64_t rows_per_batch = v.cmax || v.verify ? (int64_t)v.u : (int64_t)a.groups * v.u;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -257,74 +220,24 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     return lo;
   };
 
-  // Static part: [0, static_end) cut into `groups` equal-byte ranges; the
-  // rest (for variants with a dynamic tail) is handed out in units.
-  // Equal bytes take equal time only when the matrices share a shape; a
-  // step that mixes row lengths streams them at different rates, so part of
-  // it is handed out dynamically (variants with a tail only).
-  bool mixed = false;
-  for (int32_t i = 1; i < count; ++i) mixed = mixed || desc[(size_t)i].k != desc[0].k;
-  const bool dynamic = !v.mfma && !v.cmax && !v.verify && groups > 1 && v.tail_frac > 0.0 && mixed;
-  const double static_bytes = dynamic ? total * (1.0 - v.tail_frac) : total;
-  const int64_t static_end = dynamic ? batch_at(static_bytes) : total_batches;
+  // [0, total_batches) cut into `groups` ranges of equal cost
   std::vector<int64_t> begin((size_t)groups + 1);
   std::vector<int32_t> first((size_t)groups);
   for (int g = 0; g <= groups; ++g) {
-    int64_t gb = g == groups ? static_end : batch_at(static_bytes * (double)g / (double)groups);
-    if (gb > static_end) gb = static_end;
+    int64_t gb = g == groups ? total_batches : batch_at(total * (double)g / (double)groups);
+    if (gb > total_batches) gb = total_batches;
     if (g > 0 && gb < begin[(size_t)g - 1]) gb = begin[(size_t)g - 1];
     begin[(size_t)g] = gb;
   }
   for (int g = 0; g < groups; ++g) first[(size_t)g] = matrix_of(begin[(size_t)g]);
 
-  StepTail tail{};
-  std::vector<int32_t> unit_mat;
-  if (dynamic && static_end < total_batches) {
-    const int64_t left = total_batches - static_end;
-    const double avg = (total - static_bytes) / (double)left;   // bytes per tail batch
-    int64_t ub = (int64_t)(v.unit_bytes / avg + 0.5);
-    if (ub < 1) ub = 1;
-    if ((left + ub - 1) / ub > kMaxUnits) ub = (left + kMaxUnits - 1) / kMaxUnits;
-    tail.units = (int32_t)((left + ub - 1) / ub);
-    tail.start = static_end;
-    tail.unit_batches = ub;
-    tail.total = total_batches;
-    unit_mat.resize((size_t)tail.units);
-    for (int32_t u = 0; u < tail.units; ++u) unit_mat[(size_t)u] = matrix_of(static_end + (int64_t)u * ub);
-  }
-
-  char* ws = reinterpret_cast<char*>(workspace);
-  const size_t desc_bytes = v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs);
-  const size_t off_begin = (size_t)count * desc_bytes;
+  const size_t off_begin = (size_t)count * sizeof(GemvArgs);
   const size_t off_first = off_begin + ((size_t)groups + 1) * 8;
-  const size_t off_tail = tail_offset(desc_bytes, count, groups);
-  std::vector<char> host(off_tail + sizeof(StepTail) + unit_mat.size() * 4, 0);
-  if (v.mfma) {
-    std::vector<MfmaArgs> md((size_t)count);
-    for (int32_t i = 0; i < count; ++i) {
-      const GemvArgs& g = desc[(size_t)i];
-      MfmaArgs& a = md[(size_t)i];
-      a = MfmaArgs{};
-      a.x = g.x;
-      a.w = g.w;
-      a.sz = g.sz;
-      a.y32 = g.y32;
-      a.y16 = g.y16;
-      a.n = g.n;
-      a.k = g.k;
-      a.groups = (int32_t)(g.k / 32);
-      a.blocks = g.batches;
-      a.block_begin = g.batch_begin;
-    }
-    memcpy(host.data(), md.data(), off_begin);
-  } else {
-    memcpy(host.data(), desc.data(), off_begin);
-  }
+  std::vector<char> host(off_first + (size_t)groups * 4, 0);
+  memcpy(host.data(), desc.data(), off_begin);
   memcpy(host.data() + off_begin, begin.data(), ((size_t)groups + 1) * 8);
   memcpy(host.data() + off_first, first.data(), (size_t)groups * 4);
-  memcpy(host.data() + off_tail, &tail, sizeof(StepTail));
-  if (!unit_mat.empty()) memcpy(host.data() + off_tail + sizeof(StepTail), unit_mat.data(), unit_mat.size() * 4);
-  hipError_t e = hipMemcpy(ws, host.data(), host.size(), hipMemcpyHostToDevice);
+  hipError_t e = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return fail(WQ_ERR_LAUNCH, "%s: copying the plan to the workspace failed: %s", name, hipGetErrorString(e));
@@ -348,12 +261,9 @@ extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
   int rc = check_device();
   if (rc) return rc;
   char* ws = reinterpret_cast<char*>(const_cast<void*>(plan->workspace));
-  const size_t desc_bytes = v.mfma ? sizeof(MfmaArgs) : sizeof(GemvArgs);
-  const size_t off_begin = (size_t)plan->count * desc_bytes;
+  const size_t off_begin = (size_t)plan->count * sizeof(GemvArgs);
   const size_t off_first = off_begin + ((size_t)plan->groups + 1) * 8;
-  const size_t off_tail = tail_offset(desc_bytes, plan->count, plan->groups);
   v.launch(plan->groups, ws, reinterpret_cast<const int64_t*>(ws + off_begin),
-           reinterpret_cast<const int32_t*>(ws + off_first), reinterpret_cast<StepTail*>(ws + off_tail),
-           (hipStream_t)stream);
+           reinterpret_cast<const int32_t*>(ws + off_first), (hipStream_t)stream);
   return launch_status(name);
 }

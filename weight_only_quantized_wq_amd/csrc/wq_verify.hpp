@@ -40,6 +40,9 @@
 
 namespace wq {
 
+// Longest row (inputs) the verify kernel accepts (offsets stay in 32 bits).
+constexpr int kVerifyMaxK = 131072;
+
 typedef __bf16 vbf16x8 __attribute__((ext_vector_type(8)));
 typedef float vf32x4 __attribute__((ext_vector_type(4)));
 

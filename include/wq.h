@@ -215,7 +215,10 @@ int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int
                            void* workspace, int64_t workspace_bytes, wq_step_plan* plan);
 
 /* Launches a prepared step on `stream` (asynchronous; may be captured into a
- * HIP graph).  Concurrent runs of plans that share output buffers race. */
+ * HIP graph).  Runs of one plan must not overlap (they share its workspace,
+ * which for one-token steps also carries the XCD speed weights that each run
+ * measures and the next run uses to cut the step into per-CU ranges); runs
+ * of plans that share output buffers race. */
 int wq_decode_step_run(const wq_step_plan* plan, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -106,6 +106,16 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
+// A value the caller knows to be equal in every lane, as a wave-uniform
+// (scalar) value: descriptors and buffer resources built from it stay in
+// scalar registers instead of becoming per-lane loops.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 

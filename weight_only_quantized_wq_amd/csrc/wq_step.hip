@@ -18,20 +18,28 @@ namespace wq {
 // one token row; batch = u rows of one wave), the matrix-core verify kernel
 // (int4, 3..8 token rows; batch = u rows in 16-row tiles) or the register
 // kernel (int4, two token rows; batch = u rows per row group).
+// Device pointers of a prepared plan's workspace.
+struct StepLaunch {
+  const GemvArgs* mats;
+  const int64_t* begin;   // range starts (groups + 1), cut on the host
+  const int32_t* first;   // first matrix of each range
+  StepCuts cuts;          // cost prefix and XCD balance (shared-activation kernel)
+};
+
 struct StepVariant {
   int cpl_max;
   int waves;
   int u;
   const void* kernel;
-  void (*launch)(int grid, const void*, const int64_t*, const int32_t*, hipStream_t);
+  void (*launch)(int grid, const StepLaunch&, hipStream_t);
   int cmax;    // > 0: the shared-activation kernel, staging at most cmax chunks of a row
   bool verify; // the matrix-core verify kernel
 };
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static void step_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
+static void step_launch(int grid, const StepLaunch& l, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+                     stream, l.mats, l.begin, l.first);
 }
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
@@ -41,9 +49,9 @@ static StepVariant variant() {
 }
 
 template <class F, int U, int CPL, int WAVES, bool PF>
-static void shared_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
+static void shared_launch(int grid, const StepLaunch& l, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_step_shared_kernel<F, U, CPL, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+                     stream, l.mats, l.cuts);
 }
 
 template <class F, int U, int CPL, int WAVES, bool PF>
@@ -55,9 +63,9 @@ static StepVariant shared_variant() {
 constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 
 template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL>
-static void verify_launch(int grid, const void* mats, const int64_t* begin, const int32_t* mat, hipStream_t stream) {
+static void verify_launch(int grid, const StepLaunch& l, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>), dim3((unsigned)grid),
-                     dim3(WAVES * 64), 0, stream, reinterpret_cast<const GemvArgs*>(mats), begin, mat);
+                     dim3(WAVES * 64), 0, stream, l.mats, l.begin, l.first);
 }
 
 template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool QL = true>
@@ -101,10 +109,41 @@ static int64_t row_bytes_of(int format, int64_t k) {
 
 constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
 
-// Workspace layout: per-matrix descriptors, then the range starts of the
-// workgroups (groups + 1) and the first matrix of each range (groups).
-static int64_t workspace_need(int64_t count, int64_t groups) {
-  return count * (int64_t)sizeof(GemvArgs) + (groups + 1) * 8 + groups * 4 + 16;
+// Workspace layout: per-matrix descriptors, the range starts of the
+// workgroups (groups + 1) and the first matrix of each range (groups), the
+// step's cost before each matrix (count + 1) and per batch of each matrix
+// (count), then the XCD balance state.
+struct StepLayout {
+  size_t begin, first, prefix, bcost, bal, end;
+};
+
+static StepLayout step_layout(int64_t count, int64_t groups) {
+  auto up16 = [](size_t v) { return (v + 15) / 16 * 16; };
+  StepLayout l;
+  l.begin = up16((size_t)count * sizeof(GemvArgs));
+  l.first = l.begin + ((size_t)groups + 1) * 8;
+  l.prefix = up16(l.first + (size_t)groups * 4);
+  l.bcost = l.prefix + ((size_t)count + 1) * 8;
+  l.bal = up16(l.bcost + (size_t)count * 8);
+  l.end = l.bal + sizeof(StepBalance);
+  return l;
+}
+
+static int64_t workspace_need(int64_t count, int64_t groups) { return (int64_t)step_layout(count, groups).end; }
+
+static StepLaunch launch_view(void* workspace, int32_t count, int32_t groups, int64_t total) {
+  char* ws = reinterpret_cast<char*>(workspace);
+  const StepLayout l = step_layout(count, groups);
+  StepLaunch v;
+  v.mats = reinterpret_cast<const GemvArgs*>(ws);
+  v.begin = reinterpret_cast<const int64_t*>(ws + l.begin);
+  v.first = reinterpret_cast<const int32_t*>(ws + l.first);
+  v.cuts.prefix = reinterpret_cast<const double*>(ws + l.prefix);
+  v.cuts.bcost = reinterpret_cast<const double*>(ws + l.bcost);
+  v.cuts.bal = reinterpret_cast<StepBalance*>(ws + l.bal);
+  v.cuts.total = total;
+  v.cuts.count = count;
+  return v;
 }
 
 }  // namespace wq
@@ -231,12 +270,19 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   }
   for (int g = 0; g < groups; ++g) first[(size_t)g] = matrix_of(begin[(size_t)g]);
 
-  const size_t off_begin = (size_t)count * sizeof(GemvArgs);
-  const size_t off_first = off_begin + ((size_t)groups + 1) * 8;
-  std::vector<char> host(off_first + (size_t)groups * 4, 0);
-  memcpy(host.data(), desc.data(), off_begin);
-  memcpy(host.data() + off_begin, begin.data(), ((size_t)groups + 1) * 8);
-  memcpy(host.data() + off_first, first.data(), (size_t)groups * 4);
+  const StepLayout lay = step_layout(count, groups);
+  std::vector<char> host(lay.end, 0);
+  memcpy(host.data(), desc.data(), (size_t)count * sizeof(GemvArgs));
+  memcpy(host.data() + lay.begin, begin.data(), ((size_t)groups + 1) * 8);
+  memcpy(host.data() + lay.first, first.data(), (size_t)groups * 4);
+  std::vector<double> prefix((size_t)count + 1, 0.0);
+  for (int32_t i = 0; i < count; ++i)
+    prefix[(size_t)i + 1] = prefix[(size_t)i] + batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
+  memcpy(host.data() + lay.prefix, prefix.data(), prefix.size() * 8);
+  memcpy(host.data() + lay.bcost, batch_bytes.data(), (size_t)count * 8);
+  StepBalance bal{};
+  for (int x = 0; x < 8; ++x) bal.w[x] = 1.0f;
+  memcpy(host.data() + lay.bal, &bal, sizeof(bal));
   hipError_t e = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -260,10 +306,7 @@ extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
     return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_decode_step_prepare", name);
   int rc = check_device();
   if (rc) return rc;
-  char* ws = reinterpret_cast<char*>(const_cast<void*>(plan->workspace));
-  const size_t off_begin = (size_t)plan->count * sizeof(GemvArgs);
-  const size_t off_first = off_begin + ((size_t)plan->groups + 1) * 8;
-  v.launch(plan->groups, ws, reinterpret_cast<const int64_t*>(ws + off_begin),
-           reinterpret_cast<const int32_t*>(ws + off_first), (hipStream_t)stream);
+  const StepLaunch l = launch_view(const_cast<void*>(plan->workspace), plan->count, plan->groups, plan->total_batches);
+  v.launch(plan->groups, l, (hipStream_t)stream);
   return launch_status(name);
 }

@@ -2,10 +2,11 @@
 //
 // A batch-1 decode step streams every linear layer once.  This persistent
 // kernel covers a whole step in one launch:
-//   * each workgroup owns a contiguous range of the step's row batches, cut
-//     on the host so that every workgroup streams the same number of weight
-//     bytes (one workgroup per CU: waves of one CU never compete across
-//     workgroups, whose issue priority follows dispatch order);
+//   * each workgroup owns a contiguous range of the step's row batches, of
+//     equal cost on the first launch and then proportional to the measured
+//     speed of its XCD (see StepBalance); one workgroup per CU, so waves of
+//     one CU never compete across workgroups, whose issue priority follows
+//     dispatch order;
 //   * per matrix segment of its range the workgroup stages that matrix's
 //     activations ONCE into LDS in the format's pre-decoded form, so a single
 //     wave can cover a row of any length -- no split-K, no cross-wave
@@ -180,22 +181,100 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
   }
 }
 
+// Load balance across XCDs.  Workgroup g runs on XCD g mod 8 (workgroups
+// are dispatched to the XCDs round robin), and under this kernel's mix of
+// streaming and arithmetic the XCDs of one device finish equal shares up to
+// ~8 % apart.  So each launch measures, per XCD, the cost its workgroups
+// streamed and the time they took; the last workgroup to finish turns that
+// into relative speeds (a quarter of the new measurement per launch, clamped
+// to [0.7, 1.3]) and the next launch
+// cuts the step into ranges proportional to them.  Which workgroup computes a
+// row never changes the row's result.
+struct StepBalance {
+  float w[8];      // relative speed of each XCD's workgroups (mean 1)
+  float cost[8];   // this launch: cost streamed by each XCD's workgroups
+  float time[8];   // this launch: their summed durations (wall-clock ticks)
+  int32_t done;    // workgroups finished in this launch
+  int32_t pad[7];
+};
+
+struct StepCuts {
+  const double* prefix;   // [count + 1] cost of the step before matrix i
+  const double* bcost;    // [count] cost of one batch of matrix i
+  StepBalance* bal;
+  int64_t total;          // batches in the step
+  int32_t count;          // matrices
+};
+
+// Cost at which workgroup g's range starts: the step's cost times the share
+// of the speed weights of workgroups 0 .. g-1.
+__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int g, int groups) {
+  double sw = 0.0, part = 0.0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    sw += (double)w[x];
+    if (x < g % 8) part += (double)w[x];
+  }
+  double full = 0.0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+    if (x < groups % 8) full += (double)w[x];
+  const double before = (double)(g / 8) * sw + part;
+  const double all = (double)(groups / 8) * sw + full;
+  return c.prefix[c.count] * (before / all);
+}
+
 // mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of
-// passes per row); wg_begin[g] .. wg_begin[g + 1]: workgroup g's global
-// batches, starting in matrix wg_mat[g].
+// passes per row).  Each workgroup cuts its own contiguous range of the
+// step's batches from the cost prefix and the XCD speed weights.
 template <class F, int U, int CPL, int WAVES, bool PF>
 __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const GemvArgs* __restrict__ mats,
-                                                                      const int64_t* __restrict__ wg_begin,
-                                                                      const int32_t* __restrict__ wg_mat) {
+                                                                      StepCuts cuts) {
   constexpr int CMAX = shared_x_cmax<F, CPL>();
   __shared__ __attribute__((aligned(16))) uint32_t xs[kSharedXWords];
   __shared__ int ctr;
+  __shared__ int64_t range[2];
+  __shared__ int first_mat;
   const int lane = lane_id();
-  int64_t gb = wg_begin[blockIdx.x];
-  const int64_t gend = wg_begin[blockIdx.x + 1];
-  int mi = wg_mat[blockIdx.x];
+  const long long t_start = wall_clock64();
+  float w[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) w[x] = cuts.bal->w[x];
+  const int G = (int)gridDim.x;
+  const double c0 = cut_cost(cuts, w, (int)blockIdx.x, G);
+  const double c1 = (int)blockIdx.x + 1 == G ? cuts.prefix[cuts.count] : cut_cost(cuts, w, (int)blockIdx.x + 1, G);
+  // the batch at cost c: first batch of matrix i (prefix[i] <= c < prefix[i + 1])
+  // whose start is at or past c; every matrix is checked by one thread
+  if (threadIdx.x == 0) {
+    range[0] = cuts.total;
+    range[1] = cuts.total;
+    first_mat = cuts.count - 1;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < cuts.count; i += WAVES * kWave) {
+    const double p0 = cuts.prefix[i], p1 = cuts.prefix[i + 1];
+    const GemvArgs& m = mats[i];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const double c = e == 0 ? c0 : c1;
+      if (p0 <= c && c < p1) {
+        int64_t local = (int64_t)((c - p0) / cuts.bcost[i] + 0.999999);
+        if (local > m.batches) local = m.batches;
+        range[e] = m.batch_begin + local;
+        if (e == 0) first_mat = i;
+      }
+    }
+  }
+  __syncthreads();
+  int64_t gb = uniform_i64(range[0]);
+  const int64_t gend = uniform_i64(range[1]);
+  int mi = __builtin_amdgcn_readfirstlane(first_mat);
   while (gb < gend) {
-    const GemvArgs a = mats[mi];
+    GemvArgs a = mats[mi];
+    if (gb >= a.batch_begin + a.batches) {   // the range starts at the next matrix
+      ++mi;
+      continue;
+    }
     const int64_t mend = a.batch_begin + a.batches;
     const int64_t lb = gb - a.batch_begin;
     const int64_t le = (gend < mend ? gend : mend) - a.batch_begin;
@@ -207,6 +286,45 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
     stream_segment<F, U, CPL, CMAX, PF>(a, lb, le, xs, &ctr, lane);
     gb = a.batch_begin + le;
     ++mi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    StepBalance* b = cuts.bal;
+    const int x = (int)(blockIdx.x % 8);
+    atomicAdd(&b->cost[x], (float)(c1 - c0));
+    atomicAdd(&b->time[x], (float)(wall_clock64() - t_start));
+    __threadfence();
+    if (atomicAdd(&b->done, 1) == G - 1) {
+      // every workgroup has reported: new speed weights for the next launch
+      __threadfence();
+      float r[8], wn[8];
+      float mean = 0.0f;
+      int n = 0;
+      for (int y = 0; y < 8; ++y) {
+        const float cy = __hip_atomic_load(&b->cost[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float ty = __hip_atomic_load(&b->time[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        r[y] = (ty > 0.0f && cy > 0.0f) ? cy / ty : 0.0f;
+        if (r[y] > 0.0f) {
+          mean += r[y];
+          ++n;
+        }
+      }
+      mean = n ? mean / (float)n : 0.0f;
+      float sw = 0.0f;
+      for (int y = 0; y < 8; ++y) {
+        float v = w[y];
+        if (mean > 0.0f && r[y] > 0.0f) v = 0.75f * w[y] + 0.25f * (r[y] / mean);
+        v = fminf(fmaxf(v, 0.7f), 1.3f);
+        wn[y] = v;
+        sw += v;
+      }
+      for (int y = 0; y < 8; ++y) {
+        atomicExch(&b->w[y], wn[y] * 8.0f / sw);
+        atomicExch(&b->cost[y], 0.0f);
+        atomicExch(&b->time[y], 0.0f);
+      }
+      atomicExch(&b->done, 0);
+    }
   }
 }
 

@@ -29,15 +29,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------------------
+// Global-memory views of device pointers.  Pointers read from descriptors in
+// memory are generic, and generic accesses compile to FLAT instructions.  A
+// FLAT access may target LDS, so while one is outstanding the compiler's
+// wait insertion can no longer count vector loads separately and waits for
+// ALL of them (vmcnt(0)) before any loaded value is used -- which drains a
+// software prefetch pipeline at every such point.  Every pointer the kernels
+// dereference outside LDS is global memory, and goes through gmem().
+
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+
+// ---------------------------------------------------------------------------
 // Streaming loads: weights are read exactly once per product, so they are
 // fetched with the nontemporal hint and do not displace x or other data.
 
 __device__ __forceinline__ u32x4 load_stream16(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load(gmem(reinterpret_cast<const u32x4*>(p)));
 }
-__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 load16(const void* p) { return *gmem(reinterpret_cast<const u32x4*>(p)); }
 __device__ __forceinline__ uint32_t load_stream4(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  return __builtin_nontemporal_load(gmem(reinterpret_cast<const uint32_t*>(p)));
 }
 
 // Buffer resource over [base, base + bytes): loads at offsets past `bytes`

@@ -143,9 +143,9 @@ __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int l
     const int m = lane - u * M;
     const int64_t r = r0 + u;
     if (r < a.n) {
-      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)a.scale[r] << 16);
-      if (a.y32) a.y32[m * a.n + r] = v;
-      if (a.y16) a.y16[m * a.n + r] = f32_to_bf16(v);
+      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)*gmem(a.scale + r) << 16);
+      if (a.y32) *gmem(a.y32 + (m * a.n + r)) = v;
+      if (a.y16) *gmem(a.y16 + (m * a.n + r)) = f32_to_bf16(v);
     }
   }
 }

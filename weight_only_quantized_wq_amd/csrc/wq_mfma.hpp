@@ -318,8 +318,8 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
         float v = sh.red[0][rt][s][r][c16];
 #pragma unroll
         for (int w = 1; w < WAVES; ++w) v += sh.red[w][rt][s][r][c16];
-        if (a.y32) a.y32[(int64_t)t * a.n + row] = v;
-        if (a.y16) a.y16[(int64_t)t * a.n + row] = f32_to_bf16(v);
+        if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = v;
+        if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(v);
       }
     }
   }

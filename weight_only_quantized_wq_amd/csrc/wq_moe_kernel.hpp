@@ -32,7 +32,8 @@ struct MoeArgs {
 
 // Top-2 of the logits (equal values -> lower index) and the pair's
 // renormalised softmax gates g_a = 1 / (1 + exp(l_b - l_a)), g_b = 1 - g_a.
-__device__ __forceinline__ void route_top2(const float* logits, int e, int& a, int& b, float& ga, float& gb) {
+__device__ __forceinline__ void route_top2(const float* logits_ptr, int e, int& a, int& b, float& ga, float& gb) {
+  const __attribute__((address_space(1))) float* logits = gmem(logits_ptr);
   a = 0;
   for (int i = 1; i < e; ++i)
     if (logits[i] > logits[a]) a = i;
@@ -132,12 +133,12 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_kernel(MoeArgs a) {
   route_top2(a.logits, a.e, ea, eb, ga, gb);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (a.sel) {
-      a.sel[0] = ea;
-      a.sel[1] = eb;
+      *gmem(a.sel + 0) = ea;
+      *gmem(a.sel + 1) = eb;
     }
     if (a.gates) {
-      a.gates[0] = ga;
-      a.gates[1] = gb;
+      *gmem(a.gates + 0) = ga;
+      *gmem(a.gates + 1) = gb;
     }
   }
 
@@ -236,8 +237,8 @@ __device__ __forceinline__ void w2_finish(const MoeArgs& a, int64_t bt, int lane
       const float sa = __uint_as_float((uint32_t)a.s2[(int64_t)ea * a.dim + r] << 16);
       const float sb = __uint_as_float((uint32_t)a.s2[(int64_t)eb * a.dim + r] << 16);
       const float y = ga * (sa * o[0]) + gb * (sb * o[1]);
-      if (a.y32) a.y32[r] = y;
-      if (a.y16) a.y16[r] = f32_to_bf16(y);
+      if (a.y32) *gmem(a.y32 + r) = y;
+      if (a.y16) *gmem(a.y16 + r) = f32_to_bf16(y);
     }
   }
   buf ^= 1;

@@ -144,12 +144,12 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
       ctr = 0;
       if (lo == 0) {
         if (L.sel) {
-          L.sel[0] = ea;
-          L.sel[1] = eb;
+          *gmem(L.sel + 0) = ea;
+          *gmem(L.sel + 1) = eb;
         }
         if (L.gates) {
-          L.gates[0] = ga;
-          L.gates[1] = gbt;
+          *gmem(L.gates + 0) = ga;
+          *gmem(L.gates + 1) = gbt;
         }
       }
     }
@@ -190,10 +190,10 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
             h3 = tot[U + u];
           }
         const int64_t j = j0 + lane;
-        const uint16_t* sc = L.s13 + (int64_t)ex * 2 * d.f;
+        const __attribute__((address_space(1))) uint16_t* sc = gmem(L.s13 + (int64_t)ex * 2 * d.f);
         h1 *= __uint_as_float((uint32_t)sc[j] << 16);
         h3 *= __uint_as_float((uint32_t)sc[j + d.f] << 16);
-        L.work[(int64_t)slot * d.f + j] = h1 / (1.0f + expf(-h1)) * h3;
+        *gmem(L.work + ((int64_t)slot * d.f + j)) = h1 / (1.0f + expf(-h1)) * h3;
       }
     };
 
@@ -301,11 +301,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerD
             oa = tot[u];
             ob = tot[U + u];
           }
-        const float sa = __uint_as_float((uint32_t)L.s2[(int64_t)ea * d.dim + n] << 16);
-        const float sb = __uint_as_float((uint32_t)L.s2[(int64_t)eb * d.dim + n] << 16);
+        const float sa = __uint_as_float((uint32_t)*gmem(L.s2 + ((int64_t)ea * d.dim + n)) << 16);
+        const float sb = __uint_as_float((uint32_t)*gmem(L.s2 + ((int64_t)eb * d.dim + n)) << 16);
         const float y = ga * (sa * oa) + gbt * (sb * ob);
-        if (L.y32) L.y32[n] = y;
-        if (L.y16) L.y16[n] = f32_to_bf16(y);
+        if (L.y32) *gmem(L.y32 + n) = y;
+        if (L.y16) *gmem(L.y16 + n) = f32_to_bf16(y);
       }
     };
 

@@ -62,17 +62,18 @@ static StepVariant shared_variant() {
 
 constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 
-template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL>
+template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL, bool SB>
 static void verify_launch(int grid, const StepLaunch& l, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB>), dim3((unsigned)grid),
                      dim3(WAVES * 64), 0, stream, l.mats, l.begin, l.first);
 }
 
-template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool QL = true>
+template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool QL = true,
+          bool SB = false>
 static StepVariant verify_variant() {
   return StepVariant{1, WAVES, 16 * RT,
-                     reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL>),
-                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL>, 0, true};
+                     reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB>),
+                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL, SB>, 0, true};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {

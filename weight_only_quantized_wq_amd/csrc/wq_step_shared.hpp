@@ -57,12 +57,17 @@ __device__ __forceinline__ int claim_batch(int* ctr, int lane) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Loads one batch-pass; with !ok every load reads zeros (an empty resource)
+// without touching memory.  The loads are issued either way, so the code
+// after a conditional prefetch sees the same outstanding loads on every
+// path and waits only for the pass it consumes.
 template <class F, int U, int CPL>
-__device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int pass, int lane, PassBuf<U, CPL>& bt) {
+__device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int pass, int lane, PassBuf<U, CPL>& bt,
+                                          bool ok = true) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = batch * U + u;
-    const bool row_ok = r < a.n;
+    const bool row_ok = ok && r < a.n;
     const int64_t rr = row_ok ? r : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rr * a.row_bytes, row_ok ? (uint32_t)a.row_bytes : 0u);
 #pragma unroll
@@ -107,9 +112,9 @@ __device__ __forceinline__ void finish_pass(const GemvArgs& a, int64_t batch, in
       if (lane == u) v = tot[u];
     const int64_t r = batch * U + lane;
     if (r < a.n) {
-      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)a.scale[r] << 16);
-      if (a.y32) a.y32[r] = v;
-      if (a.y16) a.y16[r] = f32_to_bf16(v);
+      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)*gmem(a.scale + r) << 16);
+      if (a.y32) *gmem(a.y32 + r) = v;
+      if (a.y16) *gmem(a.y16 + r) = f32_to_bf16(v);
     }
   }
 }
@@ -146,7 +151,7 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
         p2 = 0;
       }
       bool more = c2 < le;
-      if (more) load_pass<F, U, CPL>(a, c2, p2, lane, B);
+      load_pass<F, U, CPL>(a, c2, p2, lane, B, more);
       if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
       finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, A, xs, kc, acc, bias);
       if (!more) break;
@@ -160,7 +165,7 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
         p2 = 0;
       }
       more = c2 < le;
-      if (more) load_pass<F, U, CPL>(a, c2, p2, lane, A);
+      load_pass<F, U, CPL>(a, c2, p2, lane, A, more);
       if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
       finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, B, xs, kc, acc, bias);
       if (!more) break;

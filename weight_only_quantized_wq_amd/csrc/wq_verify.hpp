@@ -87,6 +87,7 @@ __device__ __forceinline__ vf32x4 mfma16x16x32(const uint32_t (&a)[4], const uin
 template <int M, int KW, int THREADS>
 __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad, VerifyShared<M, KW>& sh) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
+#pragma unroll 1
   for (int it = threadIdx.x; it < 4 * SETS * kpad; it += THREADS) {
     const int t = it / kpad;
     const int g = it - t * kpad;
@@ -105,8 +106,8 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
 }
 
 // Loads the codes of item `it` of window [g0, ...) of block `blk` (tiles
-// RT blk .. RT blk + RT - 1): OCT groups of each of 4 k-slots for the 16
-// rows of each tile.  With QL a wave-wide load is laid out so that each quad
+// RT blk .. RT blk + RT - 1): OCT quads of 4 consecutive groups (k-slot s of
+// quad o = group 4 o + s of the item) for the 16 rows of each tile.  With QL a wave-wide load is laid out so that each quad
 // of lanes reads ONE row (lane (row = lane / 4, k-slot = lane % 4)) and
 // verify_item moves each word to the MFMA lane (k-slot = lane / 16, row =
 // lane % 16) with a cross-lane permute; without QL each lane loads its own
@@ -116,7 +117,7 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
                                             VerifyItem<RT, OCT>& q) {
   const uint32_t row_bytes = (uint32_t)a.row_bytes;
   const int lrow = QL ? lane >> 2 : lane & 15;
-  const int gl = g0 + it * 4 * OCT + OCT * (QL ? lane & 3 : lane >> 4);   // first of this lane's OCT groups
+  const int gl = g0 + it * 4 * OCT + (QL ? lane & 3 : lane >> 4);   // this lane's group of quad 0
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = (blk * RT + rt) * 16;
@@ -126,8 +127,9 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * a.row_bytes, rows_ok * row_bytes);
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
-      const bool ok = gl + o < a.chunks;
-      q.w[rt][o] = buffer_load16_nt(rw, ok ? (uint32_t)lrow * row_bytes + (uint32_t)(gl + o) * 16u : 0x80000000u);
+      const bool ok = gl + 4 * o < a.chunks;
+      q.w[rt][o] =
+          buffer_load16_nt(rw, ok ? (uint32_t)lrow * row_bytes + (uint32_t)(gl + 4 * o) * 16u : 0x80000000u);
     }
   }
 }
@@ -203,7 +205,7 @@ __device__ __forceinline__ void verify_a(const VerifyShared<M, KW>& sh, int ga, 
 // Accumulates one item into y[tile][set][token]; `il` is the item's first
 // group within the staged activation window and `iz` within the (scale,
 // zero) window held in `szb`.
-template <int M, int KW, int RT, int OCT, bool QL>
+template <int M, int KW, int RT, int OCT, bool QL, bool SB>
 __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il, int iz, int rq, int col,
                                             const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
                                             const FmtInt4::K& kc, uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
@@ -212,8 +214,8 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
   const int src = (4 * col + rq) * 4;   // byte address of the lane holding this lane's codes (QL)
 #pragma unroll
   for (int o = 0; o < OCT; ++o) {
-    const int g = il + OCT * rq + o;            // this lane's group (activation window)
-    verify_a<M, KW>(sh, il + OCT * (col >> 2) + o, rq, col, av);
+    const int g = il + 4 * o + rq;              // this lane's group (activation window)
+    verify_a<M, KW>(sh, il + 4 * o + (col >> 2), rq, col, av);
     vf32x4 xs4[SETS];
 #pragma unroll
     for (int st = 0; st < SETS; ++st) xs4[st] = *reinterpret_cast<const vf32x4*>(&sh.gs[g][st][0]);
@@ -224,7 +226,7 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
         w = u32x4{to_mfma_lane(w[0], src), to_mfma_lane(w[1], src), to_mfma_lane(w[2], src),
                   to_mfma_lane(w[3], src)};
       }
-      const uint32_t szw = szb[rt][col][iz + OCT * rq + o];
+      const uint32_t szw = szb[rt][col][iz + 4 * o + rq];
       FmtInt4::D d;
       FmtInt4::decode(w, d, kc);
       const float s = __uint_as_float(szw << 16);
@@ -242,6 +244,9 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
           if (4 * st + r < M) y[rt][st][r] = fmaf(zb, xs4[st][r], fmaf(s, acc[r], y[rt][st][r]));
         }
       }
+      // SB: finish one chunk before the next is decoded, which bounds the
+      // registers in flight (the other waves of the CU hide the latency)
+      if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -271,8 +276,8 @@ __device__ __forceinline__ void verify_store(const GemvArgs& a, int64_t blk, int
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * st + r;
           if (t >= M) continue;
-          if (a.y32) a.y32[(int64_t)t * a.n + row] = y[rt][st][r];
-          if (a.y16) a.y16[(int64_t)t * a.n + row] = f32_to_bf16(y[rt][st][r]);
+          if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = y[rt][st][r];
+          if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(y[rt][st][r]);
         }
     }
 #pragma unroll
@@ -285,7 +290,7 @@ __device__ __forceinline__ void verify_store(const GemvArgs& a, int64_t blk, int
 // mats: per-matrix descriptors (batch = one block of RT 16-row tiles;
 // `chunks` = groups per row); wg_begin[g] .. wg_begin[g + 1]: workgroup g's
 // global blocks, starting in matrix wg_mat[g].
-template <int M, int KW, int WAVES, int RT, int OCT, bool PF, bool QL>
+template <int M, int KW, int WAVES, int RT, int OCT, bool PF, bool QL, bool SB>
 __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const GemvArgs* __restrict__ mats,
                                                                       const int64_t* __restrict__ wg_begin,
                                                                       const int32_t* __restrict__ wg_mat) {
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
           const bool more = b2 < le;
           if (PF && more) verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, A);
           if (more && i2 == 0) nxt = lb + claim_batch(&ctr, lane);
-          verify_item<M, KW, RT, OCT, QL>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
+          verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
           if (it + 1 == items) verify_store<M, RT, SETS>(a, blk, rq, col, y);
           if (!more) break;
           if (!PF) verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, A);
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
             }
             VerifyItem<RT, OCT> cur = A;
             if (PF && it + 1 < items) verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, A);
-            verify_item<M, KW, RT, OCT, QL>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
+            verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
             if (!PF && it + 1 < items) verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, A);
           }
         }

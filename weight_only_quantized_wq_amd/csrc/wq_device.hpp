@@ -46,6 +46,13 @@ __device__ __forceinline__ const __attribute__((address_space(1))) T* gmem(const
   return (const __attribute__((address_space(1))) T*)p;
 }
 
+// Waits for every outstanding vector-memory access.  A loop that ends with a
+// prefetch still in flight hands it to whatever code follows, and the wait
+// bookkeeping of the next loop, merging that path, may then drain all loads
+// in every iteration; draining once where the loop ends is cheaper.
+// (s_waitcnt with vmcnt = 0, expcnt and lgkmcnt at their "no wait" maxima.)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // Streaming loads: weights are read exactly once per product, so they are
 // fetched with the nontemporal hint and do not displace x or other data.

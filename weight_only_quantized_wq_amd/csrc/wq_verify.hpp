@@ -111,10 +111,12 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
 // of lanes reads ONE row (lane (row = lane / 4, k-slot = lane % 4)) and
 // verify_item moves each word to the MFMA lane (k-slot = lane / 16, row =
 // lane % 16) with a cross-lane permute; without QL each lane loads its own
-// MFMA chunk.  Rows past n and groups past the row read as zero.
+// MFMA chunk.  Rows past n and groups past the row read as zero, and so does
+// everything with !any: the loads are issued on every path, so code after a
+// conditional prefetch waits only for the item it consumes.
 template <int RT, int OCT, bool QL>
 __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int g0, int it, int lane,
-                                            VerifyItem<RT, OCT>& q) {
+                                            VerifyItem<RT, OCT>& q, bool any = true) {
   const uint32_t row_bytes = (uint32_t)a.row_bytes;
   const int lrow = QL ? lane >> 2 : lane & 15;
   const int gl = g0 + it * 4 * OCT + (QL ? lane & 3 : lane >> 4);   // this lane's group of quad 0
@@ -122,8 +124,11 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = (blk * RT + rt) * 16;
     const int64_t left = a.n - rbase;
-    const uint32_t rows_ok = left <= 0 ? 0u : (left >= 16 ? 16u : (uint32_t)left);
-    const int64_t rb = left > 0 ? rbase : 0;
+    // !any empties the (wave-uniform) resource rather than the per-lane
+    // offsets, which keeps the loads free of branches
+    const bool live = any && left > 0;
+    const uint32_t rows_ok = !live ? 0u : (left >= 16 ? 16u : (uint32_t)left);
+    const int64_t rb = live ? rbase : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * a.row_bytes, rows_ok * row_bytes);
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
@@ -134,16 +139,19 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
   }
 }
 
-// Loads the (scale, zero) words of groups [gw, gw + kSzWin) of block `blk`.
+// Loads the (scale, zero) words of groups [gw, gw + kSzWin) of block `blk`
+// (zeros with !any).
 template <int RT>
-__device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, int lane, SzWindow<RT>& z) {
+__device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, int lane, SzWindow<RT>& z,
+                                        bool any = true) {
   const int g = gw + 4 * (lane & 7);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = (blk * RT + rt) * 16;
     const int64_t left = a.n - rbase;
-    const uint32_t rows_ok = left <= 0 ? 0u : (left >= 16 ? 16u : (uint32_t)left);
-    const int64_t rb = left > 0 ? rbase : 0;
+    const bool live = any && left > 0;
+    const uint32_t rows_ok = !live ? 0u : (left >= 16 ? 16u : (uint32_t)left);
+    const int64_t rb = live ? rbase : 0;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.chunks, rows_ok * (uint32_t)a.chunks * 4u);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -341,34 +349,50 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
       if (blk < le) {
         int64_t nxt = lb + claim_batch(&ctr, lane);
         int it = 0;
-        VerifyItem<RT, OCT> A;
+        bool more = true;
+        VerifyItem<RT, OCT> A, B;
         SzWindow<RT> Z;
+        sz_load<RT>(a, blk, 0, lane, Z);   // first: it is consumed first
         verify_load<RT, OCT, QL>(a, blk, 0, 0, lane, A);
-        sz_load<RT>(a, blk, 0, lane, Z);
-        for (;;) {
+        // consumes item (blk, it) from `cur` after requesting the next one
+        // into `nx`; the two buffers alternate, so no loaded value is copied
+        // (a copy would wait for the request just made)
+        auto step = [&](const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
           if (it % IW == 0) {
             // the window of this item has arrived: publish it, request the next
             sz_put<RT>(a, it * GI, lane, Z, szb);
             const bool same = it + IW < items;
             const int64_t zb = same ? blk : nxt;
-            if (zb < le) sz_load<RT>(a, zb, same ? (it + IW) * GI : 0, lane, Z);
+            sz_load<RT>(a, zb, same ? (it + IW) * GI : 0, lane, Z, zb < le);
           }
-          VerifyItem<RT, OCT> cur = A;
           int64_t b2 = blk;
           int i2 = it + 1;
           if (i2 == items) {
             b2 = nxt;
             i2 = 0;
           }
-          const bool more = b2 < le;
-          if (PF && more) verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, A);
+          more = b2 < le;
+          verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, nx, more);
           if (more && i2 == 0) nxt = lb + claim_batch(&ctr, lane);
           verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
           if (it + 1 == items) verify_store<M, RT, SETS>(a, blk, rq, col, y);
-          if (!more) break;
-          if (!PF) verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, A);
           blk = b2;
           it = i2;
+        };
+        // the prefetch left in flight is drained on the way out: otherwise
+        // the (never taken) CFG edge from an exit test back to the loop head
+        // carries it, and every iteration would wait for all loads
+        for (;;) {
+          step(A, B);
+          if (!more) {
+            wait_vmem_all();
+            break;
+          }
+          step(B, A);
+          if (!more) {
+            wait_vmem_all();
+            break;
+          }
         }
       }
     } else {
@@ -385,19 +409,29 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
           verify_stage<M, KW, WAVES * 64>(a, g0, items * GI, sh);
           __syncthreads();
           if (!mine) continue;
-          VerifyItem<RT, OCT> A;
+          VerifyItem<RT, OCT> A, B;
           SzWindow<RT> Z;
-          verify_load<RT, OCT, QL>(a, blk, g0, 0, lane, A);
           sz_load<RT>(a, blk, g0, lane, Z);
-          for (int it = 0; it < items; ++it) {
+          verify_load<RT, OCT, QL>(a, blk, g0, 0, lane, A);
+          auto step = [&](int it, const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
             if (it % IW == 0) {
               sz_put<RT>(a, g0 + it * GI, lane, Z, szb);
-              if (it + IW < items) sz_load<RT>(a, blk, g0 + (it + IW) * GI, lane, Z);
+              sz_load<RT>(a, blk, g0 + (it + IW) * GI, lane, Z, it + IW < items);
             }
-            VerifyItem<RT, OCT> cur = A;
-            if (PF && it + 1 < items) verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, A);
+            verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, nx, it + 1 < items);
             verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
-            if (!PF && it + 1 < items) verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, A);
+          };
+          for (int it = 0;; it += 2) {
+            step(it, A, B);
+            if (it + 1 >= items) {
+              wait_vmem_all();
+              break;
+            }
+            step(it + 1, B, A);
+            if (it + 2 >= items) {
+              wait_vmem_all();
+              break;
+            }
           }
         }
         if (mine) verify_store<M, RT, SETS>(a, blk, rq, col, y);

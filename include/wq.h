@@ -204,8 +204,8 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
  * Validates every matrix on the host (null -> sizes -> alignment; k must be a
  * positive multiple of 8 / 16 / 32 per format and within the kernel's row
  * limit: with one token row the activations are staged whole in LDS, so
- * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with two token rows
- * k <= 32768, with 3..8 token rows k <= 131072), then writes the launch description into `workspace` (device
+ * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with 2..8 token rows
+ * k <= 131072), then writes the launch description into `workspace` (device
  * memory, 16-byte aligned, `workspace_bytes` long, caller-owned; it must
  * stay allocated and unmodified while the plan is used).  This copy is
  * synchronous: prepare once, outside any graph capture.  The matrices'
@@ -216,9 +216,10 @@ int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int
 
 /* Launches a prepared step on `stream` (asynchronous; may be captured into a
  * HIP graph).  Runs of one plan must not overlap (they share its workspace,
- * which for one-token steps also carries the XCD speed weights that each run
- * measures and the next run uses to cut the step into per-CU ranges); runs
- * of plans that share output buffers race. */
+ * which carries balance state that each run measures and the next run uses
+ * to cut the step into per-CU ranges: the XCD speed weights of one-token
+ * steps, the relative cost of rows longer than one activation window for
+ * 2..8 token rows); runs of plans that share output buffers race. */
 int wq_decode_step_run(const wq_step_plan* plan, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -206,84 +206,4 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Whole decode step in one launch (two-token rows).  The step's row batches,
-// matrix after matrix, form one global sequence; workgroup g walks the
-// contiguous range [wg_begin[g], wg_begin[g + 1]) (cut so that every
-// workgroup streams the same number of weight bytes), starting in matrix
-// wg_mat[g].  Per matrix segment a workgroup reads the descriptor, takes its
-// wave roles (split, row groups, chunks per lane <= CPL), loads that matrix's
-// activations and streams its batches; waves without a row group in a matrix
-// only join the split-K barriers.
-template <class F, int M, int CPL, int U, int WAVES, bool PF>
-__device__ __forceinline__ void step_range(const GemvArgs* __restrict__ mats, int64_t gb, const int64_t gend, int mi,
-                                           float (&red)[2][WAVES][U * M], int& buf) {
-  const int lane = lane_id();
-  const int wave = wave_id();
-  while (gb < gend) {
-    const GemvArgs a = mats[mi];
-    const int cpl = a.cpl;
-    const int ks = wave % a.split;
-    const int rg = wave / a.split;
-    const bool active = rg < a.groups;
-    int cidx[CPL];
-    uint32_t off[CPL];
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      cidx[j] = (ks * cpl + j) * kWave + lane;
-      off[j] = (uint32_t)cidx[j] * 16u;
-    }
-    int64_t b = gb - a.batch_begin;
-    const int64_t mend = a.batch_begin + a.batches;
-    const int64_t bend = (gend < mend ? gend : mend) - a.batch_begin;
-
-    Batch<F, U, CPL> A;
-    if (active) load_batch<F, U, CPL>(a, b, rg, off, A, cpl);
-
-    typename F::X xr[M][CPL];
-    float bias[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      bias[m] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        xr[m][j] = F::load_x(a.x + m * a.k, cidx[j], active && j < cpl && cidx[j] < a.chunks);
-        bias[m] += F::lane_bias(xr[m][j]);
-      }
-    }
-    const typename F::K kc = F::consts();
-
-    if constexpr (PF) {
-      Batch<F, U, CPL> B;
-      while (b < bend) {
-        if (active && b + 1 < bend) load_batch<F, U, CPL>(a, b + 1, rg, off, B, cpl);
-        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf, cpl, active);
-        ++b;
-        if (b >= bend) break;
-        if (active && b + 1 < bend) load_batch<F, U, CPL>(a, b + 1, rg, off, A, cpl);
-        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, kc, red, buf, cpl, active);
-        ++b;
-      }
-    } else {
-      while (b < bend) {
-        finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf, cpl, active);
-        ++b;
-        if (active && b < bend) load_batch<F, U, CPL>(a, b, rg, off, A, cpl);
-      }
-    }
-    gb = a.batch_begin + bend;
-    ++mi;
-  }
-}
-
-template <class F, int M, int CPL, int U, int WAVES, bool PF>
-__global__ __launch_bounds__(WAVES * 64) void gemv_step_kernel(const GemvArgs* __restrict__ mats,
-                                                               const int64_t* __restrict__ wg_begin,
-                                                               const int32_t* __restrict__ wg_mat) {
-  __shared__ float red[2][WAVES][U * M];
-  int buf = 0;
-  step_range<F, M, CPL, U, WAVES, PF>(mats, wg_begin[blockIdx.x], wg_begin[blockIdx.x + 1], wg_mat[blockIdx.x], red,
-                                      buf);
-}
-
 }  // namespace wq

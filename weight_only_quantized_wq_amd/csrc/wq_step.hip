@@ -1,5 +1,6 @@
 // Whole decode step in one launch: plan once on the host, then launch the
-// persistent step kernel (wq_gemv_kernel.hpp) as often as needed.
+// persistent step kernel (wq_step_shared.hpp for one token row, wq_verify.hpp
+// for 2..8) as often as needed.
 #include <stdint.h>
 #include <string.h>
 
@@ -12,20 +13,18 @@
 
 namespace wq {
 
-// One persistent kernel configuration per (format, tokens per pass): the
-// largest chunks per lane a pass uses, waves per workgroup and rows per wave
-// per batch, and which kernel: the shared-activation kernel (one format,
-// one token row; batch = u rows of one wave), the matrix-core verify kernel
-// (int4, 3..8 token rows; batch = u rows in 16-row tiles) or the register
-// kernel (int4, two token rows; batch = u rows per row group).
 // Device pointers of a prepared plan's workspace.
 struct StepLaunch {
   const GemvArgs* mats;
-  const int64_t* begin;   // range starts (groups + 1), cut on the host
-  const int32_t* first;   // first matrix of each range
   StepCuts cuts;          // cost prefix and XCD balance (shared-activation kernel)
+  VerifyCuts vcuts;       // cost prefixes and long-row balance (verify kernel)
 };
 
+// One persistent kernel configuration per (format, tokens per pass): the
+// largest chunks per lane a pass uses, waves per workgroup and rows per
+// batch, and which kernel: the shared-activation kernel (one format, one
+// token row; batch = u rows of one wave) or the matrix-core verify kernel
+// (int4, 2..8 token rows; batch = u rows in 16-row tiles).
 struct StepVariant {
   int cpl_max;
   int waves;
@@ -34,19 +33,8 @@ struct StepVariant {
   void (*launch)(int grid, const StepLaunch&, hipStream_t);
   int cmax;    // > 0: the shared-activation kernel, staging at most cmax chunks of a row
   bool verify; // the matrix-core verify kernel
+  int kw = 0;   // verify: groups of one staged activation window
 };
-
-template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static void step_launch(int grid, const StepLaunch& l, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_step_kernel<F, M, CPL, U, WAVES, PF>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
-                     stream, l.mats, l.begin, l.first);
-}
-
-template <class F, int M, int CPL, int U, int WAVES, bool PF>
-static StepVariant variant() {
-  return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_kernel<F, M, CPL, U, WAVES, PF>),
-                     &step_launch<F, M, CPL, U, WAVES, PF>, 0, false};
-}
 
 template <class F, int U, int CPL, int WAVES, bool PF>
 static void shared_launch(int grid, const StepLaunch& l, hipStream_t stream) {
@@ -61,11 +49,15 @@ static StepVariant shared_variant() {
 }
 
 constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
+// starting value of the verify kernel's long-row cost factor (measured on
+// the Llama-3.1-70B set: rows of 28672 inputs cost ~1.2x per byte); each
+// launch refines it
+constexpr double kVerifyLongRowPrior = 1.2;
 
 template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL, bool SB>
 static void verify_launch(int grid, const StepLaunch& l, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB>), dim3((unsigned)grid),
-                     dim3(WAVES * 64), 0, stream, l.mats, l.begin, l.first);
+                     dim3(WAVES * 64), 0, stream, l.mats, l.vcuts);
 }
 
 template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool QL = true,
@@ -73,7 +65,7 @@ template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, i
 static StepVariant verify_variant() {
   return StepVariant{1, WAVES, 16 * RT,
                      reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB>),
-                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL, SB>, 0, true};
+                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL, SB>, 0, true, KW};
 }
 
 static bool pick_variant(int format, int m, StepVariant& v) {
@@ -85,13 +77,13 @@ static bool pick_variant(int format, int m, StepVariant& v) {
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
-      case 2: v = variant<FmtInt4, 2, 2, 2, 8, false>(); break;
-      case 3: v = verify_variant<3, 12, true>(); break;
+      case 2: v = verify_variant<2, 8, true, 2, 4, 512>(); break;
+      case 3: v = verify_variant<3, 8, true, 2, 4>(); break;
       case 4: v = verify_variant<4, 12, true>(); break;
-      case 5: v = verify_variant<5, 8, true>(); break;
-      case 6: v = verify_variant<6, 8, true, 2, 2, 128>(); break;
-      case 7: v = verify_variant<7, 8, true, 2, 2, 128>(); break;
-      case 8: v = verify_variant<8, 8, true, 2, 2, 128>(); break;
+      case 5: v = verify_variant<5, 8, true, 2, 4>(); break;
+      case 6: v = verify_variant<6, 8, true, 2, 4>(); break;
+      case 7: v = verify_variant<7, 6, true, 2, 4>(); break;
+      case 8: v = verify_variant<8, 8, true, 2, 4, 192>(); break;
       default: return false;
     }
   } else {
@@ -110,40 +102,45 @@ static int64_t row_bytes_of(int format, int64_t k) {
 
 constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
 
-// Workspace layout: per-matrix descriptors, the range starts of the
-// workgroups (groups + 1) and the first matrix of each range (groups), the
-// step's cost before each matrix (count + 1) and per batch of each matrix
-// (count), then the XCD balance state.
+// Workspace layout: per-matrix descriptors, the step's cost before each
+// matrix (count + 1; for the verify kernel: of the short-row matrices), the
+// long-row cost before each matrix (count + 1, verify kernel), the cost per
+// batch of each matrix (count), then the XCD balance state and the verify
+// kernel's long-row balance state.  Workgroups cut their ranges from these
+// on the device.
 struct StepLayout {
-  size_t begin, first, prefix, bcost, bal, end;
+  size_t prefix, prefl, bcost, bal, vbal, end;
 };
 
-static StepLayout step_layout(int64_t count, int64_t groups) {
+static StepLayout step_layout(int64_t count) {
   auto up16 = [](size_t v) { return (v + 15) / 16 * 16; };
   StepLayout l;
-  l.begin = up16((size_t)count * sizeof(GemvArgs));
-  l.first = l.begin + ((size_t)groups + 1) * 8;
-  l.prefix = up16(l.first + (size_t)groups * 4);
-  l.bcost = l.prefix + ((size_t)count + 1) * 8;
+  l.prefix = up16((size_t)count * sizeof(GemvArgs));
+  l.prefl = l.prefix + ((size_t)count + 1) * 8;
+  l.bcost = l.prefl + ((size_t)count + 1) * 8;
   l.bal = up16(l.bcost + (size_t)count * 8);
-  l.end = l.bal + sizeof(StepBalance);
+  l.vbal = up16(l.bal + sizeof(StepBalance));
+  l.end = l.vbal + sizeof(VerifyBalance);
   return l;
 }
 
-static int64_t workspace_need(int64_t count, int64_t groups) { return (int64_t)step_layout(count, groups).end; }
+static int64_t workspace_need(int64_t count) { return (int64_t)step_layout(count).end; }
 
-static StepLaunch launch_view(void* workspace, int32_t count, int32_t groups, int64_t total) {
+static StepLaunch launch_view(void* workspace, int32_t count, int64_t total) {
   char* ws = reinterpret_cast<char*>(workspace);
-  const StepLayout l = step_layout(count, groups);
+  const StepLayout l = step_layout(count);
   StepLaunch v;
   v.mats = reinterpret_cast<const GemvArgs*>(ws);
-  v.begin = reinterpret_cast<const int64_t*>(ws + l.begin);
-  v.first = reinterpret_cast<const int32_t*>(ws + l.first);
   v.cuts.prefix = reinterpret_cast<const double*>(ws + l.prefix);
   v.cuts.bcost = reinterpret_cast<const double*>(ws + l.bcost);
   v.cuts.bal = reinterpret_cast<StepBalance*>(ws + l.bal);
   v.cuts.total = total;
   v.cuts.count = count;
+  v.vcuts.pre_short = v.cuts.prefix;
+  v.vcuts.pre_long = reinterpret_cast<const double*>(ws + l.prefl);
+  v.vcuts.bcost = v.cuts.bcost;
+  v.vcuts.bal = reinterpret_cast<VerifyBalance*>(ws + l.vbal);
+  v.vcuts.count = count;
   return v;
 }
 
@@ -153,7 +150,7 @@ using namespace wq;
 
 extern "C" int64_t wq_decode_step_workspace_bytes(int32_t count) {
   if (count < 0) return 0;
-  return workspace_need(count, kMaxGroups);
+  return workspace_need(count);
 }
 
 extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int32_t count,
@@ -180,9 +177,8 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
                   name, i, (long long)mt.n, (long long)mt.k, wpc);
     const int64_t chunks = mt.k / wpc;
     const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
-    const int64_t split = v.cmax || v.verify ? 1 : (chunks + per_wave_max - 1) / per_wave_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
-    if (split > v.waves || (v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
+    if ((v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -200,14 +196,14 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.k = mt.k;
     a.row_bytes = row_bytes_of(format, mt.k);
     a.chunks = (int32_t)chunks;
-    a.split = (int32_t)split;
-    a.groups = v.cmax || v.verify ? 1 : v.waves / (int32_t)split;
+    a.split = 1;
+    a.groups = 1;
     // the shared-activation kernel streams a row in `passes` passes of cpl_max
     // chunks per lane
-    a.cpl = v.cmax ? (int32_t)passes : (int32_t)((chunks + split * kWave - 1) / (split * kWave));
+    a.cpl = v.cmax ? (int32_t)passes : 1;
     // the verify kernel's batch is a block of 16-row tiles, the
     // shared-activation kernel's u rows of one wave
-    const int64_t rows_per_batch = v.cmax || v.verify ? (int64_t)v.u : (int64_t)a.groups * v.u;
+    const int64_t rows_per_batch = (int64_t)v.u;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -226,64 +222,33 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   if (groups > kMaxGroups) groups = kMaxGroups;
   if (groups > total_batches) groups = (int)total_batches;
   if (groups < 1) groups = 1;
-  const int64_t need = workspace_need(count, groups);
+  const int64_t need = workspace_need(count);
   if (workspace_bytes < need)
     return fail(WQ_ERR_SHAPE, "%s: workspace of %lld bytes is smaller than the %lld needed", name,
                 (long long)workspace_bytes, (long long)need);
   if (!aligned16(workspace)) return fail(WQ_ERR_ALIGN, "%s: workspace must be 16-byte aligned", name);
 
-  // The first global batch at or after byte offset `target` of the step
-  // (a batch belongs to the range its first byte falls in).
-  double total = 0;
-  for (int32_t i = 0; i < count; ++i) total += batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
-  auto batch_at = [&](double target) -> int64_t {
-    double acc = 0;   // bytes before matrix i
-    for (int32_t i = 0; i < count; ++i) {
-      const double mb = batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
-      if (acc + mb > target) {
-        int64_t local = (int64_t)((target - acc) / batch_bytes[(size_t)i] + 0.999999);
-        if (local > desc[(size_t)i].batches) local = desc[(size_t)i].batches;
-        return desc[(size_t)i].batch_begin + local;
-      }
-      acc += mb;
-    }
-    return total_batches;
-  };
-  auto matrix_of = [&](int64_t gb) -> int32_t {
-    if (gb >= total_batches) gb = total_batches - 1;
-    int32_t lo = 0, hi = count - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) / 2;
-      if (desc[(size_t)mid].batch_begin <= gb) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  };
-
-  // [0, total_batches) cut into `groups` ranges of equal cost
-  std::vector<int64_t> begin((size_t)groups + 1);
-  std::vector<int32_t> first((size_t)groups);
-  for (int g = 0; g <= groups; ++g) {
-    int64_t gb = g == groups ? total_batches : batch_at(total * (double)g / (double)groups);
-    if (gb > total_batches) gb = total_batches;
-    if (g > 0 && gb < begin[(size_t)g - 1]) gb = begin[(size_t)g - 1];
-    begin[(size_t)g] = gb;
-  }
-  for (int g = 0; g < groups; ++g) first[(size_t)g] = matrix_of(begin[(size_t)g]);
-
-  const StepLayout lay = step_layout(count, groups);
+  const StepLayout lay = step_layout(count);
   std::vector<char> host(lay.end, 0);
   memcpy(host.data(), desc.data(), (size_t)count * sizeof(GemvArgs));
-  memcpy(host.data() + lay.begin, begin.data(), ((size_t)groups + 1) * 8);
-  memcpy(host.data() + lay.first, first.data(), (size_t)groups * 4);
-  std::vector<double> prefix((size_t)count + 1, 0.0);
-  for (int32_t i = 0; i < count; ++i)
-    prefix[(size_t)i + 1] = prefix[(size_t)i] + batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
+  // verify kernel: short-row and long-row bytes kept apart (the kernel weighs
+  // the long ones by its balance factor); other kernels: prefl stays zero
+  std::vector<double> prefix((size_t)count + 1, 0.0), prefl((size_t)count + 1, 0.0);
+  for (int32_t i = 0; i < count; ++i) {
+    const double mb = batch_bytes[(size_t)i] * (double)desc[(size_t)i].batches;
+    const bool is_long = v.verify && desc[(size_t)i].chunks > v.kw;
+    prefix[(size_t)i + 1] = prefix[(size_t)i] + (is_long ? 0.0 : mb);
+    prefl[(size_t)i + 1] = prefl[(size_t)i] + (is_long ? mb : 0.0);
+  }
   memcpy(host.data() + lay.prefix, prefix.data(), prefix.size() * 8);
+  memcpy(host.data() + lay.prefl, prefl.data(), prefl.size() * 8);
   memcpy(host.data() + lay.bcost, batch_bytes.data(), (size_t)count * 8);
   StepBalance bal{};
   for (int x = 0; x < 8; ++x) bal.w[x] = 1.0f;
   memcpy(host.data() + lay.bal, &bal, sizeof(bal));
+  VerifyBalance vbal{};
+  vbal.f = kVerifyLongRowPrior;
+  memcpy(host.data() + lay.vbal, &vbal, sizeof(vbal));
   hipError_t e = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -307,7 +272,7 @@ extern "C" int wq_decode_step_run(const wq_step_plan* plan, void* stream) {
     return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_decode_step_prepare", name);
   int rc = check_device();
   if (rc) return rc;
-  const StepLaunch l = launch_view(const_cast<void*>(plan->workspace), plan->count, plan->groups, plan->total_batches);
+  const StepLaunch l = launch_view(const_cast<void*>(plan->workspace), plan->count, plan->total_batches);
   v.launch(plan->groups, l, (hipStream_t)stream);
   return launch_status(name);
 }

@@ -62,17 +62,21 @@ struct VerifyItem {
 };
 
 // (scale, zero) words of the 16 rows of each tile for a window of kSzWin
-// groups, loaded with full cache lines (8 rows x 32 groups per wave-wide
-// load) and passed through a per-wave LDS buffer, from which each lane reads
-// the words of its own (row, group).  Loads whose lanes span 16 rows touch a
-// line per row for a few bytes each; the address path, not HBM, then sets the
-// pace.
+// groups, loaded with 4 consecutive words per lane (a quad of lanes covers
+// 64 contiguous bytes of a row) and passed through a per-wave LDS buffer,
+// from which each lane reads the word of its own (row, group).  A load whose
+// lanes each fetch one word of a different row would touch a cache line per
+// lane; the address path, not HBM, would then set the pace.
 constexpr int kSzWin = 32;
-constexpr int kSzRow = kSzWin + 4;   // LDS words per row (16-byte aligned, skewed banks)
+constexpr int kSzRow = kSzWin + 4;            // LDS words per row (16-byte aligned, skewed banks)
+constexpr int kSzLanesPerRow = kSzWin / 4;
+constexpr int kSzRowsPerLoad = kWave / kSzLanesPerRow;
+constexpr int kSzLoads = 16 / kSzRowsPerLoad;
+static_assert(kSzWin % 4 == 0 && 16 % kSzRowsPerLoad == 0, "window must split into whole-row loads");
 
 template <int RT>
 struct SzWindow {
-  u32x4 r[RT][2];   // rows 8h + lane / 8, groups 4 (lane % 8) .. + 3
+  u32x4 r[RT][kSzLoads];   // load h: row kSzRowsPerLoad h + lane / kSzLanesPerRow, groups 4 (lane % ..) + 0..3
 };
 
 __device__ __forceinline__ vf32x4 mfma16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4], vf32x4 c) {
@@ -144,7 +148,7 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
 template <int RT>
 __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, int lane, SzWindow<RT>& z,
                                         bool any = true) {
-  const int g = gw + 4 * (lane & 7);
+  const int g = gw + 4 * (lane % kSzLanesPerRow);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = (blk * RT + rt) * 16;
@@ -154,8 +158,8 @@ __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, 
     const int64_t rb = live ? rbase : 0;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.chunks, rows_ok * (uint32_t)a.chunks * 4u);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t row = (uint32_t)(8 * h + (lane >> 3));
+    for (int h = 0; h < kSzLoads; ++h) {
+      const uint32_t row = (uint32_t)(kSzRowsPerLoad * h + lane / kSzLanesPerRow);
       z.r[rt][h] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                      rs, g < a.chunks ? (int)((row * (uint32_t)a.chunks + (uint32_t)g) * 4u) : (int)0x80000000, 0, 2));
@@ -168,16 +172,16 @@ __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, 
 template <int RT>
 __device__ __forceinline__ void sz_put(const GemvArgs& a, int gw, int lane, const SzWindow<RT>& z,
                                        uint32_t (*buf)[16][kSzRow]) {
-  const int g = gw + 4 * (lane & 7);
+  const int g = gw + 4 * (lane % kSzLanesPerRow);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kSzLoads; ++h) {
       u32x4 v = z.r[rt][h];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (g + e >= a.chunks) v[e] = 0u;
-      *reinterpret_cast<u32x4*>(&buf[rt][8 * h + (lane >> 3)][4 * (lane & 7)]) = v;
+      *reinterpret_cast<u32x4*>(&buf[rt][kSzRowsPerLoad * h + lane / kSzLanesPerRow][4 * (lane % kSzLanesPerRow)]) = v;
     }
 }
 
@@ -259,11 +263,25 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
   }
 }
 
-// Sums the four k-slots of each column (lanes col, col + 16, col + 32,
-// col + 48) in a fixed order and stores the block's rows; zeroes y.
-template <int M, int RT, int SETS>
-__device__ __forceinline__ void verify_store(const GemvArgs& a, int64_t blk, int rq, int col,
-                                             float (&y)[RT][SETS][4]) {
+// Rounds of blocks for rows longer than one activation window: each window
+// is staged once per round and the round's blocks are claimed for it; the
+// sums of a block's finished windows wait in LDS (VerifyPart).
+template <int WAVES>
+constexpr int verify_round_blocks() { return WAVES; }
+
+template <int M, int RT, int SR>
+struct VerifyPart {
+  float v[SR][RT * 16][M];
+};
+
+// Block `blk` (index `bi` of its round) has streamed the window: sums the
+// four k-slots of each column (lanes col, col + 16, col + 32, col + 48) in a
+// fixed order, adds the block's earlier windows (!first) and stores the rows
+// (last) or keeps the running sum for the next window; zeroes y.  The sum of
+// a row is taken window by window in order, whichever wave streams them.
+template <int M, int RT, int SETS, int SR>
+__device__ __forceinline__ void verify_fold(const GemvArgs& a, int64_t blk, int bi, bool first, bool last, int rq,
+                                            int col, float (&y)[RT][SETS][4], VerifyPart<M, RT, SR>& part) {
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -277,15 +295,21 @@ __device__ __forceinline__ void verify_store(const GemvArgs& a, int64_t blk, int
         y[rt][st][r] = v;
       }
     const int64_t row = (blk * RT + rt) * 16 + col;
-    if (rq == 0 && row < a.n) {
+    if (rq == 0) {
 #pragma unroll
       for (int st = 0; st < SETS; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 4 * st + r;
           if (t >= M) continue;
-          if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = y[rt][st][r];
-          if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(y[rt][st][r]);
+          float v = y[rt][st][r];
+          if (!first) v = part.v[bi][rt * 16 + col][t] + v;
+          if (!last) {
+            part.v[bi][rt * 16 + col][t] = v;
+          } else if (row < a.n) {
+            if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = v;
+            if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(v);
+          }
         }
     }
 #pragma unroll
@@ -295,26 +319,152 @@ __device__ __forceinline__ void verify_store(const GemvArgs& a, int64_t blk, int
   }
 }
 
-// mats: per-matrix descriptors (batch = one block of RT 16-row tiles;
-// `chunks` = groups per row); wg_begin[g] .. wg_begin[g + 1]: workgroup g's
-// global blocks, starting in matrix wg_mat[g].
-template <int M, int KW, int WAVES, int RT, int OCT, bool PF, bool QL, bool SB>
-__global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const GemvArgs* __restrict__ mats,
-                                                                      const int64_t* __restrict__ wg_begin,
-                                                                      const int32_t* __restrict__ wg_mat) {
+// The waves' share of one activation window: blocks [b0, b1) of matrix `a`,
+// claimed one at a time from `ctr` (zeroed by the caller); each streams the
+// window's `items` items (groups [g0, g0 + GI items)) and folds its sums
+// (verify_fold).  The next item's loads are issued before the current one is
+// reduced, across block boundaries too; the two item buffers alternate, so
+// no loaded value is copied (a copy would wait for the loads just issued).
+template <int M, int KW, int WAVES, int RT, int OCT, bool QL, bool SB, int SR>
+__device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int64_t b1, int g0, int items,
+                                              bool first, bool last, int* ctr, int lane, int rq, int col,
+                                              const VerifyShared<M, KW>& sh, uint32_t (*szb)[16][kSzRow],
+                                              const FmtInt4::K& kc,
+                                              uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
+                                              float (&y)[RT][VerifyShared<M, KW>::kSets][4],
+                                              VerifyPart<M, RT, SR>& part) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
   constexpr int GI = 4 * OCT;          // groups per item
   constexpr int IW = kSzWin / GI;      // items per (scale, zero) window
+  const int64_t nb = b1 - b0;
+  int64_t bi = claim_batch(ctr, lane);
+  if (bi >= nb) return;
+  int64_t nxt = claim_batch(ctr, lane);
+  int it = 0;
+  bool more = true;
+  VerifyItem<RT, OCT> A, B;
+  SzWindow<RT> Z;
+  sz_load<RT>(a, b0 + bi, g0, lane, Z);   // first: it is consumed first
+  verify_load<RT, OCT, QL>(a, b0 + bi, g0, 0, lane, A);
+  // consumes item (bi, it) from `cur` after requesting the next one into `nx`
+  auto step = [&](const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
+    if (it % IW == 0) {
+      // the window of this item has arrived: publish it, request the next
+      sz_put<RT>(a, g0 + it * GI, lane, Z, szb);
+      const bool same = it + IW < items;
+      const int64_t zb = same ? bi : nxt;
+      sz_load<RT>(a, b0 + zb, g0 + (same ? (it + IW) * GI : 0), lane, Z, zb < nb);
+    }
+    int64_t b2 = bi;
+    int i2 = it + 1;
+    if (i2 == items) {
+      b2 = nxt;
+      i2 = 0;
+    }
+    more = b2 < nb;
+    verify_load<RT, OCT, QL>(a, b0 + b2, g0, i2, lane, nx, more);
+    if (more && i2 == 0) nxt = claim_batch(ctr, lane);
+    verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
+    if (it + 1 == items) verify_fold<M, RT, SETS, SR>(a, b0 + bi, (int)bi, first, last, rq, col, y, part);
+    bi = b2;
+    it = i2;
+  };
+  // the prefetch left in flight is drained on the way out: otherwise the
+  // (never taken) CFG edge from an exit test back to the loop head carries
+  // it, and every iteration would wait for all loads
+  for (;;) {
+    step(A, B);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+    step(B, A);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+  }
+}
+
+// Balance between rows within one activation window ("short") and longer
+// rows ("long"), which stream more slowly per byte (window rounds with a
+// barrier each, rows further apart).  Ranges are cut in cost units in which
+// a long-row byte costs f short-row bytes.  Each launch measures the time its
+// workgroups spend on each kind and the last one to finish moves f a quarter
+// of the way to the measured ratio of the two rates (clamped to [0.5, 4]);
+// the next launch cuts with it.  Which workgroup computes a row never changes
+// the row's result.
+struct VerifyBalance {
+  double f;
+  double t[2];      // this launch: wall-clock ticks spent on short / long rows
+  double c[2];      // this launch: bytes of short / long rows streamed
+  int32_t done;     // workgroups finished in this launch
+  int32_t pad[3];
+};
+
+struct VerifyCuts {
+  const double* pre_short;   // [count + 1] bytes of short-row matrices before matrix i
+  const double* pre_long;    // [count + 1] bytes of long-row matrices before matrix i
+  const double* bcost;       // [count] bytes of one block of matrix i
+  VerifyBalance* bal;
+  int32_t count;
+};
+
+// mats: per-matrix descriptors (batch = one block of RT 16-row tiles;
+// `chunks` = groups per row).  Each workgroup cuts its own contiguous range
+// of the step's blocks from the cost prefixes and the balance factor.
+template <int M, int KW, int WAVES, int RT, int OCT, bool PF, bool QL, bool SB>
+__global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const GemvArgs* __restrict__ mats,
+                                                                      VerifyCuts cuts) {
+  constexpr int SETS = VerifyShared<M, KW>::kSets;
+  constexpr int GI = 4 * OCT;          // groups per item
+  constexpr int SR = verify_round_blocks<WAVES>();
   static_assert(kSzWin % GI == 0 && KW % kSzWin == 0, "windows must nest");
   __shared__ VerifyShared<M, KW> sh;
   __shared__ __attribute__((aligned(16))) uint32_t szs[WAVES][RT][16][kSzRow];
+  __shared__ VerifyPart<M, RT, SR> part;
   __shared__ int ctr;
+  __shared__ int64_t range[2];
+  __shared__ int first_mat;
   const int lane = lane_id();
   const int wave = wave_id();
   const int rq = lane >> 4;
   const int col = lane & 15;
   uint32_t (*szb)[16][kSzRow] = szs[wave];
   const FmtInt4::K kc = FmtInt4::consts();
+
+  // this workgroup's range: equal shares of the step's cost
+  const double f = cuts.bal->f;
+  const int G = (int)gridDim.x;
+  const double total = cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count];
+  const double c0 = total * (double)blockIdx.x / (double)G;
+  const double c1 = (int)blockIdx.x + 1 == G ? total : total * (double)(blockIdx.x + 1) / (double)G;
+  if (threadIdx.x == 0) {
+    range[0] = mats[cuts.count - 1].batch_begin + mats[cuts.count - 1].batches;
+    range[1] = range[0];
+    first_mat = cuts.count - 1;
+  }
+  __syncthreads();
+  // the block at cost c: first block of matrix i (p0 <= c < p1) whose start
+  // is at or past c; every matrix is checked by one thread
+  for (int i = threadIdx.x; i < cuts.count; i += WAVES * kWave) {
+    const double p0 = cuts.pre_short[i] + f * cuts.pre_long[i];
+    const double p1 = cuts.pre_short[i + 1] + f * cuts.pre_long[i + 1];
+    const GemvArgs& m = mats[i];
+    const double bc = cuts.bcost[i] * (m.chunks > KW ? f : 1.0);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const double c = e == 0 ? c0 : c1;
+      if (p0 <= c && c < p1) {
+        int64_t local = (int64_t)((c - p0) / bc + 0.999999);
+        if (local > m.batches) local = m.batches;
+        range[e] = m.batch_begin + local;
+        if (e == 0) first_mat = i;
+      }
+    }
+  }
+  __syncthreads();
+
   uint32_t av[SETS][4][4];
 #pragma unroll
   for (int st = 0; st < SETS; ++st)
@@ -329,116 +479,81 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
     for (int st = 0; st < SETS; ++st)
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[rt][st][r] = 0.0f;
-  int64_t gb = wg_begin[blockIdx.x];
-  const int64_t gend = wg_begin[blockIdx.x + 1];
-  int mi = wg_mat[blockIdx.x];
+  int64_t gb = uniform_i64(range[0]);
+  const int64_t gend = uniform_i64(range[1]);
+  int mi = __builtin_amdgcn_readfirstlane(first_mat);
+  double tk[2] = {0.0, 0.0}, ck[2] = {0.0, 0.0};
+  long long tprev = 0;
+  int kprev = -1;
   while (gb < gend) {
     const GemvArgs a = mats[mi];
     const int64_t mend = a.batch_begin + a.batches;
+    if (gb >= mend) {   // the range starts at the next matrix
+      ++mi;
+      continue;
+    }
     const int64_t lb = gb - a.batch_begin;
     const int64_t le = (gend < mend ? gend : mend) - a.batch_begin;
     const int groups = a.chunks;
-    if (groups <= KW) {
-      // one activation window: stage once, waves claim whole-row blocks
-      const int items = (groups + GI - 1) / GI;
-      __syncthreads();
-      verify_stage<M, KW, WAVES * 64>(a, 0, items * GI, sh);
-      if (threadIdx.x == 0) ctr = 0;
-      __syncthreads();
-      int64_t blk = lb + claim_batch(&ctr, lane);
-      if (blk < le) {
-        int64_t nxt = lb + claim_batch(&ctr, lane);
-        int it = 0;
-        bool more = true;
-        VerifyItem<RT, OCT> A, B;
-        SzWindow<RT> Z;
-        sz_load<RT>(a, blk, 0, lane, Z);   // first: it is consumed first
-        verify_load<RT, OCT, QL>(a, blk, 0, 0, lane, A);
-        // consumes item (blk, it) from `cur` after requesting the next one
-        // into `nx`; the two buffers alternate, so no loaded value is copied
-        // (a copy would wait for the request just made)
-        auto step = [&](const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
-          if (it % IW == 0) {
-            // the window of this item has arrived: publish it, request the next
-            sz_put<RT>(a, it * GI, lane, Z, szb);
-            const bool same = it + IW < items;
-            const int64_t zb = same ? blk : nxt;
-            sz_load<RT>(a, zb, same ? (it + IW) * GI : 0, lane, Z, zb < le);
-          }
-          int64_t b2 = blk;
-          int i2 = it + 1;
-          if (i2 == items) {
-            b2 = nxt;
-            i2 = 0;
-          }
-          more = b2 < le;
-          verify_load<RT, OCT, QL>(a, b2, 0, i2, lane, nx, more);
-          if (more && i2 == 0) nxt = lb + claim_batch(&ctr, lane);
-          verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
-          if (it + 1 == items) verify_store<M, RT, SETS>(a, blk, rq, col, y);
-          blk = b2;
-          it = i2;
-        };
-        // the prefetch left in flight is drained on the way out: otherwise
-        // the (never taken) CFG edge from an exit test back to the loop head
-        // carries it, and every iteration would wait for all loads
-        for (;;) {
-          step(A, B);
-          if (!more) {
-            wait_vmem_all();
-            break;
-          }
-          step(B, A);
-          if (!more) {
-            wait_vmem_all();
-            break;
-          }
-        }
-      }
-    } else {
-      // longer rows: rounds of one block per wave, activation windows staged
-      // in turn
-      const int64_t rounds = (le - lb + WAVES - 1) / WAVES;
-      for (int64_t rd = 0; rd < rounds; ++rd) {
-        const int64_t blk = lb + rd * WAVES + wave;
-        const bool mine = blk < le;
-        for (int g0 = 0; g0 < groups; g0 += KW) {
-          const int kw = groups - g0 < KW ? groups - g0 : KW;
-          const int items = (kw + GI - 1) / GI;
-          __syncthreads();
-          verify_stage<M, KW, WAVES * 64>(a, g0, items * GI, sh);
-          __syncthreads();
-          if (!mine) continue;
-          VerifyItem<RT, OCT> A, B;
-          SzWindow<RT> Z;
-          sz_load<RT>(a, blk, g0, lane, Z);
-          verify_load<RT, OCT, QL>(a, blk, g0, 0, lane, A);
-          auto step = [&](int it, const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
-            if (it % IW == 0) {
-              sz_put<RT>(a, g0 + it * GI, lane, Z, szb);
-              sz_load<RT>(a, blk, g0 + (it + IW) * GI, lane, Z, it + IW < items);
-            }
-            verify_load<RT, OCT, QL>(a, blk, g0, it + 1, lane, nx, it + 1 < items);
-            verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
-          };
-          for (int it = 0;; it += 2) {
-            step(it, A, B);
-            if (it + 1 >= items) {
-              wait_vmem_all();
-              break;
-            }
-            step(it + 1, B, A);
-            if (it + 2 >= items) {
-              wait_vmem_all();
-              break;
-            }
-          }
-        }
-        if (mine) verify_store<M, RT, SETS>(a, blk, rq, col, y);
+    const int kind = groups > KW;
+    // time of a segment: from the barrier that opens it to the one that
+    // opens the next
+    __syncthreads();
+    const long long now = wall_clock64();
+    if (kprev >= 0) tk[kprev] += (double)(now - tprev);
+    tprev = now;
+    kprev = kind;
+    ck[kind] += (double)(le - lb) * cuts.bcost[mi];
+    // rows within one window: a single round over the whole range; longer
+    // rows: rounds of SR blocks, windows staged in turn
+    const int64_t span = kind ? (int64_t)SR : le - lb;
+    for (int64_t r0 = lb; r0 < le; r0 += span) {
+      const int64_t r1 = le - r0 < span ? le : r0 + span;
+      for (int g0 = 0; g0 < groups; g0 += KW) {
+        const int kw = groups - g0 < KW ? groups - g0 : KW;
+        const int items = (kw + GI - 1) / GI;
+        __syncthreads();
+        verify_stage<M, KW, WAVES * 64>(a, g0, items * GI, sh);
+        if (threadIdx.x == 0) ctr = 0;
+        __syncthreads();
+        verify_window<M, KW, WAVES, RT, OCT, QL, SB, SR>(a, r0, r1, g0, items, g0 == 0, g0 + KW >= groups, &ctr,
+                                                         lane, rq, col, sh, szb, kc, av, y, part);
       }
     }
     gb = a.batch_begin + le;
     ++mi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (kprev >= 0) tk[kprev] += (double)(wall_clock64() - tprev);
+    VerifyBalance* b = cuts.bal;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      atomicAdd(&b->t[e], tk[e]);
+      atomicAdd(&b->c[e], ck[e]);
+    }
+    __threadfence();
+    if (atomicAdd(&b->done, 1) == G - 1) {
+      // every workgroup has reported: the factor for the next launch
+      __threadfence();
+      double t[2], c[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        t[e] = __hip_atomic_load(&b->t[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        c[e] = __hip_atomic_load(&b->c[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (t[0] > 0.0 && t[1] > 0.0 && c[0] > 0.0 && c[1] > 0.0) {
+        double nf = 0.75 * f + 0.25 * ((t[1] / c[1]) / (t[0] / c[0]));
+        nf = fmin(fmax(nf, 0.5), 4.0);
+        __hip_atomic_store(&b->f, nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        __hip_atomic_store(&b->t[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&b->c[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(&b->done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

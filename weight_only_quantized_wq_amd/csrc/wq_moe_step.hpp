@@ -107,6 +107,70 @@ __device__ __forceinline__ void moe_acc_pass(const MoePass<NR, CPL>& p, const ui
   }
 }
 
+// The waves' share of one layer segment: batches [lo, hi) claimed one at a
+// time from `ctr`, each streamed in `passes` passes of NR rows.  The next
+// pass (of this batch or of the batch claimed last) is requested before the
+// current one is reduced; the two pass buffers alternate, so no loaded value
+// is copied (a copy would wait for the loads just issued), and the request is
+// issued on every path (empty rows when there is none), so each pass waits
+// only for its own loads.  rows(b, base, ok) gives batch b's row pointers,
+// scales(b) loads the two bf16 row scales the epilogue of batch b reads, as
+// raw bits, from clamped (always valid) addresses without a branch -- so
+// nothing waits for them before the next pass is requested -- and
+// finish(b, acc, sc) reduces and stores a finished batch.
+template <int NR, int CPL, int CMAX, int PLANES, class Rows, class Scales, class Finish>
+__device__ __forceinline__ void moe_stream(int64_t lo, int64_t hi, int passes, uint32_t row_bytes, int* ctr,
+                                           int lane, const uint32_t* xs, float (&acc)[NR], Rows&& rows,
+                                           Scales&& scales, Finish&& finish) {
+  int64_t cur = lo + claim_batch(ctr, lane);
+  if (cur >= hi) return;
+  int64_t nxt = lo + claim_batch(ctr, lane);
+  int pass = 0;
+  bool more = true;
+  const int8_t* base[NR];
+  bool ok[NR];
+  rows(cur, base, ok);
+  MoePass<NR, CPL> A, B;
+  moe_load_pass<NR, CPL>(base, ok, row_bytes, 0, lane, A);
+  auto step = [&](const MoePass<NR, CPL>& p, MoePass<NR, CPL>& nx) {
+    const int64_t c_batch = cur;
+    const int c_pass = pass;
+    int64_t c2 = cur;
+    int p2 = pass + 1;
+    if (p2 == passes) {
+      c2 = nxt;
+      p2 = 0;
+    }
+    more = c2 < hi;
+    const bool last = c_pass + 1 == passes;
+    const uint2 sc = scales(c_batch);   // every pass: a branch would make the loads wait at its end
+    if (more && p2 == 0) rows(c2, base, ok);
+    bool live[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) live[i] = more && ok[i];
+    moe_load_pass<NR, CPL>(base, live, row_bytes, p2, lane, nx);
+    if (more && p2 == 0) nxt = lo + claim_batch(ctr, lane);
+    moe_acc_pass<NR, CPL, CMAX, PLANES>(p, xs, c_pass, lane, acc);
+    if (last) finish(c_batch, acc, sc);
+    cur = c2;
+    pass = p2;
+  };
+  // the request left in flight is drained on the way out, so that no path
+  // reaches the loop head with loads outstanding
+  for (;;) {
+    step(A, B);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+    step(B, A);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+  }
+}
+
 // Workgroup range [lo, hi) of a launch of `total` batches.
 __device__ __forceinline__ void moe_range(int64_t total, int64_t& lo, int64_t& hi) {
   lo = total * (int64_t)blockIdx.x / (int64_t)gridDim.x;
@@ -159,7 +223,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
 
     // batch b: units j0 .. j0 + U - 1 of expert slot b / half
     auto rows = [&](int64_t b, const int8_t* (&base)[NR], bool (&ok)[NR]) {
-      const int slot = (int)(b / half);
+      const int slot = b >= half ? 1 : 0;   // b < 2 half
       const int64_t j0 = (b - slot * half) * U;
       const int ex = slot == 0 ? ea : eb;
 #pragma unroll
@@ -171,16 +235,24 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
         base[U + u] = L.w13 + (r1 + d.f) * d.dim;
       }
     };
-    auto finish = [&](int64_t b, float (&acc)[NR]) {
+    // this lane's (w1, w3) row scales of batch b (lanes < U)
+    auto scales = [&](int64_t b) -> uint2 {
+      const int slot = b >= half ? 1 : 0;   // b < 2 half
+      int64_t j = (b - slot * half) * U + lane;
+      if (j >= d.f) j = d.f - 1;
+      const int ex = slot == 0 ? ea : eb;
+      const __attribute__((address_space(1))) uint16_t* sc = gmem(L.s13 + (int64_t)ex * 2 * d.f);
+      return uint2{(uint32_t)sc[j], (uint32_t)sc[j + d.f]};
+    };
+    auto finish = [&](int64_t b, float (&acc)[NR], uint2 sc) {
       float tot[NR];
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
         tot[i] = wave_sum(acc[i]);
         acc[i] = bias;
       }
-      const int slot = (int)(b / half);
+      const int slot = b >= half ? 1 : 0;   // b < 2 half
       const int64_t j0 = (b - slot * half) * U;
-      const int ex = slot == 0 ? ea : eb;
       if (lane < U && j0 + lane < d.f) {
         float h1 = 0.0f, h3 = 0.0f;
 #pragma unroll
@@ -190,47 +262,16 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
             h3 = tot[U + u];
           }
         const int64_t j = j0 + lane;
-        const __attribute__((address_space(1))) uint16_t* sc = gmem(L.s13 + (int64_t)ex * 2 * d.f);
-        h1 *= __uint_as_float((uint32_t)sc[j] << 16);
-        h3 *= __uint_as_float((uint32_t)sc[j + d.f] << 16);
+        h1 *= __uint_as_float(sc.x << 16);
+        h3 *= __uint_as_float(sc.y << 16);
         *gmem(L.work + ((int64_t)slot * d.f + j)) = h1 / (1.0f + expf(-h1)) * h3;
       }
     };
 
-    int64_t cur = lo + claim_batch(&ctr, lane);
-    if (cur < hi) {
-      int64_t nxt = lo + claim_batch(&ctr, lane);
-      int pass = 0;
-      float acc[NR];
+    float acc[NR];
 #pragma unroll
-      for (int i = 0; i < NR; ++i) acc[i] = bias;
-      const int8_t* base[NR];
-      bool ok[NR];
-      rows(cur, base, ok);
-      MoePass<NR, CPL> A;
-      moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.dim, 0, lane, A);
-      for (;;) {
-        MoePass<NR, CPL> C = A;
-        const int64_t c_batch = cur;
-        const int c_pass = pass;
-        int64_t c2 = cur;
-        int p2 = pass + 1;
-        if (p2 == passes) {
-          c2 = nxt;
-          p2 = 0;
-        }
-        const bool more = c2 < hi;
-        if (more && p2 == 0) rows(c2, base, ok);
-        if (PF && more) moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.dim, p2, lane, A);
-        if (more && p2 == 0) nxt = lo + claim_batch(&ctr, lane);
-        moe_acc_pass<NR, CPL, CMAX, 1>(C, xs, c_pass, lane, acc);
-        if (c_pass + 1 == passes) finish(c_batch, acc);
-        if (!more) break;
-        if (!PF) moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.dim, p2, lane, A);
-        cur = c2;
-        pass = p2;
-      }
-    }
+    for (int i = 0; i < NR; ++i) acc[i] = bias;
+    moe_stream<NR, CPL, CMAX, 1>(lo, hi, passes, (uint32_t)d.dim, &ctr, lane, xs, acc, rows, scales, finish);
     gb = (int64_t)layer * per_layer + hi;
   }
 }
@@ -285,7 +326,13 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerD
         base[U + u] = L.w2 + ((int64_t)eb * d.dim + nn) * d.f;
       }
     };
-    auto finish = [&](int64_t b, float (&acc)[NR]) {
+    // this lane's row scales of batch b in experts a and b (lanes < U)
+    auto scales = [&](int64_t b) -> uint2 {
+      int64_t n = b * U + lane;
+      if (n >= d.dim) n = d.dim - 1;
+      return uint2{(uint32_t)*gmem(L.s2 + ((int64_t)ea * d.dim + n)), (uint32_t)*gmem(L.s2 + ((int64_t)eb * d.dim + n))};
+    };
+    auto finish = [&](int64_t b, float (&acc)[NR], uint2 sc) {
       float tot[NR];
 #pragma unroll
       for (int i = 0; i < NR; ++i) {
@@ -301,48 +348,16 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerD
             oa = tot[u];
             ob = tot[U + u];
           }
-        const float sa = __uint_as_float((uint32_t)*gmem(L.s2 + ((int64_t)ea * d.dim + n)) << 16);
-        const float sb = __uint_as_float((uint32_t)*gmem(L.s2 + ((int64_t)eb * d.dim + n)) << 16);
-        const float y = ga * (sa * oa) + gbt * (sb * ob);
+        const float y = ga * (__uint_as_float(sc.x << 16) * oa) + gbt * (__uint_as_float(sc.y << 16) * ob);
         if (L.y32) *gmem(L.y32 + n) = y;
         if (L.y16) *gmem(L.y16 + n) = f32_to_bf16(y);
       }
     };
 
-    int64_t cur = lo + claim_batch(&ctr, lane);
-    if (cur < hi) {
-      int64_t nxt = lo + claim_batch(&ctr, lane);
-      int pass = 0;
-      float acc[NR];
+    float acc[NR];
 #pragma unroll
-      for (int i = 0; i < NR; ++i) acc[i] = bias[i < U ? 0 : 1];
-      const int8_t* base[NR];
-      bool ok[NR];
-      rows(cur, base, ok);
-      MoePass<NR, CPL> A;
-      moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.f, 0, lane, A);
-      for (;;) {
-        MoePass<NR, CPL> C = A;
-        const int64_t c_batch = cur;
-        const int c_pass = pass;
-        int64_t c2 = cur;
-        int p2 = pass + 1;
-        if (p2 == passes) {
-          c2 = nxt;
-          p2 = 0;
-        }
-        const bool more = c2 < hi;
-        if (more && p2 == 0) rows(c2, base, ok);
-        if (PF && more) moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.f, p2, lane, A);
-        if (more && p2 == 0) nxt = lo + claim_batch(&ctr, lane);
-        moe_acc_pass<NR, CPL, CMAX, 2>(C, xs, c_pass, lane, acc);
-        if (c_pass + 1 == passes) finish(c_batch, acc);
-        if (!more) break;
-        if (!PF) moe_load_pass<NR, CPL>(base, ok, (uint32_t)d.f, p2, lane, A);
-        cur = c2;
-        pass = p2;
-      }
-    }
+    for (int i = 0; i < NR; ++i) acc[i] = bias[i < U ? 0 : 1];
+    moe_stream<NR, CPL, CMAX, 2>(lo, hi, passes, (uint32_t)d.f, &ctr, lane, xs, acc, rows, scales, finish);
     gb = (int64_t)layer * per_layer + hi;
   }
 }

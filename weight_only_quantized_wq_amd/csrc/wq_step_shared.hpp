@@ -83,11 +83,26 @@ __device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int 
   }
 }
 
-// Accumulates one batch-pass; after the row's last pass, reduces and stores.
+// Raw bf16 bits of the row scale of row batch * U + lane (formats with a
+// row scale; clamped to a valid row, so the load needs no branch and nothing
+// waits for it before the next pass is requested).
+template <class F, int U>
+__device__ __forceinline__ uint32_t row_scale_bits(const GemvArgs& a, int64_t batch, int lane) {
+  if constexpr (F::kRowScale) {
+    int64_t r = batch * U + (lane < U ? lane : 0);
+    if (r >= a.n) r = a.n - 1;
+    return (uint32_t)*gmem(a.scale + r);
+  } else {
+    return 0u;
+  }
+}
+
+// Accumulates one batch-pass; after the row's last pass, reduces and stores
+// (`sbits`: this lane's row_scale_bits of the batch).
 template <class F, int U, int CPL, int CMAX>
 __device__ __forceinline__ void finish_pass(const GemvArgs& a, int64_t batch, int pass, int passes, int lane,
                                             const PassBuf<U, CPL>& bt, const uint32_t* xs,
-                                            const typename F::K& kc, float (&acc)[U], float bias) {
+                                            const typename F::K& kc, float (&acc)[U], float bias, uint32_t sbits) {
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const typename F::X xv = F::lds_x(xs, CMAX, (pass * CPL + j) * kWave + lane);
@@ -112,7 +127,7 @@ __device__ __forceinline__ void finish_pass(const GemvArgs& a, int64_t batch, in
       if (lane == u) v = tot[u];
     const int64_t r = batch * U + lane;
     if (r < a.n) {
-      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)*gmem(a.scale + r) << 16);
+      if constexpr (F::kRowScale) v *= __uint_as_float(sbits << 16);
       if (a.y32) *gmem(a.y32 + r) = v;
       if (a.y16) *gmem(a.y16 + r) = f32_to_bf16(v);
     }
@@ -151,10 +166,14 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
         p2 = 0;
       }
       bool more = c2 < le;
+      uint32_t sb = row_scale_bits<F, U>(a, cur, lane);
       load_pass<F, U, CPL>(a, c2, p2, lane, B, more);
       if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
-      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, A, xs, kc, acc, bias);
-      if (!more) break;
+      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, A, xs, kc, acc, bias, sb);
+      if (!more) {
+        wait_vmem_all();   // no path reaches the loop head with the last request in flight
+        break;
+      }
       cur = c2;
       pass = p2;
 
@@ -165,16 +184,21 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
         p2 = 0;
       }
       more = c2 < le;
+      sb = row_scale_bits<F, U>(a, cur, lane);
       load_pass<F, U, CPL>(a, c2, p2, lane, A, more);
       if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
-      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, B, xs, kc, acc, bias);
-      if (!more) break;
+      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, B, xs, kc, acc, bias, sb);
+      if (!more) {
+        wait_vmem_all();
+        break;
+      }
       cur = c2;
       pass = p2;
     }
   } else {
     for (;;) {
-      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, A, xs, kc, acc, bias);
+      finish_pass<F, U, CPL, CMAX>(a, cur, pass, passes, lane, A, xs, kc, acc, bias,
+                                   row_scale_bits<F, U>(a, cur, lane));
       if (++pass == passes) {
         pass = 0;
         cur = nxt;

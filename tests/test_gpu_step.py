@@ -126,3 +126,38 @@ def test_step_argument_errors():
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
     assert ei.value.status == 2
+
+
+@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g32", 2), ("int4g32", 5)])
+def test_step_balance_never_changes_results(fmt, m):
+    """Each launch re-cuts the workgroups' ranges from the balance state the
+    previous launches measured (XCD speed weights for one token row, the
+    long-row cost factor for 2..8); which workgroup streams a row must never
+    change the row's bits.  30 launches of one plan, and a fresh plan whose
+    state starts from the prior, all give the first launch's outputs."""
+    import torch
+    import weight_only_quantized_wq_amd as wq
+    say(f"balance {fmt} m={m}")
+    mats, _ = _build(fmt, m, 2)
+    ws = torch.empty(wq.wq_decode_step_workspace_bytes(len(mats)), dtype=torch.uint8, device="cuda")
+    plan = wq.wq_decode_step_prepare(fmt, m, mats, ws)
+    wq.wq_decode_step_run(plan)
+    torch.cuda.synchronize()
+    first = [(host(mt[5]).copy(), host_u16(mt[6]).copy()) for mt in mats]
+    for rep in range(30):
+        for mt in mats:
+            mt[5].fill_(-7.0)
+            mt[6].fill_(0x7BAD)
+        wq.wq_decode_step_run(plan)
+        torch.cuda.synchronize()
+        for mt, (f32, f16) in zip(mats, first):
+            assert np.array_equal(host(mt[5]), f32), f"launch {rep + 2}: fp32 outputs differ"
+            assert np.array_equal(host_u16(mt[6]), f16), f"launch {rep + 2}: bf16 outputs differ"
+    ws2 = torch.empty_like(ws)
+    plan2 = wq.wq_decode_step_prepare(fmt, m, mats, ws2)
+    for mt in mats:
+        mt[5].fill_(-7.0)
+    wq.wq_decode_step_run(plan2)
+    torch.cuda.synchronize()
+    for mt, (f32, _) in zip(mats, first):
+        assert np.array_equal(host(mt[5]), f32), "a fresh plan differs"

@@ -52,15 +52,27 @@ template <class F, int U, int CPL>
 struct Batch {
   u32x4 w[U][CPL];
   uint32_t aux[U][CPL];
+  uint32_t sb;   // formats with a row scale: raw bf16 bits of this lane's output row (finish_batch)
 };
 
 // Requests batch b's weights through per-row buffer resources: a row past
 // n gets an empty resource and a chunk past the row lies past the resource's
 // end, so both read as zero without a branch.  off[j] = 16 * chunk index.
-template <class F, int U, int CPL>
+// The row scale the epilogue of lane l needs (row r0 + l / M) is requested
+// with the batch, from a clamped row, so nothing waits for it inside the
+// epilogue's branch.
+template <class F, int U, int CPL, int M = 1>
 __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg, const uint32_t (&off)[CPL],
                                            Batch<F, U, CPL>& bt, int cpl = CPL) {
   const int64_t r0 = b * ((int64_t)a.groups * U) + (int64_t)rg * U;
+  if constexpr (F::kRowScale) {
+    const int lane = lane_id();
+    int64_t rs = r0 + (lane < U * M ? lane / M : 0);
+    if (rs >= a.n) rs = a.n - 1;
+    bt.sb = (uint32_t)*gmem(a.scale + rs);
+  } else {
+    bt.sb = 0u;
+  }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t r = r0 + u;
@@ -143,7 +155,7 @@ __device__ __forceinline__ void finish_batch(const GemvArgs& a, int64_t b, int l
     const int m = lane - u * M;
     const int64_t r = r0 + u;
     if (r < a.n) {
-      if constexpr (F::kRowScale) v *= __uint_as_float((uint32_t)*gmem(a.scale + r) << 16);
+      if constexpr (F::kRowScale) v *= __uint_as_float(bt.sb << 16);
       if (a.y32) *gmem(a.y32 + (m * a.n + r)) = v;
       if (a.y16) *gmem(a.y16 + (m * a.n + r)) = f32_to_bf16(v);
     }
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
   int64_t b = blockIdx.x;
   const int64_t step = gridDim.x;
   Batch<F, U, CPL> A;
-  load_batch<F, U, CPL>(a, b, rg, off, A);
+  load_batch<F, U, CPL, M>(a, b, rg, off, A);
 
   typename F::X xr[M][CPL];
   float bias[M];
@@ -189,11 +201,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
   if constexpr (PF) {
     Batch<F, U, CPL> B;
     while (b < a.batches) {
-      load_batch<F, U, CPL>(a, b + step, rg, off, B);
+      load_batch<F, U, CPL, M>(a, b + step, rg, off, B);
       finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf);
       b += step;
       if (b >= a.batches) break;
-      load_batch<F, U, CPL>(a, b + step, rg, off, A);
+      load_batch<F, U, CPL, M>(a, b + step, rg, off, A);
       finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, B, xr, bias, kc, red, buf);
       b += step;
     }
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(GemvArgs a) {
     while (b < a.batches) {
       finish_batch<F, M, CPL, U, WAVES>(a, b, lane, wave, ks, rg, A, xr, bias, kc, red, buf);
       b += step;
-      if (b < a.batches) load_batch<F, U, CPL>(a, b, rg, off, A);
+      if (b < a.batches) load_batch<F, U, CPL, M>(a, b, rg, off, A);
     }
   }
 }

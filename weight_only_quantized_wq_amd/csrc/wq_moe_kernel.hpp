@@ -53,6 +53,7 @@ __device__ __forceinline__ void route_top2(const float* logits_ptr, int e, int& 
 template <int CPL>
 struct W13Batch {
   u32x4 w[2][CPL];
+  uint32_t sc[2];   // raw bf16 scales of rows j and j + f (requested with the batch)
 };
 
 template <int CPL>
@@ -69,6 +70,9 @@ __device__ __forceinline__ void w13_load(const MoeArgs& a, int64_t bt, int rg, i
     const __amdgpu_buffer_rsrc_t r = buffer_rsrc(a.w13 + row * a.dim, ok ? (uint32_t)a.dim : 0u);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) B.w[u][j] = buffer_load16_nt(r, off[j]);
+    // the epilogue's scales, loaded here (a valid row also past the end) so
+    // that nothing waits for them inside the epilogue's branch
+    B.sc[u] = (uint32_t)a.s13[row];
   }
 }
 
@@ -110,10 +114,8 @@ __device__ __forceinline__ void w13_finish(const MoeArgs& a, int64_t bt, int lan
   if (ks == 0 && lane == 0 && unit < 2 * a.f) {
     const int slot = (int)(unit / a.f);
     const int64_t jrow = unit - (int64_t)slot * a.f;
-    const int ex = slot == 0 ? ea : eb;
-    const uint16_t* sc = a.s13 + (int64_t)ex * 2 * a.f;
-    float h1 = tot[0] * __uint_as_float((uint32_t)sc[jrow] << 16);
-    float h3 = tot[1] * __uint_as_float((uint32_t)sc[jrow + a.f] << 16);
+    float h1 = tot[0] * __uint_as_float(B.sc[0] << 16);
+    float h3 = tot[1] * __uint_as_float(B.sc[1] << 16);
     float silu = h1 / (1.0f + expf(-h1));
     a.work[(int64_t)slot * a.f + jrow] = silu * h3;
   }
@@ -190,10 +192,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_kernel(MoeArgs a) {
 template <int CPL, int U>
 struct W2Batch {
   u32x4 w[U][CPL];
+  uint32_t sc[2];   // raw bf16 scales of this lane's output row in experts a and b
 };
 
 template <int CPL, int U>
-__device__ __forceinline__ void w2_load(const MoeArgs& a, int64_t bt, const int8_t* base,
+__device__ __forceinline__ void w2_load(const MoeArgs& a, int64_t bt, const int8_t* base, int ea, int eb,
                                         const uint32_t (&off)[CPL], W2Batch<CPL, U>& B) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -203,6 +206,12 @@ __device__ __forceinline__ void w2_load(const MoeArgs& a, int64_t bt, const int8
 #pragma unroll
     for (int j = 0; j < CPL; ++j) B.w[u][j] = buffer_load16_nt(rs, off[j]);
   }
+  // the epilogue's scales (lane l < U: row bt U + l; clamped to a valid row)
+  const int lane = lane_id();
+  int64_t r = bt * U + (lane < U ? lane : 0);
+  if (r >= a.dim) r = a.dim - 1;
+  B.sc[0] = (uint32_t)a.s2[(int64_t)ea * a.dim + r];
+  B.sc[1] = (uint32_t)a.s2[(int64_t)eb * a.dim + r];
 }
 
 template <int CPL, int WAVES, int U>
@@ -234,8 +243,8 @@ __device__ __forceinline__ void w2_finish(const MoeArgs& a, int64_t bt, int lane
         for (int s = 1; s < S; ++s) v += red[buf][tm * S + s][lane];
         o[tm] = v;
       }
-      const float sa = __uint_as_float((uint32_t)a.s2[(int64_t)ea * a.dim + r] << 16);
-      const float sb = __uint_as_float((uint32_t)a.s2[(int64_t)eb * a.dim + r] << 16);
+      const float sa = __uint_as_float(B.sc[0] << 16);
+      const float sb = __uint_as_float(B.sc[1] << 16);
       const float y = ga * (sa * o[0]) + gb * (sb * o[1]);
       if (a.y32) *gmem(a.y32 + r) = y;
       if (a.y16) *gmem(a.y16 + r) = f32_to_bf16(y);
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_kernel(MoeArgs a) {
   int64_t bt = blockIdx.x;
   const int64_t step = gridDim.x;
   W2Batch<CPL, U> A;
-  w2_load<CPL, U>(a, bt, base, off, A);
+  w2_load<CPL, U>(a, bt, base, ea, eb, off, A);
 
   F::X xr[CPL];
   float bias = 0.0f;
@@ -285,11 +294,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_kernel(MoeArgs a) {
   if constexpr (PF) {
     W2Batch<CPL, U> B;
     while (bt < a.batches) {
-      w2_load<CPL, U>(a, bt + step, base, off, B);
+      w2_load<CPL, U>(a, bt + step, base, ea, eb, off, B);
       w2_finish<CPL, WAVES, U>(a, bt, lane, wave, ea, eb, ga, gb, A, xr, bias, red, buf);
       bt += step;
       if (bt >= a.batches) break;
-      w2_load<CPL, U>(a, bt + step, base, off, A);
+      w2_load<CPL, U>(a, bt + step, base, ea, eb, off, A);
       w2_finish<CPL, WAVES, U>(a, bt, lane, wave, ea, eb, ga, gb, B, xr, bias, red, buf);
       bt += step;
     }
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_kernel(MoeArgs a) {
     while (bt < a.batches) {
       w2_finish<CPL, WAVES, U>(a, bt, lane, wave, ea, eb, ga, gb, A, xr, bias, red, buf);
       bt += step;
-      if (bt < a.batches) w2_load<CPL, U>(a, bt, base, off, A);
+      if (bt < a.batches) w2_load<CPL, U>(a, bt, base, ea, eb, off, A);
     }
   }
 }

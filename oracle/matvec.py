@@ -17,7 +17,7 @@ as bf16 bit patterns (or, for the MoE second projection, as fp64 values).
 import numpy as np
 
 from .bf16 import bf16_to_f64
-from .quant import dequantize_int8, dequantize_int4g32
+from .quant import dequantize_int8, dequantize_int4
 
 
 def activations_f64(x_bits):
@@ -49,13 +49,17 @@ def gemv_int8_f64x(x64, q, s):
     return gemv_dequantized(x64, dequantize_int8(q, s))
 
 
-def gemv_int4g32(x_bits, packed, sz):
-    """int4 G=32 weights: y[n] = sum_g (s[n,g] sum_{k in g} x[k] q[n,k] + z[n,g] sum_{k in g} x[k])."""
-    return gemv_dequantized(activations_f64(x_bits), dequantize_int4g32(packed, sz))
+def gemv_int4(x_bits, packed, sz):
+    """int4 weights in groups of G = K / sz.shape[1]:
+    y[n] = sum_g (s[n,g] sum_{k in g} x[k] q[n,k] + z[n,g] sum_{k in g} x[k])."""
+    return gemv_dequantized(activations_f64(x_bits), dequantize_int4(packed, sz))
+
+
+gemv_int4g32 = gemv_int4   # the G = 32 name
 
 
 def gemm_small_m(x_bits, packed, sz):
-    """Speculative verify: M token rows x [M, K] against int4 G=32 weights -> [M, N]."""
+    """Speculative verify: M token rows x [M, K] against int4 weights -> [M, N]."""
     x_bits = np.asarray(x_bits)
     if x_bits.ndim != 2:
         raise ValueError("x must be [M, K]")

@@ -21,8 +21,10 @@ Readings taken where the pages are silent (the plainest ones):
   q = round-half-even(w / s) of the exact real quotient, clamped to
   [-127, 127].  The stored bf16 s is the one the codes are taken against, so
   |w - q s| <= s/2 holds exactly.  A zero scale gives zero codes.
-* int4: asymmetric, 32 consecutive inputs of one output row per group.  The
-  zero z = bf16(min) is the value code 0 decodes to; t = fp32(max - z);
+* int4: asymmetric, G consecutive inputs of one output row per group (G = 32
+  unless stated; the group-size knob also takes 64, 128 and 256, which store
+  0.5 + 4/G bytes per weight).  The zero z = bf16(min) is the value code 0
+  decodes to; t = fp32(max - z);
   s = bf16(fp32(t / 15)) when t > 0, else s = 0; codes are
   round-half-even((w - z) / s) of the exact real quotient clamped to [0, 15]
   (all zero when s == 0); w ~ z + q s.
@@ -40,6 +42,7 @@ import numpy as np
 from .bf16 import round_f32_to_bf16, bf16_to_f32, bf16_to_f64
 
 GROUP = 32
+GROUPS = (32, 64, 128, 256)   # group sizes the library supports
 INT8_MAX = 127
 INT4_MAX = 15
 
@@ -122,17 +125,17 @@ def dequantize_int8(q, s):
 
 
 # ----------------------------------------------------------------------------
-# int4, groups of 32 inputs, bf16 scale and zero
+# int4, groups of G inputs (32 by default), bf16 scale and zero
 
 
-def int4g32_scale_zero(w):
-    """Per-group (s, z) bf16 bit patterns, each [N, K/32].
+def int4_scale_zero(w, group=GROUP):
+    """Per-group (s, z) bf16 bit patterns, each [N, K/group].
 
     z = bf16(min), t = fp32(max - z), s = bf16(fp32(t / 15)) if t > 0 else 0.
     """
     w = np.asarray(w, np.float32)
     n, k = w.shape
-    g = w.reshape(n, k // GROUP, GROUP)
+    g = w.reshape(n, k // group, group)
     mn = g.min(axis=2)
     mx = g.max(axis=2)
     z = round_f32_to_bf16(mn)
@@ -142,11 +145,11 @@ def int4g32_scale_zero(w):
     return s, z
 
 
-def int4g32_codes(w, s, z):
+def int4_codes(w, s, z, group=GROUP):
     """Codes q[n, k] in [0, 15] and the count of codes the clamp changed."""
     w = np.asarray(w, np.float32)
     n, k = w.shape
-    g = w.reshape(n, k // GROUP, GROUP).astype(np.float64)
+    g = w.reshape(n, k // group, group).astype(np.float64)
     sv = bf16_to_f64(s)[..., None]
     zv = bf16_to_f64(z)[..., None]
     q = np.zeros(g.shape, np.float64)
@@ -174,20 +177,22 @@ def unpack_int4(packed):
     return q
 
 
-def quantize_int4g32(w, return_clamped=False):
-    """W fp32 [N, K] (K % 32 == 0) -> (packed u8 [N, K/2], sz u16 [N, K/32, 2]).
+def quantize_int4(w, group=GROUP, return_clamped=False):
+    """W fp32 [N, K] (K % group == 0) -> (packed u8 [N, K/2], sz u16 [N, K/group, 2]).
 
     With ``return_clamped`` also returns how many codes the [0, 15] clamp
     changed (never any for groups that span zero; only a group of one sign
     whose range is tiny next to its magnitude can clamp at code 0).
     """
+    if group not in GROUPS:
+        raise ValueError(f"group must be one of {GROUPS}")
     w = np.asarray(w, np.float32)
-    if w.ndim != 2 or w.shape[1] % GROUP != 0:
-        raise ValueError("W must be [N, K] with K a multiple of 32")
+    if w.ndim != 2 or w.shape[1] % group != 0:
+        raise ValueError(f"W must be [N, K] with K a multiple of {group}")
     _check_finite(w)
     n, k = w.shape
-    s, z = int4g32_scale_zero(w)
-    q, clamped = int4g32_codes(w, s, z)
+    s, z = int4_scale_zero(w, group)
+    q, clamped = int4_codes(w, s, z, group)
     packed = pack_int4(q)
     sz = np.stack([s, z], axis=-1).astype(np.uint16)
     if return_clamped:
@@ -195,11 +200,32 @@ def quantize_int4g32(w, return_clamped=False):
     return packed, sz
 
 
-def dequantize_int4g32(packed, sz):
-    """deq[n, k] = z[n, g] + q[n, k] * s[n, g] with g = k // 32, exact in fp64."""
+def dequantize_int4(packed, sz):
+    """deq[n, k] = z[n, g] + q[n, k] * s[n, g] with g = k // G, exact in fp64;
+    the group size G is K over the number of (s, z) pairs per row."""
     q = unpack_int4(packed).astype(np.float64)
     n, k = q.shape
+    groups = sz.shape[1]
+    if groups == 0 or k % groups:
+        raise ValueError("sz must hold K/G (scale, zero) pairs per row")
     s = bf16_to_f64(sz[..., 0])
     z = bf16_to_f64(sz[..., 1])
-    g = q.reshape(n, k // GROUP, GROUP)
+    g = q.reshape(n, groups, k // groups)
     return (z[..., None] + g * s[..., None]).reshape(n, k)
+
+
+# The G = 32 names: the benchmark table's "4-bit (G=32)" format.
+def quantize_int4g32(w, return_clamped=False):
+    """``quantize_int4`` with groups of 32."""
+    return quantize_int4(w, GROUP, return_clamped)
+
+
+def int4g32_scale_zero(w):
+    return int4_scale_zero(w, GROUP)
+
+
+def int4g32_codes(w, s, z):
+    return int4_codes(w, s, z, GROUP)
+
+
+dequantize_int4g32 = dequantize_int4

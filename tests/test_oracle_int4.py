@@ -177,3 +177,101 @@ def test_clamp_is_reported_for_tight_one_signed_groups():
     q = unpack_int4(packed)
     assert q.min() >= 0 and q.max() <= 15
     assert clamped >= 1
+
+
+# ----------------------------------------------------------------------------
+# The group-size knob: G = 64, 128, 256 (the pages' int4 format takes a group
+# size; the benchmark table shows G = 32).  The same readings per group of G.
+
+from oracle.quant import quantize_int4, dequantize_int4, GROUPS
+from oracle.matvec import gemv_int4
+
+LARGE = [g for g in GROUPS if g != 32]
+
+
+@pytest.mark.parametrize("group", LARGE)
+def test_groups_brute_force_argmin_over_all_codes(group):
+    rng = np.random.default_rng(group)
+    n, k = 3, 2 * group
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    packed, sz = quantize_int4(w, group)
+    assert packed.shape == (n, k // 2) and sz.shape == (n, k // group, 2)
+    q = unpack_int4(packed)
+    for r in range(n):
+        for g in range(k // group):
+            grp = w[r, group * g:group * (g + 1)]
+            s_ex, z_ex = _independent_scale_zero(grp)
+            assert frac_of_bf16(int(sz[r, g, 0])) == s_ex
+            assert frac_of_bf16(int(sz[r, g, 1])) == z_ex
+            for c in range(0, group, 7):
+                wv = Fraction(float(grp[c]))
+                best = min(range(16), key=lambda code: (abs(wv - (z_ex + code * s_ex)), code % 2))
+                assert q[r, group * g + c] == best
+
+
+@pytest.mark.parametrize("group", LARGE)
+def test_groups_span_group_inputs_not_32(group):
+    """A row whose 32-input blocks have disjoint ranges: with groups of G the
+    (scale, zero) of each group covers all G inputs (min of the first block,
+    max of the last), which no group of 32 reproduces."""
+    blocks = group // 32
+    w = np.concatenate([np.linspace(b, b + 0.5, 32, dtype=np.float32) for b in range(blocks)])[None, :]
+    packed, sz = quantize_int4(w, group)
+    assert sz.shape == (1, 1, 2)
+    s_ex, z_ex = _independent_scale_zero(w[0])
+    assert z_ex == 0 and frac_of_bf16(int(sz[0, 0, 1])) == 0
+    assert frac_of_bf16(int(sz[0, 0, 0])) == s_ex == round_to_bf16(round_to_f32(Fraction(blocks - 0.5) / 15))
+    q = unpack_int4(packed)
+    assert q[0, 0] == 0 and q[0, -1] == 15
+    p32, sz32 = quantize_int4(w, 32)
+    assert sz32.shape == (1, blocks, 2) and not np.array_equal(unpack_int4(p32), q)
+
+
+@pytest.mark.parametrize("group", LARGE)
+def test_groups_error_bound_extremes_and_identity(group):
+    rng = np.random.default_rng(100 + group)
+    w = (rng.standard_normal((16, 4 * group)) * 0.02).astype(np.float32)
+    packed, sz, clamped = quantize_int4(w, group, return_clamped=True)
+    assert clamped == 0
+    deq = dequantize_int4(packed, sz)
+    s = np.repeat(bf16_to_f64(sz[..., 0]), group, axis=1)
+    assert np.all(np.abs(w.astype(np.float64) - deq) <= s / 2)
+    q = unpack_int4(packed).reshape(16, 4, group)
+    gw = w.reshape(16, 4, group)
+    assert np.all(np.take_along_axis(q, gw.argmin(axis=2)[..., None], 2) == 0)
+    assert np.all(np.take_along_axis(q, gw.argmax(axis=2)[..., None], 2) == 15)
+    # identity: every group holds at most one 1, so s = bf16(1/15), z = 0 as for G = 32
+    k = 2 * group
+    pe, sze = quantize_int4(np.eye(k, dtype=np.float32), group)
+    rows = np.arange(k)
+    assert np.all(sze[rows, rows // group, 0] == 0x3D89) and np.all(sze[..., 1] == 0)
+    x = (rng.standard_normal(k).astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)
+    y = gemv_int4((x.view(np.uint32) >> 16).astype(np.uint16), pe, sze)
+    assert np.array_equal(y, x.astype(np.float64) * float(C_ID))
+
+
+@pytest.mark.parametrize("group", LARGE)
+def test_groups_matvec_exact_rational(group):
+    rng = np.random.default_rng(200 + group)
+    n, k = 3, 2 * group
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    packed, sz = quantize_int4(w, group)
+    x = (rng.standard_normal(k).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = gemv_int4(x, packed, sz)
+    q = unpack_int4(packed)
+    xf = [frac_of_bf16(int(v)) for v in x]
+    for r in range(n):
+        total = Fraction(0)
+        for g in range(k // group):
+            s = frac_of_bf16(int(sz[r, g, 0]))
+            z = frac_of_bf16(int(sz[r, g, 1]))
+            lo, hi = group * g, group * (g + 1)
+            total += s * sum((int(q[r, c]) * xf[c] for c in range(lo, hi)), Fraction(0)) + z * sum(xf[lo:hi], Fraction(0))
+        assert abs(Fraction(float(y[r])) - total) <= abs(total) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 30)
+
+
+def test_group_argument_checks():
+    with pytest.raises(ValueError):
+        quantize_int4(np.zeros((2, 64), np.float32), 48)
+    with pytest.raises(ValueError):
+        quantize_int4(np.zeros((2, 96), np.float32), 64)

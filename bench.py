@@ -218,13 +218,13 @@ def cpu_baseline(wl_name, target_s):
     """The CPU oracle (fp64 dequantize + BLAS matvec) on a bounded sample of the
     workload's matrices, host-generated; GB/s of the same algorithmic bytes."""
     import numpy as np
-    from oracle.quant import quantize_int8, quantize_int4g32, dequantize_int8
+    from oracle.quant import quantize_int8, quantize_int4
     from oracle.bf16 import round_f32_to_bf16
-    from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
+    from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4, gemm_small_m
     from oracle.moe import moe_top2
     from synth.workloads import WORKLOADS
     from synth.gen import host_normal, host_bf16_normal, host_logits
-    from weight_only_quantized_wq_amd.layerset import matrix_bytes, moe_layer_bytes
+    from weight_only_quantized_wq_amd.layerset import matrix_bytes, moe_layer_bytes, int4_group
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -249,10 +249,10 @@ def cpu_baseline(wl_name, target_s):
         for mat in mats:
             w = host_normal((mat.n, mat.k), wl.sigma, 78, mat.mid)
             x = host_bf16_normal((wl.m, mat.k) if wl.m > 1 else (mat.k,), 78, mat.mid, 1)
-            if wl.fmt == "int4g32":
-                p, sz = quantize_int4g32(w)
+            if int4_group(wl.fmt):
+                p, sz = quantize_int4(w, int4_group(wl.fmt))
                 fn = (lambda x=x, p=p, sz=sz: gemm_small_m(x, p, sz)) if wl.m > 1 else \
-                     (lambda x=x, p=p, sz=sz: gemv_int4g32(x, p, sz))
+                     (lambda x=x, p=p, sz=sz: gemv_int4(x, p, sz))
             elif wl.fmt == "int8":
                 q, s = quantize_int8(w)
                 fn = lambda x=x, q=q, s=s: gemv_int8(x, q, s)

@@ -202,10 +202,13 @@ def quantize_int4(w, group=GROUP, return_clamped=False):
 
 def dequantize_int4(packed, sz):
     """deq[n, k] = z[n, g] + q[n, k] * s[n, g] with g = k // G, exact in fp64;
-    the group size G is K over the number of (s, z) pairs per row."""
+    the group size G is K over the number of (s, z) pairs per row.  K = 0
+    (no groups) is the empty [n, 0] matrix."""
     q = unpack_int4(packed).astype(np.float64)
     n, k = q.shape
     groups = sz.shape[1]
+    if k == 0 and groups == 0:
+        return q
     if groups == 0 or k % groups:
         raise ValueError("sz must hold K/G (scale, zero) pairs per row")
     s = bf16_to_f64(sz[..., 0])

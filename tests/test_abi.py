@@ -32,7 +32,8 @@ def wq():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32",
+    for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_quantize_int4", "wq_gemv_bf16", "wq_gemv_int8",
+                 "wq_gemv_int4g32", "wq_gemv_int4",
                  "wq_gemm_smallM", "moe_top2_gemv", "wq_status_string", "wq_last_error",
                  "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
                  "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run"]:
@@ -79,6 +80,19 @@ def test_shape_errors(wq):
     assert _rc("moe_top2_gemv", BAD, BAD, 4, BAD, BAD, BAD, BAD, 64, 64, BAD, BAD, None, None, None, None) == 2
     assert _rc("moe_top2_gemv", BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 40, BAD, BAD, None, None, None, None) == 2
     assert "multiple" in wq.last_error() or "16" in wq.last_error()
+
+
+def test_group_size_errors(wq):
+    # group sizes other than 32/64/128/256, and k not a multiple of the group
+    assert _rc("wq_quantize_int4", BAD, 4, 96, 48, BAD, BAD, None) == 2
+    assert _rc("wq_quantize_int4", BAD, 4, 96, 64, BAD, BAD, None) == 2
+    assert "k % 64" in wq.last_error()
+    assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 256, 16, BAD, None, None) == 2
+    assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 192, 128, BAD, None, None) == 2
+    assert _rc("wq_gemv_int4", BAD, BAD, None, 4, 256, 128, BAD, None, None) == 1    # null before sizes
+    # alignment is checked after sizes, before any launch (n = 0)
+    assert _rc("wq_quantize_int4", BAD, 0, 256, 128, 0x2000, 0x2000, None) == 3
+    assert _rc("wq_gemv_int4", BAD, 0x2000, 0x2000, 0, 256, 128, 0x2000, None, None) == 3
 
 
 def test_alignment_errors_before_any_launch(wq):

@@ -185,3 +185,26 @@ def test_misaligned_pointers_rejected(wq):
         with pytest.raises(wq.WQError) as ei:
             call()
         assert ei.value.status == 3
+
+
+GROUP_SHAPES = [(64, 37, 64), (128, 300, 4096), (256, 40, 11008 // 256 * 256), (64, 40, 11008), (128, 17, 28672),
+                (256, 2, 131072), (128, 7, 0)]
+
+
+@pytest.mark.parametrize("group,n,k", GROUP_SHAPES)
+def test_gemv_int4_groups(wq, group, n, k):
+    """int4 with groups of 64/128/256: each 32-input chunk applies its group's
+    (scale, zero); the same tolerances as G = 32."""
+    from oracle.quant import quantize_int4
+    from oracle.matvec import gemv_int4
+    say(f"gemv_int4 group={group} n={n} k={k}")
+    w = host_normal((n, k), 0.02, 941, n, k, group)
+    p, sz = quantize_int4(w, group) if k else (np.zeros((n, 0), np.uint8), np.zeros((n, 0, 2), np.uint16))
+    x = host_bf16_normal((k,), 941, n, k, 1)
+    ref = gemv_int4(x, p, sz) if k else np.zeros(n)
+    (b32, y32), (b16, y16) = _outputs(n)
+    pd, szd, xd = _d(p), _d(sz), _d(x)
+    wq.wq_gemv_int4(xd, pd, szd, n, k, group, y32, y16)
+    e = _compare(y32, y16, ref, (n,))
+    _check_guards(b32, b16, n)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")

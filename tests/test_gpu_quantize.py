@@ -99,3 +99,21 @@ def test_quantize_empty_is_noop(wq):
     wq.wq_quantize_int4g32(w, 0, 32, q, s)
     torch.cuda.synchronize()
     assert host(q).tolist() == [7] * 4 and host(s).tolist() == [7] * 4
+
+
+@pytest.mark.parametrize("group,n,k", [(64, 13, 1088), (128, 9, 1024), (256, 7, 2048), (64, 1, 64), (256, 40, 4096)])
+def test_quantize_int4_groups_bitexact(wq, group, n, k):
+    """Groups of 64/128/256 inputs: codes, scales and zeros bit-identical to
+    the oracle, on the same hard cases (ties, neighbours, clamped one-signed
+    groups, subnormal scales) spread over wider groups."""
+    import torch
+    from oracle.quant import quantize_int4
+    say(f"quantize_int4 group={group} n={n} k={k}")
+    w = _int4_special(n, k, 3) if k >= 96 else host_normal((n, k), 0.02, 912, n, k, 0)
+    p_ref, sz_ref = quantize_int4(w, group)
+    rows = w.shape[0]
+    p = empty((rows, k // 2), torch.uint8)
+    sz = empty((rows, k // group, 2), torch.int16)
+    wq.wq_quantize_int4(dev(w), rows, k, group, p, sz)
+    assert np.array_equal(host_u16(sz), sz_ref)
+    assert np.array_equal(host(p), p_ref)

@@ -12,7 +12,7 @@ import pytest
 
 from gpu_util import dev, host, host_u16, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say
 from oracle.bf16 import round_f32_to_bf16
-from oracle.quant import quantize_int8, quantize_int4g32
+from oracle.quant import quantize_int8, quantize_int4
 from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
 from synth.gen import host_normal, host_bf16_normal
 
@@ -30,6 +30,9 @@ SHAPES = {
     ("int4g32", 4): [(45, 4096), (9, 16384), (77, 12352)],
     ("int4g32", 6): [(45, 4096), (9, 16384)],
     ("int4g32", 7): [(45, 4096), (31, 8192), (2, 32)],
+    ("int4g64", 1): [(300, 4096), (37, 11008), (1, 64), (64, 28672)],
+    ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128)],
+    ("int4g256", 1): [(300, 4096), (37, 11008 // 256 * 256), (1, 256), (9, 28672)],
 }
 
 
@@ -48,7 +51,7 @@ def _build(fmt, m, seed):
             ref = gemv_int8(x, q, s)
             W, A = dev(q), dev(s)
         else:
-            p, sz = quantize_int4g32(w)
+            p, sz = quantize_int4(w, int(fmt[5:]))     # "int4g<G>"
             ref = gemm_small_m(x, p, sz) if m > 1 else gemv_int4g32(x, p, sz)
             W, A = dev(p), dev(sz)
         y32 = torch.full((m * n,), -7.0, dtype=torch.float32, device="cuda")
@@ -126,9 +129,19 @@ def test_step_argument_errors():
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
     assert ei.value.status == 2
+    # wider int4 groups: one token row only, k a multiple of the group
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g128", 2, [good], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g128", 1, [(buf, buf, buf, 4, 192, buf, None)], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4g256", 1, [(buf, buf, buf, 4, 28928, buf, None)], ws)
+    assert ei.value.status == 2
 
 
-@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g32", 2), ("int4g32", 5)])
+@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4g32", 2), ("int4g32", 5)])
 def test_step_balance_never_changes_results(fmt, m):
     """Each launch re-cuts the workgroups' ranges from the balance state the
     previous launches measured (XCD speed weights for one token row, the

@@ -275,3 +275,14 @@ def test_group_argument_checks():
         quantize_int4(np.zeros((2, 64), np.float32), 48)
     with pytest.raises(ValueError):
         quantize_int4(np.zeros((2, 96), np.float32), 64)
+
+
+def test_empty_rows_dequantize_to_empty():
+    """K = 0: no groups, an empty [N, 0] matrix, and every output of the
+    matvec is the empty sum 0."""
+    from oracle.quant import dequantize_int4
+    from oracle.matvec import gemv_int4
+    p = np.zeros((7, 0), np.uint8)
+    sz = np.zeros((7, 0, 2), np.uint16)
+    assert dequantize_int4(p, sz).shape == (7, 0)
+    assert np.array_equal(gemv_int4(np.zeros(0, np.uint16), p, sz), np.zeros(7))

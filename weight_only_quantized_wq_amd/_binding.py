@@ -19,18 +19,21 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
 
 _SIGNATURES = {
     "wq_quantize_int8": [_P, _I64, _I64, _P, _P, _P],
     "wq_quantize_int4g32": [_P, _I64, _I64, _P, _P, _P],
+    "wq_quantize_int4": [_P, _I64, _I64, _I32, _P, _P, _P],
     "wq_gemv_bf16": [_P, _P, _I64, _I64, _P, _P, _P],
     "wq_gemv_int8": [_P, _P, _P, _I64, _I64, _P, _P, _P],
     "wq_gemv_int4g32": [_P, _P, _P, _I64, _I64, _P, _P, _P],
+    "wq_gemv_int4": [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P],
     "wq_gemm_smallM": [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P],
     "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
 }
 
-WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3}
+WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3, "int4g64": 4, "int4g128": 5, "int4g256": 6}
 
 
 class wq_matrix(ctypes.Structure):
@@ -145,6 +148,10 @@ def wq_quantize_int4g32(w, n, k, qpacked, sz, stream=None):
     _call("wq_quantize_int4g32", _ptr(w), n, k, _ptr(qpacked), _ptr(sz), _stream(stream))
 
 
+def wq_quantize_int4(w, n, k, group, qpacked, sz, stream=None):
+    _call("wq_quantize_int4", _ptr(w), n, k, group, _ptr(qpacked), _ptr(sz), _stream(stream))
+
+
 def wq_gemv_bf16(x, w, n, k, y_f32=None, y_bf16=None, stream=None):
     _call("wq_gemv_bf16", _ptr(x), _ptr(w), n, k, _ptr(y_f32), _ptr(y_bf16), _stream(stream))
 
@@ -155,6 +162,11 @@ def wq_gemv_int8(x, q, scale, n, k, y_f32=None, y_bf16=None, stream=None):
 
 def wq_gemv_int4g32(x, qpacked, sz, n, k, y_f32=None, y_bf16=None, stream=None):
     _call("wq_gemv_int4g32", _ptr(x), _ptr(qpacked), _ptr(sz), n, k, _ptr(y_f32), _ptr(y_bf16),
+          _stream(stream))
+
+
+def wq_gemv_int4(x, qpacked, sz, n, k, group, y_f32=None, y_bf16=None, stream=None):
+    _call("wq_gemv_int4", _ptr(x), _ptr(qpacked), _ptr(sz), n, k, group, _ptr(y_f32), _ptr(y_bf16),
           _stream(stream))
 
 
@@ -175,7 +187,8 @@ def wq_decode_step_workspace_bytes(count):
 
 def wq_decode_step_prepare(format, m, mats, workspace, workspace_bytes=None):
     """mats: sequence of (x, w, aux, n, k, y_f32, y_bf16) with tensors (or None).
-    `format` is 1/2/3 or "bf16"/"int8"/"int4g32".  Returns the wq_step_plan."""
+    `format` is a WQ_FORMAT code or name ("bf16", "int8", "int4g32", "int4g64",
+    "int4g128", "int4g256").  Returns the wq_step_plan."""
     fmt = WQ_FORMAT.get(format, format)
     arr = (wq_matrix * len(mats))()
     for i, (x, w, aux, n, k, y32, y16) in enumerate(mats):

@@ -46,6 +46,7 @@ struct GemvArgs {
   int32_t split;
   int32_t groups;
   int32_t cpl;            // multi-matrix launches: chunks per lane used (<= CPL)
+  int32_t gshift;         // int4: log2(group / 32): chunk c's (scale, zero) word is sz[row][c >> gshift]
 };
 
 template <class F, int U, int CPL>
@@ -82,9 +83,10 @@ __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg,
 #pragma unroll
     for (int j = 0; j < CPL; ++j) bt.w[u][j] = j < cpl ? buffer_load16_nt(rw, off[j]) : u32x4{0, 0, 0, 0};
     if constexpr (F::kGroupAux) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * a.chunks, row_ok ? (uint32_t)a.chunks * 4u : 0u);
+      const int64_t words = a.chunks >> a.gshift;   // (scale, zero) words per row
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, row_ok ? (uint32_t)words * 4u : 0u);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = j < cpl ? buffer_load4_nt(rs, off[j] >> 2) : 0u;
+      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = j < cpl ? buffer_load4_nt(rs, ((off[j] >> 4) >> a.gshift) << 2) : 0u;
     } else {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;

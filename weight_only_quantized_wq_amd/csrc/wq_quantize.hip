@@ -94,32 +94,25 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
-// int4 G=32: one lane per group of 32 consecutive inputs.
+// int4 with groups of G (32, 64, 128, 256): one lane per group of G
+// consecutive inputs -- a pass over the group for (min, max), then the codes
+// 32 inputs (16 output bytes) at a time.
 
-__global__ __launch_bounds__(256) void quantize_int4g32_kernel(const float* __restrict__ w, int64_t n, int64_t k,
-                                                               uint8_t* __restrict__ qpacked,
-                                                               uint32_t* __restrict__ sz) {
-  const int64_t groups_per_row = k / 32;
+template <int G>
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const float* __restrict__ w, int64_t n, int64_t k,
+                                                            uint8_t* __restrict__ qpacked, uint32_t* __restrict__ sz) {
+  const int64_t groups_per_row = k / G;
   const int64_t total = n * groups_per_row;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t gidx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gidx < total; gidx += stride) {
     const int64_t r = gidx / groups_per_row;
     const int64_t g = gidx - r * groups_per_row;
-    const float4* src = reinterpret_cast<const float4*>(w + r * k + g * 32);
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float4 t = src[i];
-      v[4 * i] = t.x;
-      v[4 * i + 1] = t.y;
-      v[4 * i + 2] = t.z;
-      v[4 * i + 3] = t.w;
-    }
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) {
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
+    const float4* src = reinterpret_cast<const float4*>(w + r * k + g * G);
+    float mn = src[0].x, mx = src[0].x;
+    for (int i = 0; i < G / 4; ++i) {
+      const float4 t = src[i];
+      mn = fminf(fminf(mn, t.x), fminf(t.y, fminf(t.z, t.w)));
+      mx = fmaxf(fmaxf(mx, t.x), fmaxf(t.y, fmaxf(t.z, t.w)));
     }
     const uint16_t zb = f32_to_bf16(mn);
     const float zf = __uint_as_float((uint32_t)zb << 16);
@@ -127,18 +120,29 @@ __global__ __launch_bounds__(256) void quantize_int4g32_kernel(const float* __re
     const uint16_t sb = t > 0.0f ? f32_to_bf16(__fdiv_rn(t, 15.0f)) : (uint16_t)0;
     const double s = (double)__uint_as_float((uint32_t)sb << 16);
     const double z = (double)zf;
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
-    if (s > 0.0) {
+    for (int c32 = 0; c32 < G / 32; ++c32) {
+      float v[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const double wd = (double)v[i];
-        int c = rne_code(wd, z, s, candidate(wd, z, s, -64, 64));
-        c = c < 0 ? 0 : (c > 15 ? 15 : c);
-        words[i >> 3] |= (uint32_t)c << (4 * (i & 7));
+      for (int i = 0; i < 8; ++i) {
+        const float4 t4 = src[8 * c32 + i];
+        v[4 * i] = t4.x;
+        v[4 * i + 1] = t4.y;
+        v[4 * i + 2] = t4.z;
+        v[4 * i + 3] = t4.w;
       }
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+      if (s > 0.0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const double wd = (double)v[i];
+          int c = rne_code(wd, z, s, candidate(wd, z, s, -64, 64));
+          c = c < 0 ? 0 : (c > 15 ? 15 : c);
+          words[i >> 3] |= (uint32_t)c << (4 * (i & 7));
+        }
+      }
+      u32x4 out = {words[0], words[1], words[2], words[3]};
+      *reinterpret_cast<u32x4*>(qpacked + r * (k / 2) + g * (G / 2) + 16 * c32) = out;
     }
-    u32x4 out = {words[0], words[1], words[2], words[3]};
-    *reinterpret_cast<u32x4*>(qpacked + r * (k / 2) + g * 16) = out;
     sz[gidx] = (uint32_t)sb | ((uint32_t)zb << 16);
   }
 }
@@ -164,6 +168,41 @@ extern "C" int wq_quantize_int8(const float* w, int64_t n, int64_t k, int8_t* q,
   return launch_status(name);
 }
 
+template <int G>
+static int launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* qpacked, uint16_t* sz,
+                                hipStream_t stream, const char* name) {
+  static int resident = 0;
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int4_kernel<G>), 256);
+  const int64_t blocks = (n * (k / G) + 255) / 256;
+  const int64_t grid = balanced_grid(blocks, resident);
+  hipLaunchKernelGGL(quantize_int4_kernel<G>, dim3((unsigned)grid), dim3(256), 0, stream, w, n, k, qpacked,
+                     reinterpret_cast<uint32_t*>(sz));
+  return launch_status(name);
+}
+
+extern "C" int wq_quantize_int4(const float* w, int64_t n, int64_t k, int32_t group, uint8_t* qpacked, uint16_t* sz,
+                                void* stream) {
+  const char* name = "wq_quantize_int4";
+  if (!w || !qpacked || !sz) return fail(WQ_ERR_NULL, "%s: w, qpacked and sz must be non-null", name);
+  if (group != 32 && group != 64 && group != 128 && group != 256)
+    return fail(WQ_ERR_SHAPE, "%s: group = %d (need 32, 64, 128 or 256)", name, group);
+  if (n < 0 || k < 0 || k % group)
+    return fail(WQ_ERR_SHAPE, "%s: need n, k >= 0 and k %% %d == 0 (n = %lld, k = %lld)", name, group, (long long)n,
+                (long long)k);
+  if (!aligned16(w) || !aligned16(qpacked) || (reinterpret_cast<uintptr_t>(sz) & 3u))
+    return fail(WQ_ERR_ALIGN, "%s: w and qpacked must be 16-byte and sz 4-byte aligned", name);
+  if (n == 0 || k == 0) return WQ_OK;
+  int rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  switch (group) {
+    case 32: return launch_quantize_int4<32>(w, n, k, qpacked, sz, st, name);
+    case 64: return launch_quantize_int4<64>(w, n, k, qpacked, sz, st, name);
+    case 128: return launch_quantize_int4<128>(w, n, k, qpacked, sz, st, name);
+    default: return launch_quantize_int4<256>(w, n, k, qpacked, sz, st, name);
+  }
+}
+
 extern "C" int wq_quantize_int4g32(const float* w, int64_t n, int64_t k, uint8_t* qpacked, uint16_t* sz,
                                    void* stream) {
   const char* name = "wq_quantize_int4g32";
@@ -175,11 +214,5 @@ extern "C" int wq_quantize_int4g32(const float* w, int64_t n, int64_t k, uint8_t
   if (n == 0 || k == 0) return WQ_OK;
   int rc = check_device();
   if (rc) return rc;
-  static int resident = 0;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int4g32_kernel), 256);
-  int64_t blocks = (n * (k / 32) + 255) / 256;
-  int64_t grid = balanced_grid(blocks, resident);
-  hipLaunchKernelGGL(quantize_int4g32_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, n, k,
-                     qpacked, reinterpret_cast<uint32_t*>(sz));
-  return launch_status(name);
+  return launch_quantize_int4<32>(w, n, k, qpacked, sz, (hipStream_t)stream, name);
 }

@@ -74,6 +74,10 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     v = shared_variant<FmtBf16, 4, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT8 && m == 1) {
     v = shared_variant<FmtInt8, 2, 2, 16, true>();
+  } else if ((format == WQ_FORMAT_INT4G64 || format == WQ_FORMAT_INT4G128 || format == WQ_FORMAT_INT4G256) &&
+             m == 1) {
+    // larger groups: the same kernel, each chunk reading its group's word
+    v = shared_variant<FmtInt4, 2, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
@@ -95,6 +99,11 @@ static bool pick_variant(int format, int m, StepVariant& v) {
 static int weights_per_chunk(int format) {
   return format == WQ_FORMAT_BF16 ? 8 : (format == WQ_FORMAT_INT8 ? 16 : 32);
 }
+
+static bool is_int4(int format) { return format >= WQ_FORMAT_INT4G32 && format <= WQ_FORMAT_INT4G256; }
+
+// int4: log2(group / 32)
+static int int4_gshift(int format) { return is_int4(format) ? format - WQ_FORMAT_INT4G32 : 0; }
 
 static int64_t row_bytes_of(int format, int64_t k) {
   return format == WQ_FORMAT_BF16 ? 2 * k : (format == WQ_FORMAT_INT8 ? k : k / 2);
@@ -160,7 +169,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   if (count < 1) return fail(WQ_ERR_SHAPE, "%s: count = %d must be >= 1", name, count);
   StepVariant v{};
   if (!pick_variant(format, m, v))
-    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16/int8, 1..8 for int4)", name,
+    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int8 and int4 G64/128/256, 1..8 for int4 G32)", name,
                 format, m);
   const int wpc = weights_per_chunk(format);
   std::vector<GemvArgs> desc((size_t)count);
@@ -172,9 +181,10 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_NULL, "%s: matrix %d: x, w (and scales) must be non-null", name, i);
     if (!mt.y_f32 && !mt.y_bf16)
       return fail(WQ_ERR_NULL, "%s: matrix %d: at least one of y_f32 / y_bf16 must be non-null", name, i);
-    if (mt.n < 1 || mt.k < wpc || mt.k % wpc || mt.n > ((int64_t)1 << 31))
+    const int kmult = wpc << int4_gshift(format);   // int4: the group size
+    if (mt.n < 1 || mt.k < kmult || mt.k % kmult || mt.n > ((int64_t)1 << 31))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
-                  name, i, (long long)mt.n, (long long)mt.k, wpc);
+                  name, i, (long long)mt.n, (long long)mt.k, kmult);
     const int64_t chunks = mt.k / wpc;
     const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
@@ -182,14 +192,15 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
-        (format == WQ_FORMAT_INT4G32 && (reinterpret_cast<uintptr_t>(mt.aux) & 3u)))
+        (is_int4(format) && (reinterpret_cast<uintptr_t>(mt.aux) & 3u)))
       return fail(WQ_ERR_ALIGN, "%s: matrix %d: x and w must be 16-byte aligned (sz 4-byte)", name, i);
     GemvArgs& a = desc[(size_t)i];
     a = GemvArgs{};
     a.x = reinterpret_cast<const uint16_t*>(mt.x);
     a.w = reinterpret_cast<const uint8_t*>(mt.w);
     if (format == WQ_FORMAT_INT8) a.scale = reinterpret_cast<const uint16_t*>(mt.aux);
-    if (format == WQ_FORMAT_INT4G32) a.sz = reinterpret_cast<const uint32_t*>(mt.aux);
+    if (is_int4(format)) a.sz = reinterpret_cast<const uint32_t*>(mt.aux);
+    a.gshift = int4_gshift(format);
     a.y32 = mt.y_f32;
     a.y16 = mt.y_bf16;
     a.n = mt.n;
@@ -207,7 +218,8 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
-    const double aux_bytes = format == WQ_FORMAT_INT4G32 ? (double)chunks * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
+    const double aux_bytes =
+        is_int4(format) ? (double)(chunks >> a.gshift) * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
     batch_bytes[(size_t)i] = (double)rows_per_batch * ((double)a.row_bytes + aux_bytes);
     // the shared-activation kernel spends arithmetic on every lane of a pass,
     // including the lanes past a row's end in its last pass: weigh a batch by

@@ -73,9 +73,13 @@ __device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int 
 #pragma unroll
     for (int j = 0; j < CPL; ++j) bt.w[u][j] = buffer_load16_nt(rw, (uint32_t)(((pass * CPL + j) * kWave + lane) * 16));
     if constexpr (F::kGroupAux) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * a.chunks, row_ok ? (uint32_t)a.chunks * 4u : 0u);
+      // chunk c's (scale, zero) word: c >> gshift of the row's words (chunks
+      // past the row, and so past its words, read as zero)
+      const int64_t words = a.chunks >> a.gshift;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, row_ok ? (uint32_t)words * 4u : 0u);
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = buffer_load4_nt(rs, (uint32_t)(((pass * CPL + j) * kWave + lane) * 4));
+      for (int j = 0; j < CPL; ++j)
+        bt.aux[u][j] = buffer_load4_nt(rs, (uint32_t)((((pass * CPL + j) * kWave + lane) >> a.gshift) * 4));
     } else {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;

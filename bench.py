@@ -36,8 +36,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # 20 warmup steps: the step kernels re-cut their workgroups' ranges from
+    # the balance state each launch measures, and the clocks ramp; both
+    # settle within about 20 launches
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama2-7b-int4")
     p.add_argument("--launch", choices=("fused", "per-matrix"), default="fused",
                    help="linear sets: one persistent launch per step (default) or one launch per matrix")

@@ -23,7 +23,8 @@ Readings taken where the pages are silent (the plainest ones):
   |w - q s| <= s/2 holds exactly.  A zero scale gives zero codes.
 * int4: asymmetric, G consecutive inputs of one output row per group (G = 32
   unless stated; the group-size knob also takes 64, 128 and 256, which store
-  0.5 + 4/G bytes per weight).  The zero z = bf16(min) is the value code 0
+  0.5 + 4/G bytes per weight, and its limit G = K, one group per output row:
+  per-channel int4, for K a multiple of 32).  The zero z = bf16(min) is the value code 0
   decodes to; t = fp32(max - z);
   s = bf16(fp32(t / 15)) when t > 0, else s = 0; codes are
   round-half-even((w - z) / s) of the exact real quotient clamped to [0, 15]
@@ -180,14 +181,19 @@ def unpack_int4(packed):
 def quantize_int4(w, group=GROUP, return_clamped=False):
     """W fp32 [N, K] (K % group == 0) -> (packed u8 [N, K/2], sz u16 [N, K/group, 2]).
 
-    With ``return_clamped`` also returns how many codes the [0, 15] clamp
-    changed (never any for groups that span zero; only a group of one sign
-    whose range is tiny next to its magnitude can clamp at code 0).
+    group is one of ``GROUPS`` or K itself (one group per row, K a positive
+    multiple of 32).  With ``return_clamped`` also returns how many codes the
+    [0, 15] clamp changed (never any for groups that span zero; only a group
+    of one sign whose range is tiny next to its magnitude can clamp at code 0).
     """
-    if group not in GROUPS:
-        raise ValueError(f"group must be one of {GROUPS}")
     w = np.asarray(w, np.float32)
-    if w.ndim != 2 or w.shape[1] % group != 0:
+    if w.ndim != 2:
+        raise ValueError("W must be [N, K]")
+    k = w.shape[1]
+    per_row = group == k and k > 0 and k % GROUP == 0
+    if group not in GROUPS and not per_row:
+        raise ValueError(f"group must be one of {GROUPS} or K (a multiple of {GROUP})")
+    if k % group != 0:
         raise ValueError(f"W must be [N, K] with K a multiple of {group}")
     _check_finite(w)
     n, k = w.shape

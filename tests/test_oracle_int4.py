@@ -286,3 +286,62 @@ def test_empty_rows_dequantize_to_empty():
     sz = np.zeros((7, 0, 2), np.uint16)
     assert dequantize_int4(p, sz).shape == (7, 0)
     assert np.array_equal(gemv_int4(np.zeros(0, np.uint16), p, sz), np.zeros(7))
+
+
+# Per-channel int4: the group-size knob at its limit G = K (one group per row).
+
+@pytest.mark.parametrize("k", [96, 288, 32])
+def test_per_channel_brute_force_argmin_over_all_codes(k):
+    rng = np.random.default_rng(300 + k)
+    w = (rng.standard_normal((3, k)) * 0.02).astype(np.float32)
+    packed, sz = quantize_int4(w, k)
+    assert packed.shape == (3, k // 2) and sz.shape == (3, 1, 2)
+    q = unpack_int4(packed)
+    for r in range(3):
+        s_ex, z_ex = _independent_scale_zero(w[r])
+        assert frac_of_bf16(int(sz[r, 0, 0])) == s_ex
+        assert frac_of_bf16(int(sz[r, 0, 1])) == z_ex
+        for c in range(0, k, 5):
+            wv = Fraction(float(w[r, c]))
+            best = min(range(16), key=lambda code: (abs(wv - (z_ex + code * s_ex)), code % 2))
+            assert q[r, c] == best
+
+
+def test_per_channel_one_scale_zero_spans_the_row():
+    """Blocks of 32 with disjoint ranges 0..0.5, 1..1.5, 2..2.5: the row's one
+    (scale, zero) is (bf16(fp32(2.5 / 15)), 0); the first input takes code 0 and
+    the last code 15; every input is within s/2 of its decoded value."""
+    w = np.concatenate([np.linspace(b, b + 0.5, 32, dtype=np.float32) for b in range(3)])[None, :]
+    packed, sz, clamped = quantize_int4(w, 96, return_clamped=True)
+    assert clamped == 0 and sz.shape == (1, 1, 2)
+    assert frac_of_bf16(int(sz[0, 0, 0])) == round_to_bf16(round_to_f32(Fraction(5, 2) / 15))
+    assert sz[0, 0, 1] == 0
+    q = unpack_int4(packed)
+    assert q[0, 0] == 0 and q[0, -1] == 15
+    deq = dequantize_int4(packed, sz)
+    assert np.all(np.abs(w.astype(np.float64) - deq) <= bf16_to_f64(sz[0, 0, 0]) / 2)
+
+
+def test_per_channel_matvec_exact_rational():
+    rng = np.random.default_rng(400)
+    n, k = 4, 160
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    packed, sz = quantize_int4(w, k)
+    x = (rng.standard_normal(k).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    y = gemv_int4(x, packed, sz)
+    q = unpack_int4(packed)
+    xf = [frac_of_bf16(int(v)) for v in x]
+    for r in range(n):
+        s = frac_of_bf16(int(sz[r, 0, 0]))
+        z = frac_of_bf16(int(sz[r, 0, 1]))
+        total = s * sum((int(q[r, c]) * xf[c] for c in range(k)), Fraction(0)) + z * sum(xf, Fraction(0))
+        assert abs(Fraction(float(y[r])) - total) <= abs(total) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 30)
+
+
+def test_per_channel_argument_checks():
+    with pytest.raises(ValueError):
+        quantize_int4(np.zeros((2, 48), np.float32), 48)      # K not a multiple of 32
+    with pytest.raises(ValueError):
+        quantize_int4(np.zeros((2, 192), np.float32), 96)     # neither a listed size nor K
+    with pytest.raises(ValueError):
+        quantize_int4(np.zeros((2, 0), np.float32), 0)

@@ -25,7 +25,8 @@ Readings taken where the pages are silent (the plainest ones):
   unless stated; the group-size knob also takes 64, 128 and 256, which store
   0.5 + 4/G bytes per weight, and its limit G = K, one group per output row:
   per-channel int4, for K a multiple of 32).  The zero z = bf16(min) is the value code 0
-  decodes to; t = fp32(max - z);
+  decodes to (a minimum of zero is taken as +0: the minimum of a group holding
+  both +0 and -0 is otherwise a matter of comparison order); t = fp32(max - z);
   s = bf16(fp32(t / 15)) when t > 0, else s = 0; codes are
   round-half-even((w - z) / s) of the exact real quotient clamped to [0, 15]
   (all zero when s == 0); w ~ z + q s.
@@ -133,11 +134,12 @@ def int4_scale_zero(w, group=GROUP):
     """Per-group (s, z) bf16 bit patterns, each [N, K/group].
 
     z = bf16(min), t = fp32(max - z), s = bf16(fp32(t / 15)) if t > 0 else 0.
+    A zero minimum is +0 (adding +0 maps -0 to +0 and changes nothing else).
     """
     w = np.asarray(w, np.float32)
     n, k = w.shape
     g = w.reshape(n, k // group, group)
-    mn = g.min(axis=2)
+    mn = (g.min(axis=2) + np.float32(0.0)).astype(np.float32)
     mx = g.max(axis=2)
     z = round_f32_to_bf16(mn)
     t = (mx - bf16_to_f32(z)).astype(np.float32)          # IEEE fp32 subtraction

@@ -345,3 +345,24 @@ def test_per_channel_argument_checks():
         quantize_int4(np.zeros((2, 192), np.float32), 96)     # neither a listed size nor K
     with pytest.raises(ValueError):
         quantize_int4(np.zeros((2, 0), np.float32), 0)
+
+
+@pytest.mark.parametrize("group", [32, 64, 96])
+def test_zero_minimum_is_positive_zero(group):
+    """A group whose minimum is zero stores z = +0 (bits 0x0000) whether the
+    zeros are +0, -0 or both, in any order; codes and scale are unchanged by
+    the sign of a zero."""
+    base = np.linspace(0.0, 1.0, group, dtype=np.float32)
+    rows = []
+    for pattern in ([0.0], [-0.0], [0.0, -0.0], [-0.0, 0.0]):
+        r = base.copy()
+        r[:len(pattern)] = np.array(pattern, np.float32)
+        rows.append(r[::-1].copy())
+        rows.append(r)
+    w = np.stack(rows)
+    packed, sz = quantize_int4(w, group)
+    assert np.all(sz[:, 0, 1] == 0)
+    assert np.all(sz[:, 0, 0] == sz[0, 0, 0])
+    q = unpack_int4(packed)
+    for i in range(0, len(rows), 2):
+        assert np.array_equal(q[i], q[1][::-1]) and np.array_equal(q[i + 1], q[1])

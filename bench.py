@@ -252,8 +252,8 @@ def cpu_baseline(wl_name, target_s):
         for mat in mats:
             w = host_normal((mat.n, mat.k), wl.sigma, 78, mat.mid)
             x = host_bf16_normal((wl.m, mat.k) if wl.m > 1 else (mat.k,), 78, mat.mid, 1)
-            if int4_group(wl.fmt):
-                p, sz = quantize_int4(w, int4_group(wl.fmt))
+            if int4_group(wl.fmt, mat.k):
+                p, sz = quantize_int4(w, int4_group(wl.fmt, mat.k))
                 fn = (lambda x=x, p=p, sz=sz: gemm_small_m(x, p, sz)) if wl.m > 1 else \
                      (lambda x=x, p=p, sz=sz: gemv_int4(x, p, sz))
             elif wl.fmt == "int8":

@@ -98,7 +98,8 @@ int wq_quantize_int4g32(const float* w, int64_t n, int64_t k, uint8_t* qpacked, 
  * int4 with a chosen group size -- [README] "Int4 仅权重量化" (the int4
  * quantizer takes a group size; the benchmark rows show 32);
  * [TAGS] "Grouped Quantization".  As wq_quantize_int4g32 with groups of
- * `group` consecutive inputs, group one of 32, 64, 128, 256:
+ * `group` consecutive inputs, group one of 32, 64, 128, 256, or group == k
+ * (one group per output row, "per-channel"; k a positive multiple of 32):
  *   sz bf16 [n][k/group][2]; 0.5 + 4/group bytes per weight.
  * k % group == 0.  Errors: WQ_ERR_SHAPE for another group size.
  */
@@ -135,9 +136,11 @@ int wq_gemv_int4g32(const uint16_t* x, const uint8_t* qpacked, const uint16_t* s
                     int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
 
 /*
- * int4 with groups of `group` inputs (32, 64, 128 or 256), qpacked and sz as
- * written by wq_quantize_int4 with that group; the same sum over groups of
- * `group`.  k % group == 0, k <= 131072.  group == 32 is wq_gemv_int4g32.
+ * int4 with groups of `group` inputs (32, 64, 128, 256, or k: one group per
+ * row), qpacked and sz as written by wq_quantize_int4 with that group; the
+ * same sum over groups of `group`.  k % group == 0 (k % 32 == 0 for a
+ * per-row group), k <= 131072.  group == 32 is wq_gemv_int4g32.
+ * Errors: WQ_ERR_SHAPE for another group size.
  */
 int wq_gemv_int4(const uint16_t* x, const uint8_t* qpacked, const uint16_t* sz, int64_t n, int64_t k,
                  int32_t group, float* y_f32, uint16_t* y_bf16, void* stream);
@@ -190,13 +193,17 @@ enum {
   /* int4 with larger groups (wq_quantize_int4); one token row per step */
   WQ_FORMAT_INT4G64 = 4,
   WQ_FORMAT_INT4G128 = 5,
-  WQ_FORMAT_INT4G256 = 6
+  WQ_FORMAT_INT4G256 = 6,
+  /* int4 with one group per row (wq_quantize_int4 with group == k): each
+     matrix's sz is [n][1][2]; k % 32 == 0; one token row per step */
+  WQ_FORMAT_INT4PC = 7
 };
 
 /* One linear layer of a step, in the layout of the single-matrix calls:
  *   x    bf16 [m][k]   (16-byte aligned)
  *   w    bf16 [n][k] | int8 [n][k] | int4 packed [n][k/2]   (16-byte aligned)
- *   aux  NULL (bf16) | bf16 scale [n] (int8) | sz [n][k/G][2] (int4 with groups of G, 4-byte aligned)
+ *   aux  NULL (bf16) | bf16 scale [n] (int8) | sz [n][k/G][2] (int4 with groups of G, G = k per row;
+ *        4-byte aligned)
  *   y_f32 / y_bf16  [m][n], either may be NULL but not both. */
 typedef struct {
   const void* x;
@@ -223,14 +230,14 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
 
 /*
  * Plans `count` independent matvecs of one format (m token rows each: m = 1
- * for bf16, int8 and int4 with groups of 64/128/256, 1 <= m <= 8 for int4
- * G=32) as ONE persistent launch: every
+ * for bf16, int8, int4 with groups of 64/128/256 and int4 with one group
+ * per row, 1 <= m <= 8 for int4 G=32) as ONE persistent launch: every
  * workgroup streams an equal share of the step's weight bytes as a contiguous
  * range of row batches across the matrices, so no matrix pays its own
  * launch, ramp-up and drain.  Results equal the single-matrix calls' to fp32
  * rounding (the per-row reduction order may differ).
  * Validates every matrix on the host (null -> sizes -> alignment; k must be a
- * positive multiple of 8 / 16 / G per format and within the kernel's row
+ * positive multiple of 8 / 16 / G per format (32 for a per-row group) and within the kernel's row
  * limit: with one token row the activations are staged whole in LDS, so
  * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with 2..8 token rows
  * k <= 131072), then writes the launch description into `workspace` (device

@@ -8,6 +8,7 @@ N(0, 1) bf16 activations standing in for trained checkpoints:
                    a step sweeps 64 resident copies of it
   llama2-7b-int4   Llama-2-7B linear set, int4 G=32          (129 matvecs)
   llama2-7b-int4g128  the same weights, int4 with groups of 128 inputs
+  llama2-7b-int4pc    the same weights, int4 with one group per output row
   llama2-7b-bf16 / llama2-7b-int8 / llama3.1-8b-bf16 / llama3.1-8b-int8
   llama3.1-70b-int4-m5  Llama-3.1-70B set, int4 G=32, 5 tokens per pass,
                         W N(0, 0.015)                       (321 matmuls)
@@ -50,6 +51,7 @@ WORKLOADS = {w.name: w for w in [
     Workload("int8-4096", 1, "int8", 1, 0.02, None, "single int8 GEMV 4096x4096, seed 0"),
     Workload("llama2-7b-int4", 2, "int4g32", 1, 0.02, LLAMA2_7B),
     Workload("llama2-7b-int4g128", 2, "int4g128", 1, 0.02, LLAMA2_7B),
+    Workload("llama2-7b-int4pc", 2, "int4pc", 1, 0.02, LLAMA2_7B),
     Workload("llama2-7b-bf16", 3, "bf16", 1, 0.02, LLAMA2_7B),
     Workload("llama2-7b-int8", 3, "int8", 1, 0.02, LLAMA2_7B),
     Workload("llama3.1-8b-bf16", 6, "bf16", 1, 0.02, LLAMA31_8B),

@@ -95,6 +95,20 @@ def test_group_size_errors(wq):
     assert _rc("wq_gemv_int4", BAD, 0x2000, 0x2000, 0, 256, 128, 0x2000, None, None) == 3
 
 
+
+def test_per_row_group_errors(wq):
+    # one group per row: group == k, k a positive multiple of 32
+    assert _rc("wq_quantize_int4", BAD, 4, 48, 48, BAD, BAD, None) == 2
+    assert _rc("wq_quantize_int4", BAD, 4, 0, 0, BAD, BAD, None) == 2
+    assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 80, 80, BAD, None, None) == 2
+    assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 0, 0, BAD, None, None) == 2
+    assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 64, 0, BAD, None, None) == 2
+    assert "group" in wq.last_error()
+    # a valid per-row group passes the size checks and reaches alignment
+    assert _rc("wq_quantize_int4", BAD, 0, 96, 96, 0x2000, 0x2000, None) == 3
+    assert _rc("wq_gemv_int4", BAD, 0x2000, 0x2000, 0, 96, 96, 0x2000, None, None) == 3
+
+
 def test_alignment_errors_before_any_launch(wq):
     # n = 0: even a missing alignment check would return without launching
     assert _rc("wq_gemv_int4g32", BAD, 0x2000, 0x2000, 0, 64, 0x2000, None, None) == 3
@@ -146,7 +160,7 @@ def test_step_plan_errors_before_any_device_work(wq):
     assert lib.wq_decode_step_prepare(3, 1, one, 1, BAD, 1 << 20, ctypes.byref(plan)) == 3
     # run rejects a plan it did not produce
     assert lib.wq_decode_step_run(None, None) == 1
-    junk = wq_step_plan(7, 1, 1, 1, 1, BAD)
+    junk = wq_step_plan(99, 1, 1, 1, 1, BAD)
     assert lib.wq_decode_step_run(ctypes.byref(junk), None) == 2
     assert wq.wq_decode_step_workspace_bytes(129) > 129 * 64
 

@@ -208,3 +208,21 @@ def test_gemv_int4_groups(wq, group, n, k):
     e = _compare(y32, y16, ref, (n,))
     _check_guards(b32, b16, n)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+@pytest.mark.parametrize("n,k", [(37, 32), (300, 4096), (40, 11008), (17, 28672), (2, 131072), (7, 96)])
+def test_gemv_int4_per_row(wq, n, k):
+    """One group per row: every chunk, the padding past the row included,
+    reads the row's single (scale, zero) word."""
+    from oracle.quant import quantize_int4
+    from oracle.matvec import gemv_int4
+    say(f"gemv_int4 per-row n={n} k={k}")
+    w = host_normal((n, k), 0.02, 942, n, k, 0)
+    p, sz = quantize_int4(w, k)
+    x = host_bf16_normal((k,), 942, n, k, 1)
+    ref = gemv_int4(x, p, sz)
+    (b32, y32), (b16, y16) = _outputs(n)
+    wq.wq_gemv_int4(_d(x), _d(p), _d(sz), n, k, k, y32, y16)
+    e = _compare(y32, y16, ref, (n,))
+    _check_guards(b32, b16, n)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")

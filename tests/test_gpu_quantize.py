@@ -117,3 +117,47 @@ def test_quantize_int4_groups_bitexact(wq, group, n, k):
     wq.wq_quantize_int4(dev(w), rows, k, group, p, sz)
     assert np.array_equal(host_u16(sz), sz_ref)
     assert np.array_equal(host(p), p_ref)
+
+
+@pytest.mark.parametrize("n,k", [(13, 1056), (3, 32), (40, 4096), (5, 11008), (2, 28672)])
+def test_quantize_int4_per_row_bitexact(wq, n, k):
+    """One group per row (group == k): the wave-reduced min/max, scale, zero
+    and every code bit-identical to the oracle, hard rows included."""
+    import torch
+    from oracle.quant import quantize_int4
+    say(f"quantize_int4 per-row n={n} k={k}")
+    w = _int4_special(n, k, 4) if k >= 96 else host_normal((n, k), 0.02, 913, n, k, 0)
+    p_ref, sz_ref = quantize_int4(w, k)
+    rows = w.shape[0]
+    p = empty((rows, k // 2), torch.uint8)
+    sz = empty((rows, 1, 2), torch.int16)
+    wq.wq_quantize_int4(dev(w), rows, k, k, p, sz)
+    assert np.array_equal(host_u16(sz), sz_ref)
+    assert np.array_equal(host(p), p_ref)
+
+
+@pytest.mark.parametrize("group", [32, 128, "row"])
+def test_quantize_int4_zero_minimum_is_positive_zero(wq, group):
+    """Groups whose minimum is zero, written as +0, -0 or both in either
+    order, store z = +0 like the oracle."""
+    import torch
+    from oracle.quant import quantize_int4
+    k = 256
+    g = k if group == "row" else group
+    say(f"quantize_int4 signed zeros group={group}")
+    base = np.linspace(0.0, 1.0, k, dtype=np.float32)
+    rows = []
+    for pattern in ([0.0], [-0.0], [0.0, -0.0], [-0.0, 0.0]):
+        for start in range(0, k, g):
+            r = base.copy()
+            r[start:start + len(pattern)] = np.array(pattern, np.float32)
+            rows.append(r)
+            rows.append(r[::-1].copy())
+    w = np.stack(rows)
+    p_ref, sz_ref = quantize_int4(w, g)
+    assert np.all(sz_ref[..., 1] == 0) or g != k
+    p = empty((w.shape[0], k // 2), torch.uint8)
+    sz = empty((w.shape[0], k // g, 2), torch.int16)
+    wq.wq_quantize_int4(dev(w), w.shape[0], k, g, p, sz)
+    assert np.array_equal(host_u16(sz), sz_ref)
+    assert np.array_equal(host(p), p_ref)

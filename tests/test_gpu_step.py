@@ -33,6 +33,7 @@ SHAPES = {
     ("int4g64", 1): [(300, 4096), (37, 11008), (1, 64), (64, 28672)],
     ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128)],
     ("int4g256", 1): [(300, 4096), (37, 11008 // 256 * 256), (1, 256), (9, 28672)],
+    ("int4pc", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 32), (129, 1056), (3, 28672)],
 }
 
 
@@ -51,7 +52,7 @@ def _build(fmt, m, seed):
             ref = gemv_int8(x, q, s)
             W, A = dev(q), dev(s)
         else:
-            p, sz = quantize_int4(w, int(fmt[5:]))     # "int4g<G>"
+            p, sz = quantize_int4(w, k if fmt == "int4pc" else int(fmt[5:]))     # "int4g<G>" / one group per row
             ref = gemm_small_m(x, p, sz) if m > 1 else gemv_int4g32(x, p, sz)
             W, A = dev(p), dev(sz)
         y32 = torch.full((m * n,), -7.0, dtype=torch.float32, device="cuda")
@@ -139,9 +140,15 @@ def test_step_argument_errors():
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g256", 1, [(buf, buf, buf, 4, 28928, buf, None)], ws)
     assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4pc", 5, [good], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int4pc", 1, [(buf, buf, buf, 4, 80, buf, None)], ws)
+    assert ei.value.status == 2
 
 
-@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4g32", 2), ("int4g32", 5)])
+@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4pc", 1), ("int4g32", 2), ("int4g32", 5)])
 def test_step_balance_never_changes_results(fmt, m):
     """Each launch re-cuts the workgroups' ranges from the balance state the
     previous launches measured (XCD speed weights for one token row, the

@@ -33,7 +33,7 @@ _SIGNATURES = {
     "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
 }
 
-WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3, "int4g64": 4, "int4g128": 5, "int4g256": 6}
+WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3, "int4g64": 4, "int4g128": 5, "int4g256": 6, "int4pc": 7}
 
 
 class wq_matrix(ctypes.Structure):
@@ -188,7 +188,8 @@ def wq_decode_step_workspace_bytes(count):
 def wq_decode_step_prepare(format, m, mats, workspace, workspace_bytes=None):
     """mats: sequence of (x, w, aux, n, k, y_f32, y_bf16) with tensors (or None).
     `format` is a WQ_FORMAT code or name ("bf16", "int8", "int4g32", "int4g64",
-    "int4g128", "int4g256").  Returns the wq_step_plan."""
+    "int4g128", "int4g256", "int4pc": one group per row).  Returns the
+    wq_step_plan."""
     fmt = WQ_FORMAT.get(format, format)
     arr = (wq_matrix * len(mats))()
     for i, (x, w, aux, n, k, y32, y16) in enumerate(mats):

@@ -113,21 +113,23 @@ int run_gemv(GemvArgs a, hipStream_t stream, const char* name) {
 // Host checks in a fixed order -- null pointers, then sizes, then alignment --
 // so a call is rejected for the first problem in that order.  `aux` is the
 // scale (int8) or scale/zero (int4) array, checked when `need_aux`.
-// log2(group / 32) for the supported int4 group sizes, -1 otherwise
-static int int4_group_shift(int64_t group) {
+// log2(group / 32) for the int4 group sizes 32..256; kPerRowShift for one
+// group per row (group == k, k a positive multiple of 32, checked by the
+// caller); -1 otherwise
+static int int4_group_shift(int64_t group, int64_t k) {
   switch (group) {
     case 32: return 0;
     case 64: return 1;
     case 128: return 2;
     case 256: return 3;
-    default: return -1;
+    default: return (group == k && k > 0) ? kPerRowShift : -1;
   }
 }
 
-// `group` > 0 (int4): the group size, checked with the sizes.
+// `group` >= 0 (int4): the group size, checked with the sizes; -1: no groups.
 static int check_common(const char* name, const void* x, const void* w, const void* aux, bool need_aux, int64_t n,
                         int64_t k, const float* y32, const uint16_t* y16, int kmult, int64_t m = 1,
-                        int64_t group = 0) {
+                        int64_t group = -1) {
   if (!x || !w) return fail(WQ_ERR_NULL, "%s: x and the weights must be non-null", name);
   if (need_aux && !aux) return fail(WQ_ERR_NULL, "%s: the scale array must be non-null", name);
   if (!y32 && !y16) return fail(WQ_ERR_NULL, "%s: at least one of y_f32 / y_bf16 must be non-null", name);
@@ -136,8 +138,9 @@ static int check_common(const char* name, const void* x, const void* w, const vo
   if (m < 1 || m > 8) return fail(WQ_ERR_SHAPE, "%s: m = %lld outside [1, 8]", name, (long long)m);
   if (n > ((int64_t)1 << 31)) return fail(WQ_ERR_SHAPE, "%s: n = %lld too large", name, (long long)n);
   if (k > ((int64_t)1 << 24)) return fail(WQ_ERR_SHAPE, "%s: k = %lld too large", name, (long long)k);
-  if (group > 0 && int4_group_shift(group) < 0)
-    return fail(WQ_ERR_SHAPE, "%s: group = %lld (need 32, 64, 128 or 256)", name, (long long)group);
+  if (group >= 0 && int4_group_shift(group, k) < 0)
+    return fail(WQ_ERR_SHAPE, "%s: group = %lld (need 32, 64, 128, 256 or k = %lld)", name, (long long)group,
+                (long long)k);
   if (group > 0 && k % group)
     return fail(WQ_ERR_SHAPE, "%s: k = %lld is not a multiple of group %lld", name, (long long)k, (long long)group);
   if (!aligned16(x) || !aligned16(w)) return fail(WQ_ERR_ALIGN, "%s: x and weights must be 16-byte aligned", name);
@@ -189,7 +192,7 @@ static int int4_args(const char* name, const uint16_t* x, const uint8_t* qpacked
                      int64_t k, float* y_f32, uint16_t* y_bf16, GemvArgs& a, int64_t m = 1, int64_t group = 32) {
   int rc = check_common(name, x, qpacked, sz, true, n, k, y_f32, y_bf16, 32, m, group);
   if (rc) return rc;
-  const int gshift = int4_group_shift(group);
+  const int gshift = int4_group_shift(group, k);
   if ((reinterpret_cast<uintptr_t>(sz) & 3u) != 0) return fail(WQ_ERR_ALIGN, "%s: sz must be 4-byte aligned", name);
   a = GemvArgs{};
   a.x = x;

@@ -49,6 +49,16 @@ struct GemvArgs {
   int32_t gshift;         // int4: log2(group / 32): chunk c's (scale, zero) word is sz[row][c >> gshift]
 };
 
+// int4 with one group per row (per-channel): a shift past any row's chunk
+// count maps every chunk to the row's single (scale, zero) word.
+constexpr int kPerRowShift = 30;
+
+// (scale, zero) words of an int4 row: chunks / 2^gshift, rounded up (one
+// word for a per-row group).
+__host__ __device__ inline int64_t int4_row_words(int64_t chunks, int gshift) {
+  return (chunks + ((int64_t)1 << gshift) - 1) >> gshift;
+}
+
 template <class F, int U, int CPL>
 struct Batch {
   u32x4 w[U][CPL];
@@ -83,7 +93,7 @@ __device__ __forceinline__ void load_batch(const GemvArgs& a, int64_t b, int rg,
 #pragma unroll
     for (int j = 0; j < CPL; ++j) bt.w[u][j] = j < cpl ? buffer_load16_nt(rw, off[j]) : u32x4{0, 0, 0, 0};
     if constexpr (F::kGroupAux) {
-      const int64_t words = a.chunks >> a.gshift;   // (scale, zero) words per row
+      const int64_t words = int4_row_words(a.chunks, a.gshift);
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, row_ok ? (uint32_t)words * 4u : 0u);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) bt.aux[u][j] = j < cpl ? buffer_load4_nt(rs, ((off[j] >> 4) >> a.gshift) << 2) : 0u;

@@ -74,9 +74,11 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     v = shared_variant<FmtBf16, 4, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT8 && m == 1) {
     v = shared_variant<FmtInt8, 2, 2, 16, true>();
-  } else if ((format == WQ_FORMAT_INT4G64 || format == WQ_FORMAT_INT4G128 || format == WQ_FORMAT_INT4G256) &&
+  } else if ((format == WQ_FORMAT_INT4G64 || format == WQ_FORMAT_INT4G128 || format == WQ_FORMAT_INT4G256 ||
+              format == WQ_FORMAT_INT4PC) &&
              m == 1) {
-    // larger groups: the same kernel, each chunk reading its group's word
+    // larger groups (up to one per row): the same kernel, each chunk reading
+    // its group's word
     v = shared_variant<FmtInt4, 2, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT4G32) {
     switch (m) {
@@ -100,10 +102,15 @@ static int weights_per_chunk(int format) {
   return format == WQ_FORMAT_BF16 ? 8 : (format == WQ_FORMAT_INT8 ? 16 : 32);
 }
 
-static bool is_int4(int format) { return format >= WQ_FORMAT_INT4G32 && format <= WQ_FORMAT_INT4G256; }
+static bool is_int4(int format) {
+  return (format >= WQ_FORMAT_INT4G32 && format <= WQ_FORMAT_INT4G256) || format == WQ_FORMAT_INT4PC;
+}
 
-// int4: log2(group / 32)
-static int int4_gshift(int format) { return is_int4(format) ? format - WQ_FORMAT_INT4G32 : 0; }
+// int4: log2(group / 32), or kPerRowShift for one group per row
+static int int4_gshift(int format) {
+  if (format == WQ_FORMAT_INT4PC) return kPerRowShift;
+  return is_int4(format) ? format - WQ_FORMAT_INT4G32 : 0;
+}
 
 static int64_t row_bytes_of(int format, int64_t k) {
   return format == WQ_FORMAT_BF16 ? 2 * k : (format == WQ_FORMAT_INT8 ? k : k / 2);
@@ -169,7 +176,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   if (count < 1) return fail(WQ_ERR_SHAPE, "%s: count = %d must be >= 1", name, count);
   StepVariant v{};
   if (!pick_variant(format, m, v))
-    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int8 and int4 G64/128/256, 1..8 for int4 G32)", name,
+    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int8, int4 G64/128/256 and per-row int4, 1..8 for int4 G32)", name,
                 format, m);
   const int wpc = weights_per_chunk(format);
   std::vector<GemvArgs> desc((size_t)count);
@@ -181,7 +188,8 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_NULL, "%s: matrix %d: x, w (and scales) must be non-null", name, i);
     if (!mt.y_f32 && !mt.y_bf16)
       return fail(WQ_ERR_NULL, "%s: matrix %d: at least one of y_f32 / y_bf16 must be non-null", name, i);
-    const int kmult = wpc << int4_gshift(format);   // int4: the group size
+    // int4 with groups of G: k a multiple of G; one group per row: of 32
+    const int kmult = format == WQ_FORMAT_INT4PC ? wpc : wpc << int4_gshift(format);
     if (mt.n < 1 || mt.k < kmult || mt.k % kmult || mt.n > ((int64_t)1 << 31))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
                   name, i, (long long)mt.n, (long long)mt.k, kmult);
@@ -219,7 +227,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.batch_begin = total_batches;
     total_batches += a.batches;
     const double aux_bytes =
-        is_int4(format) ? (double)(chunks >> a.gshift) * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
+        is_int4(format) ? (double)int4_row_words(chunks, a.gshift) * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
     batch_bytes[(size_t)i] = (double)rows_per_batch * ((double)a.row_bytes + aux_bytes);
     // the shared-activation kernel spends arithmetic on every lane of a pass,
     // including the lanes past a row's end in its last pass: weigh a batch by

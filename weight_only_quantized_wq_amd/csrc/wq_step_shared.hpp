@@ -73,9 +73,11 @@ __device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int 
 #pragma unroll
     for (int j = 0; j < CPL; ++j) bt.w[u][j] = buffer_load16_nt(rw, (uint32_t)(((pass * CPL + j) * kWave + lane) * 16));
     if constexpr (F::kGroupAux) {
-      // chunk c's (scale, zero) word: c >> gshift of the row's words (chunks
-      // past the row, and so past its words, read as zero)
-      const int64_t words = a.chunks >> a.gshift;
+      // chunk c's (scale, zero) word: c >> gshift of the row's words.  A
+      // chunk past the row reads zero codes against zero activations, so it
+      // adds nothing whichever word it reads (zero past the words, or a
+      // per-row group's one word).
+      const int64_t words = int4_row_words(a.chunks, a.gshift);
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, row_ok ? (uint32_t)words * 4u : 0u);
 #pragma unroll
       for (int j = 0; j < CPL; ++j)

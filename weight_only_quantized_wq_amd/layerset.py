@@ -21,11 +21,14 @@ import torch
 
 from . import _binding as wq
 
-FORMATS = ("bf16", "int8", "int4g32", "int4g64", "int4g128", "int4g256")
+FORMATS = ("bf16", "int8", "int4g32", "int4g64", "int4g128", "int4g256", "int4pc")
 
 
-def int4_group(fmt):
-    """Group size of an ``int4g<G>`` format name, else 0."""
+def int4_group(fmt, k):
+    """Group size of an int4 format for rows of k inputs (``int4g<G>``: G;
+    ``int4pc``, one group per row: k); 0 for the other formats."""
+    if fmt == "int4pc":
+        return k
     return int(fmt[5:]) if fmt.startswith("int4g") else 0
 
 
@@ -34,8 +37,8 @@ def weight_bytes(fmt, n, k):
         return 2 * n * k
     if fmt == "int8":
         return n * k + 2 * n
-    if int4_group(fmt):
-        return n * k // 2 + (k // int4_group(fmt)) * 4 * n
+    if int4_group(fmt, k):
+        return n * k // 2 + (k // int4_group(fmt, k)) * 4 * n
     raise ValueError(fmt)
 
 
@@ -56,8 +59,8 @@ class QuantMatrix:
             self.w = torch.empty((n, k), dtype=torch.int8, device=dev)
             self.aux = torch.empty((n,), dtype=torch.int16, device=dev)
             wq.wq_quantize_int8(w32, n, k, self.w, self.aux)
-        elif int4_group(fmt):
-            g = int4_group(fmt)
+        elif int4_group(fmt, k):
+            g = int4_group(fmt, k)
             self.w = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
             self.aux = torch.empty((n, k // g, 2), dtype=torch.int16, device=dev)
             wq.wq_quantize_int4(w32, n, k, g, self.w, self.aux)
@@ -75,7 +78,7 @@ class QuantMatrix:
         elif self.fmt == "int8":
             wq.wq_gemv_int8(self.x, self.w, self.aux, self.n, self.k, y32, y16, stream)
         elif self.m == 1:
-            wq.wq_gemv_int4(self.x, self.w, self.aux, self.n, self.k, int4_group(self.fmt), y32, y16, stream)
+            wq.wq_gemv_int4(self.x, self.w, self.aux, self.n, self.k, int4_group(self.fmt, self.k), y32, y16, stream)
         else:
             wq.wq_gemm_smallM(self.x, self.m, self.w, self.aux, self.n, self.k, y32, y16, stream)
 

@@ -64,3 +64,12 @@ def gemm_small_m(x_bits, packed, sz):
     if x_bits.ndim != 2:
         raise ValueError("x must be [M, K]")
     return gemv_int4g32(x_bits, packed, sz)
+
+
+def gemm_small_m_int8(x_bits, q, s):
+    """Speculative verify through an int8 linear: M token rows x [M, K]
+    against int8 per-row weights -> [M, N], y[m, n] = s[n] sum_k x[m, k] q[n, k]."""
+    x_bits = np.asarray(x_bits)
+    if x_bits.ndim != 2:
+        raise ValueError("x must be [M, K]")
+    return gemv_int8(x_bits, q, s)

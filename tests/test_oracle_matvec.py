@@ -8,11 +8,12 @@ speculative-verify rows.
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 from exact import frac_of_bf16
 from oracle.bf16 import round_f32_to_bf16
 from oracle.quant import quantize_int8, quantize_int4g32, unpack_int4
-from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m, gemv_int8_f64x
+from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m, gemv_int8_f64x, gemm_small_m_int8
 
 
 def _bits(rng, shape):
@@ -106,3 +107,26 @@ def test_empty_k_and_n():
     packed = np.zeros((0, 16), np.uint8)
     sz = np.zeros((0, 1, 2), np.uint16)
     assert gemv_int4g32(np.zeros(32, np.uint16), packed, sz).shape == (0,)
+
+
+def test_int8_small_m_exact_rational_and_rows():
+    """M token rows through an int8 linear: y[m, n] = s[n] sum_k x[m, k] q[n, k]
+    exactly (non-square M, N, K: a swapped index fails), each row equal to
+    the one-token product, and permuted token rows give permuted outputs."""
+    rng = np.random.default_rng(26)
+    m, n, k = 3, 5, 48
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s = quantize_int8(w)
+    x = _bits(rng, (m, k))
+    y = gemm_small_m_int8(x, q, s)
+    assert y.shape == (m, n)
+    for t in range(m):
+        xf = [frac_of_bf16(int(v)) for v in x[t]]
+        for r in range(n):
+            want = frac_of_bf16(int(s[r])) * sum((int(q[r, c]) * xf[c] for c in range(k)), Fraction(0))
+            assert abs(Fraction(float(y[t, r])) - want) <= abs(want) * Fraction(1, 10 ** 14) + Fraction(1, 10 ** 30)
+        assert np.array_equal(y[t], gemv_int8(x[t], q, s))
+    perm = [2, 0, 1]
+    assert np.array_equal(gemm_small_m_int8(x[perm], q, s), y[perm])
+    with pytest.raises(ValueError):
+        gemm_small_m_int8(x[0], q, s)

@@ -158,6 +158,18 @@ int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const u
                    int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
 
 /*
+ * Speculative-decoding verify through an int8 linear -- [GUIDE] "Key
+ * Features", [README] "推测采样" (the verify pass), with the int8 weights of
+ * [README] "Int8 仅权重量化".  x bf16 [m][k], 1 <= m <= 8; q, scale as written
+ * by wq_quantize_int8; y [m][n] with y[t][r] = scale[r] * sum_k x[t][k] q[r][k];
+ * row t of y equals wq_gemv_int8 applied to row t of x (to fp32 rounding).
+ * Each weight is read once (m >= 2: on the matrix cores).  k % 16 == 0,
+ * k <= 2^24, n * k <= 0xFFFFFF00.  scale 2-byte aligned.
+ */
+int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q, const uint16_t* scale, int64_t n,
+                        int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
+
+/*
  * Top-2 mixture-of-experts decode step for one token, int8 per-row experts
  * -- [README] "Mixtral 8x7B" (sparse MoE, int8 on one GPU).
  *   x       bf16 [dim]
@@ -230,8 +242,8 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
 
 /*
  * Plans `count` independent matvecs of one format (m token rows each: m = 1
- * for bf16, int8, int4 with groups of 64/128/256 and int4 with one group
- * per row, 1 <= m <= 8 for int4 G=32) as ONE persistent launch: every
+ * for bf16, int4 with groups of 64/128/256 and int4 with one group per row,
+ * 1 <= m <= 8 for int8 and int4 G=32) as ONE persistent launch: every
  * workgroup streams an equal share of the step's weight bytes as a contiguous
  * range of row batches across the matrices, so no matrix pays its own
  * launch, ramp-up and drain.  Results equal the single-matrix calls' to fp32
@@ -240,7 +252,8 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
  * positive multiple of 8 / 16 / G per format (32 for a per-row group) and within the kernel's row
  * limit: with one token row the activations are staged whole in LDS, so
  * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with 2..8 token rows
- * k <= 131072), then writes the launch description into `workspace` (device
+ * k <= 131072; int8 with 2..8 token rows k <= 2^24 and n * k <= 0xFFFFFF00),
+ * then writes the launch description into `workspace` (device
  * memory, 16-byte aligned, `workspace_bytes` long, caller-owned; it must
  * stay allocated and unmodified while the plan is used).  This copy is
  * synchronous: prepare once, outside any graph capture.  The matrices'

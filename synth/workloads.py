@@ -12,6 +12,7 @@ N(0, 1) bf16 activations standing in for trained checkpoints:
   llama2-7b-bf16 / llama2-7b-int8 / llama3.1-8b-bf16 / llama3.1-8b-int8
   llama3.1-70b-int4-m5  Llama-3.1-70B set, int4 G=32, 5 tokens per pass,
                         W N(0, 0.015)                       (321 matmuls)
+  llama3.1-70b-int8-m5  the same weights in int8, 5 tokens per pass
   mixtral-int8     Mixtral-8x7B MoE, 32 layers x 8 int8 experts, top-2
 
 Generators are keyed by (workload id, layer, matrix id, role) so every
@@ -57,6 +58,7 @@ WORKLOADS = {w.name: w for w in [
     Workload("llama3.1-8b-bf16", 6, "bf16", 1, 0.02, LLAMA31_8B),
     Workload("llama3.1-8b-int8", 6, "int8", 1, 0.02, LLAMA31_8B),
     Workload("llama3.1-70b-int4-m5", 4, "int4g32", 5, 0.015, LLAMA31_70B),
+    Workload("llama3.1-70b-int8-m5", 4, "int8", 5, 0.015, LLAMA31_70B),
     Workload("mixtral-int8", 5, "int8", 1, 0.02, MIXTRAL_8X7B),
 ]}
 

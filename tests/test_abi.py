@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_quantize_int4", "wq_gemv_bf16", "wq_gemv_int8",
                  "wq_gemv_int4g32", "wq_gemv_int4",
-                 "wq_gemm_smallM", "moe_top2_gemv", "wq_status_string", "wq_last_error",
+                 "wq_gemm_smallM", "wq_gemm_smallM_int8", "moe_top2_gemv", "wq_status_string", "wq_last_error",
                  "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
                  "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run"]:
         assert want in names
@@ -75,6 +75,14 @@ def test_shape_errors(wq):
     assert _rc("wq_gemv_bf16", BAD, BAD, -1, 16, BAD, None, None) == 2             # n < 0
     assert _rc("wq_gemm_smallM", BAD, 0, BAD, BAD, 4, 64, BAD, None, None) == 2    # m = 0
     assert _rc("wq_gemm_smallM", BAD, 9, BAD, BAD, 4, 64, BAD, None, None) == 2    # m = 9
+    assert _rc("wq_gemm_smallM_int8", None, 2, BAD, BAD, 4, 64, BAD, None, None) == 1
+    assert _rc("wq_gemm_smallM_int8", BAD, 2, BAD, None, 4, 64, BAD, None, None) == 1   # scale
+    assert _rc("wq_gemm_smallM_int8", BAD, 9, BAD, BAD, 4, 64, BAD, None, None) == 2
+    assert _rc("wq_gemm_smallM_int8", BAD, 5, BAD, BAD, 4, 40, BAD, None, None) == 2    # k % 16
+    assert _rc("wq_gemm_smallM_int8", BAD, 5, BAD, BAD, 1 << 20, 1 << 13, BAD, None, None) == 2   # n k > 2^32 - 256
+    assert "weight bytes" in wq.last_error()
+    assert _rc("wq_gemm_smallM_int8", 0x2000, 5, 0x2000, 0x2001, 0, 64, 0x2000, None, None) == 3   # scale alignment
+    assert "scale" in wq.last_error()
     assert _rc("wq_quantize_int4g32", BAD, 4, 40, BAD, BAD, None) == 2
     assert _rc("wq_quantize_int8", BAD, 4, 6, BAD, BAD, None) == 2
     assert _rc("moe_top2_gemv", BAD, BAD, 4, BAD, BAD, BAD, BAD, 64, 64, BAD, BAD, None, None, None, None) == 2
@@ -150,7 +158,8 @@ def test_step_plan_errors_before_any_device_work(wq):
     assert lib.wq_decode_step_prepare(3, 1, no_aux, 1, BAD, 1 << 20, ctypes.byref(plan)) == 1
     # unsupported format / m / sizes
     assert lib.wq_decode_step_prepare(9, 1, one, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
-    assert lib.wq_decode_step_prepare(2, 5, one, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2
+    assert lib.wq_decode_step_prepare(1, 5, one, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2   # bf16: one token row
+    assert lib.wq_decode_step_prepare(2, 9, one, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2   # int8: up to 8
     assert lib.wq_decode_step_prepare(3, 1, one, 0, BAD, 1 << 20, ctypes.byref(plan)) == 2
     bad_k = (wq_matrix * 1)(wq_matrix(BAD, BAD, BAD, 4, 48, BAD, None))
     assert lib.wq_decode_step_prepare(3, 1, bad_k, 1, BAD, 1 << 20, ctypes.byref(plan)) == 2

@@ -226,3 +226,34 @@ def test_gemv_int4_per_row(wq, n, k):
     e = _compare(y32, y16, ref, (n,))
     _check_guards(b32, b16, n)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+I8M_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 16), (70, 8192)]] + \
+    [(m, 19, 28672) for m in (2, 5, 8)] + [(5, 300, 4112), (3, 17, 57344), (8, 5, 1 << 17), (5, 7, 0)]
+
+
+@pytest.mark.parametrize("m,n,k", I8M_CASES)
+def test_gemm_small_m_int8(wq, m, n, k):
+    """m token rows through one int8 linear (16-row tiles on the matrix
+    cores, passes split across a workgroup's waves) vs the oracle; each row
+    matches the one-token int8 matvec."""
+    import torch
+    from oracle.quant import quantize_int8
+    from oracle.matvec import gemm_small_m_int8
+    say(f"gemm_smallM_int8 m={m} n={n} k={k}")
+    w = host_normal((n, k), 0.02, 951, m, n, k)
+    q, s = quantize_int8(w)
+    x = host_bf16_normal((m, k), 951, m, n, k + 1)
+    ref = gemm_small_m_int8(x, q, s) if k else np.zeros((m, n))
+    (b32, y32), (b16, y16) = _outputs(n, m)
+    qd, sd, xd = _d(q), dev(s), _d(x)
+    wq.wq_gemm_smallM_int8(xd, m, qd, sd, n, k, y32, y16)
+    e = _compare(y32, y16, ref, (m, n))
+    _check_guards(b32, b16, m * n)
+    if 0 < k <= 65536:    # the one-token int8 matvec's row limit
+        one = torch.empty(n, dtype=torch.float32, device="cuda")
+        got = host(y32).reshape(m, n)
+        for i in range(m):
+            wq.wq_gemv_int8(xd[i], qd, sd, n, k, one, None)
+            assert rel_err(host(one), got[i]) <= 1e-5
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")

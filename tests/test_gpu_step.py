@@ -13,7 +13,7 @@ import pytest
 from gpu_util import dev, host, host_u16, rel_err, bf16_bits_to_f64, TOL_F32, TOL_BF16, say
 from oracle.bf16 import round_f32_to_bf16
 from oracle.quant import quantize_int8, quantize_int4
-from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m
+from oracle.matvec import gemv_bf16, gemv_int8, gemv_int4g32, gemm_small_m, gemm_small_m_int8
 from synth.gen import host_normal, host_bf16_normal
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +34,15 @@ SHAPES = {
     ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128)],
     ("int4g256", 1): [(300, 4096), (37, 11008 // 256 * 256), (1, 256), (9, 28672)],
     ("int4pc", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 32), (129, 1056), (3, 28672)],
+    # int8 with 2..8 token rows: 16-row tiles, passes of 256 inputs (ragged
+    # row counts, k not a multiple of a pass, one 16-input chunk)
+    ("int8", 2): [(300, 4096), (37, 11008), (1, 16)],
+    ("int8", 3): [(45, 4112), (9, 28672)],
+    ("int8", 4): [(77, 8192), (33, 1040)],
+    ("int8", 5): [(300, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 16), (40, 8208)],
+    ("int8", 6): [(45, 4096), (9, 14336)],
+    ("int8", 7): [(45, 4096), (31, 8192), (2, 48)],
+    ("int8", 8): [(45, 4096), (9, 16384), (3, 57344)],
 }
 
 
@@ -49,7 +58,7 @@ def _build(fmt, m, seed):
             W, A = dev(wb), None
         elif fmt == "int8":
             q, s = quantize_int8(w)
-            ref = gemv_int8(x, q, s)
+            ref = gemm_small_m_int8(x, q, s) if m > 1 else gemv_int8(x, q, s)
             W, A = dev(q), dev(s)
         else:
             p, sz = quantize_int4(w, k if fmt == "int4pc" else int(fmt[5:]))     # "int4g<G>" / one group per row
@@ -141,6 +150,12 @@ def test_step_argument_errors():
         wq.wq_decode_step_prepare("int4g256", 1, [(buf, buf, buf, 4, 28928, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int8", 9, [good], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
+        wq.wq_decode_step_prepare("int8", 5, [(buf, buf, buf, 4, 40, buf, None)], ws)
+    assert ei.value.status == 2
+    with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4pc", 5, [good], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
@@ -148,7 +163,8 @@ def test_step_argument_errors():
     assert ei.value.status == 2
 
 
-@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4pc", 1), ("int4g32", 2), ("int4g32", 5)])
+@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4pc", 1), ("int4g32", 2), ("int4g32", 5),
+                                  ("int8", 5)])
 def test_step_balance_never_changes_results(fmt, m):
     """Each launch re-cuts the workgroups' ranges from the balance state the
     previous launches measured (XCD speed weights for one token row, the

@@ -78,6 +78,10 @@ __device__ __forceinline__ u32x4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint
 __device__ __forceinline__ uint32_t buffer_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 2);
 }
+// default cache policy (data that other waves read again, e.g. activations)
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
 
 // A constant held in a VGPR.  gfx9 VOP3 instructions cannot take two
 // literal/SGPR operands, so a mask used with a second constant (as in

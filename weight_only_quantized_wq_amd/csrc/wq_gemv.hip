@@ -1,11 +1,14 @@
 // Batch-1 (and small-M) decode matvecs y = x . W^T over bf16, int8 per-row
-// and int4 G=32 weights, streamed from HBM: launch planning and the C entry
-// points.  The kernel itself is in wq_gemv_kernel.hpp.
+// and int4 weights, streamed from HBM: launch planning and the C entry
+// points.  The kernels are in wq_gemv_kernel.hpp (one token row, and two
+// int4 rows), wq_mfma.hpp (3..8 int4 rows) and wq_step_i8mt.hpp (2..8 int8
+// rows).
 #include <stdint.h>
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
 #include "wq_mfma.hpp"
+#include "wq_step_i8mt.hpp"
 
 namespace wq {
 
@@ -127,9 +130,11 @@ static int int4_group_shift(int64_t group, int64_t k) {
 }
 
 // `group` >= 0 (int4): the group size, checked with the sizes; -1: no groups.
+// `max_bytes` > 0: a bound on the n x row_bytes weight bytes, checked with
+// the sizes.
 static int check_common(const char* name, const void* x, const void* w, const void* aux, bool need_aux, int64_t n,
                         int64_t k, const float* y32, const uint16_t* y16, int kmult, int64_t m = 1,
-                        int64_t group = -1) {
+                        int64_t group = -1, int64_t row_bytes = 0, int64_t max_bytes = 0) {
   if (!x || !w) return fail(WQ_ERR_NULL, "%s: x and the weights must be non-null", name);
   if (need_aux && !aux) return fail(WQ_ERR_NULL, "%s: the scale array must be non-null", name);
   if (!y32 && !y16) return fail(WQ_ERR_NULL, "%s: at least one of y_f32 / y_bf16 must be non-null", name);
@@ -143,6 +148,9 @@ static int check_common(const char* name, const void* x, const void* w, const vo
                 (long long)k);
   if (group > 0 && k % group)
     return fail(WQ_ERR_SHAPE, "%s: k = %lld is not a multiple of group %lld", name, (long long)k, (long long)group);
+  if (max_bytes > 0 && n * row_bytes > max_bytes)
+    return fail(WQ_ERR_SHAPE, "%s: %lld weight bytes (n = %lld, k = %lld) exceed %lld", name,
+                (long long)(n * row_bytes), (long long)n, (long long)k, (long long)max_bytes);
   if (!aligned16(x) || !aligned16(w)) return fail(WQ_ERR_ALIGN, "%s: x and weights must be 16-byte aligned", name);
   return WQ_OK;
 }
@@ -279,4 +287,59 @@ extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpack
   }
   if (m == 2) return run_gemv<FmtInt4, 2>(a, s, "wq_gemm_smallM");
   return run_gemv<FmtInt4, 1>(a, s, "wq_gemm_smallM");
+}
+
+namespace wq {
+
+// int8 with 2..8 token rows: 16-row tiles, passes of 4 CPL 16-input chunks
+// per row, the passes split over WAVES waves.
+constexpr int kI8mCPL = 4, kI8mWaves = 8;
+constexpr int64_t kI8mMaxBytes = (int64_t)0xFFFFFF00u;   // codes addressed with 32-bit offsets
+
+template <int M>
+int launch_i8m(GemvArgs a, hipStream_t stream) {
+  static int resident = 0;
+  auto kern = gemm_i8_smallm_kernel<M, kI8mCPL, kI8mWaves>;
+  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
+  const int64_t chunks = a.k / 16, per_pass = 4 * kI8mCPL;
+  a.cpl = (int32_t)((chunks + per_pass - 1) / per_pass);
+  a.batches = (a.n + 15) / 16;
+  const int64_t grid = balanced_grid(a.batches, resident);
+  if (grid <= 0) return WQ_OK;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kI8mWaves * kWave), 0, stream, a);
+  return launch_status("wq_gemm_smallM_int8");
+}
+
+}  // namespace wq
+
+extern "C" int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q, const uint16_t* scale, int64_t n,
+                                   int64_t k, float* y_f32, uint16_t* y_bf16, void* stream) {
+  const char* name = "wq_gemm_smallM_int8";
+  int rc = check_common(name, x, q, scale, true, n, k, y_f32, y_bf16, 16, m, -1, k, kI8mMaxBytes);
+  if (rc) return rc;
+  if ((reinterpret_cast<uintptr_t>(scale) & 1u) != 0) return fail(WQ_ERR_ALIGN, "%s: scale must be 2-byte aligned", name);
+  if (n == 0) return WQ_OK;
+  if ((rc = check_device())) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  GemvArgs a{};
+  a.x = x;
+  a.w = reinterpret_cast<const uint8_t*>(q);
+  a.scale = scale;
+  a.y32 = y_f32;
+  a.y16 = y_bf16;
+  a.n = n;
+  a.k = k;
+  a.row_bytes = k;
+  a.chunks = (int32_t)(k / 16);
+  if (m == 1) return run_gemv<FmtInt8, 1>(a, s, name);
+  // (k == 0: no passes; every output is the empty sum, 0)
+  switch (m) {
+    case 2: return launch_i8m<2>(a, s);
+    case 3: return launch_i8m<3>(a, s);
+    case 4: return launch_i8m<4>(a, s);
+    case 5: return launch_i8m<5>(a, s);
+    case 6: return launch_i8m<6>(a, s);
+    case 7: return launch_i8m<7>(a, s);
+    default: return launch_i8m<8>(a, s);
+  }
 }

@@ -1,6 +1,7 @@
 // Whole decode step in one launch: plan once on the host, then launch the
 // persistent step kernel (wq_step_shared.hpp for one token row, wq_verify.hpp
-// for 2..8) as often as needed.
+// for 2..8 with int4 G=32 weights, wq_step_i8mt.hpp for 2..8 with int8
+// weights) as often as needed.
 #include <stdint.h>
 #include <string.h>
 
@@ -8,6 +9,7 @@
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
+#include "wq_step_i8mt.hpp"
 #include "wq_step_shared.hpp"
 #include "wq_verify.hpp"
 
@@ -23,8 +25,10 @@ struct StepLaunch {
 // One persistent kernel configuration per (format, tokens per pass): the
 // largest chunks per lane a pass uses, waves per workgroup and rows per
 // batch, and which kernel: the shared-activation kernel (one format, one
-// token row; batch = u rows of one wave) or the matrix-core verify kernel
-// (int4, 2..8 token rows; batch = u rows in 16-row tiles).
+// token row; batch = u rows of one wave), the matrix-core verify kernel
+// (int4, 2..8 token rows; batch = u rows in 16-row tiles) or the int8
+// matrix-core kernel (2..8 token rows; batch = u rows in 16-row tiles that
+// one wave streams, 4 cpl_max chunks of each row per pass).
 struct StepVariant {
   int cpl_max;
   int waves;
@@ -34,6 +38,7 @@ struct StepVariant {
   int cmax;    // > 0: the shared-activation kernel, staging at most cmax chunks of a row
   bool verify; // the matrix-core verify kernel
   int kw = 0;   // verify: groups of one staged activation window
+  bool tiled = false;   // the int8 matrix-core kernel
 };
 
 template <class F, int U, int CPL, int WAVES, bool PF>
@@ -47,6 +52,26 @@ static StepVariant shared_variant() {
   return StepVariant{CPL, WAVES, U, reinterpret_cast<const void*>(gemv_step_shared_kernel<F, U, CPL, WAVES, PF>),
                      &shared_launch<F, U, CPL, WAVES, PF>, shared_x_cmax<F, CPL>(), false};
 }
+
+template <int M, int U, int CPL, int WAVES>
+static void i8mt_launch(int grid, const StepLaunch& l, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_i8_step_kernel<M, U, CPL, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
+                     l.mats, l.cuts);
+}
+
+template <int M, int U = 2, int CPL = 4, int WAVES = 8>
+static StepVariant i8mt_variant() {
+  StepVariant v{CPL, WAVES, 16 * U, reinterpret_cast<const void*>(gemm_i8_step_kernel<M, U, CPL, WAVES>),
+                &i8mt_launch<M, U, CPL, WAVES>, 0, false};
+  v.tiled = true;
+  return v;
+}
+
+// the int8 matrix-core kernel addresses a matrix's codes and its M x k
+// activations with 32-bit offsets below 0xFFFFFFE0 (larger ones mean "past
+// the end")
+constexpr int64_t kTiledMaxK = (int64_t)1 << 24;
+constexpr int64_t kTiledMaxBytes = (int64_t)0xFFFFFF00u;
 
 constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 // starting value of the verify kernel's long-row cost factor (measured on
@@ -74,6 +99,17 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     v = shared_variant<FmtBf16, 4, 2, 16, true>();
   } else if (format == WQ_FORMAT_INT8 && m == 1) {
     v = shared_variant<FmtInt8, 2, 2, 16, true>();
+  } else if (format == WQ_FORMAT_INT8) {
+    switch (m) {
+      case 2: v = i8mt_variant<2>(); break;
+      case 3: v = i8mt_variant<3>(); break;
+      case 4: v = i8mt_variant<4>(); break;
+      case 5: v = i8mt_variant<5>(); break;
+      case 6: v = i8mt_variant<6>(); break;
+      case 7: v = i8mt_variant<7>(); break;
+      case 8: v = i8mt_variant<8>(); break;
+      default: return false;
+    }
   } else if ((format == WQ_FORMAT_INT4G64 || format == WQ_FORMAT_INT4G128 || format == WQ_FORMAT_INT4G256 ||
               format == WQ_FORMAT_INT4PC) &&
              m == 1) {
@@ -176,7 +212,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   if (count < 1) return fail(WQ_ERR_SHAPE, "%s: count = %d must be >= 1", name, count);
   StepVariant v{};
   if (!pick_variant(format, m, v))
-    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int8, int4 G64/128/256 and per-row int4, 1..8 for int4 G32)", name,
+    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int4 G64/128/256 and per-row int4, 1..8 for int8 and int4 G32)", name,
                 format, m);
   const int wpc = weights_per_chunk(format);
   std::vector<GemvArgs> desc((size_t)count);
@@ -194,9 +230,11 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: n = %lld, k = %lld (need n >= 1, k a positive multiple of %d)",
                   name, i, (long long)mt.n, (long long)mt.k, kmult);
     const int64_t chunks = mt.k / wpc;
-    const int64_t per_wave_max = (int64_t)kWave * v.cpl_max;
+    // chunks of a row one pass covers
+    const int64_t per_wave_max = v.tiled ? (int64_t)4 * v.cpl_max : (int64_t)kWave * v.cpl_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
-    if ((v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax))
+    if ((v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax) ||
+        (v.tiled && (mt.k > kTiledMaxK || mt.n * row_bytes_of(format, mt.k) > kTiledMaxBytes)))
       return fail(WQ_ERR_SHAPE, "%s: matrix %d: k = %lld is larger than this step kernel supports", name, i,
                   (long long)mt.k);
     if (!aligned16(mt.x) || !aligned16(mt.w) ||
@@ -217,9 +255,9 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.chunks = (int32_t)chunks;
     a.split = 1;
     a.groups = 1;
-    // the shared-activation kernel streams a row in `passes` passes of cpl_max
-    // chunks per lane
-    a.cpl = v.cmax ? (int32_t)passes : 1;
+    // the shared-activation and int8 matrix-core kernels stream a row in
+    // `passes` passes
+    a.cpl = (v.cmax || v.tiled) ? (int32_t)passes : 1;
     // the verify kernel's batch is a block of 16-row tiles, the
     // shared-activation kernel's u rows of one wave
     const int64_t rows_per_batch = (int64_t)v.u;
@@ -229,11 +267,11 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     const double aux_bytes =
         is_int4(format) ? (double)int4_row_words(chunks, a.gshift) * 4 : (format == WQ_FORMAT_INT8 ? 2 : 0);
     batch_bytes[(size_t)i] = (double)rows_per_batch * ((double)a.row_bytes + aux_bytes);
-    // the shared-activation kernel spends arithmetic on every lane of a pass,
+    // the streaming kernels spend arithmetic on every lane of a pass,
     // including the lanes past a row's end in its last pass: weigh a batch by
     // its padded length so that rows whose length is not a multiple of a
     // pass (e.g. k = 11008) get proportionally shorter ranges
-    if (v.cmax) batch_bytes[(size_t)i] *= (double)(passes * per_wave_max) / (double)chunks;
+    if (v.cmax || v.tiled) batch_bytes[(size_t)i] *= (double)(passes * per_wave_max) / (double)chunks;
   }
   int rc = check_device();
   if (rc) return rc;

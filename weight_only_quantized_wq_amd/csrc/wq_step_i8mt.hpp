@@ -1,0 +1,256 @@
+// 2..8 token rows through int8 weights (one bf16 scale per output row) on
+// the matrix cores, v_mfma_f32_16x16x32_bf16, for the decode step and for
+// one matrix:
+//   * A = 16 weight rows x 32 inputs: lane l holds row l % 16, inputs
+//     8 (l / 16) .. + 7 of the MFMA's K slice.  Each code becomes an exact
+//     bf16 (a signed 8-bit integer has at most 8 significant bits): a
+//     sign-extending byte conversion to fp32, whose upper half is the bf16.
+//   * B = the token rows' activations: column t is token t (zero for t >= M),
+//     read straight from memory -- the same M x K values serve every tile of
+//     the matrix, so they stay in L2.
+//   * D[row][t] accumulates in fp32 over the whole row; y = scale * D.
+// A wave streams a batch of U tiles (16 U rows) over K in passes.  In pass p
+// lane l loads CPL 16-byte pieces of its row: piece j is input chunk
+// c = (p CPL + j) 4 + l / 16 (16 inputs), so each load instruction reads 64
+// contiguous bytes of each of the 16 rows.  Chunk c feeds two MFMAs (its
+// first and its last 8 inputs); B of MFMA h for lane l is inputs
+// 16 c + 8 h .. + 7 of token l % 16, matching A element by element.  The
+// MACs cost one MFMA per 512 weight bytes (about a tenth of the matrix
+// cores' rate at full HBM bandwidth) and the decode 1.5 VALU ops per byte.
+#pragma once
+
+#include <stdint.h>
+
+#include "wq_gemv_kernel.hpp"
+#include "wq_mfma.hpp"
+#include "wq_step_shared.hpp"
+
+namespace wq {
+
+template <int U, int CPL>
+struct MtPassBuf {
+  u32x4 w[U][CPL];   // codes: tile u, piece j
+  u32x4 x[CPL][2];   // B operands: piece j, MFMA h
+  uint32_t sb;       // bf16 bits of the scale of row 16 U batch + lane (lanes < 16 U; clamped)
+};
+
+// bf16 pairs of the 8 codes in words d0, d1 (code 2i in the low half of pair i)
+__device__ __forceinline__ void i8_to_bf16x8(uint32_t d0, uint32_t d1, uint32_t (&p)[4]) {
+  const uint32_t d[2] = {d0, d1};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t f0 = __float_as_uint((float)(int8_t)(d[i]));
+    const uint32_t f1 = __float_as_uint((float)(int8_t)(d[i] >> 8));
+    const uint32_t f2 = __float_as_uint((float)(int8_t)(d[i] >> 16));
+    const uint32_t f3 = __float_as_uint((float)(int8_t)(d[i] >> 24));
+    p[2 * i] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);       // (upper half of f0, upper half of f1)
+    p[2 * i + 1] = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+  }
+}
+
+// Loads pass `pass` of batch `batch`.  The lanes of a wave read 16 different
+// rows, so the codes go through one buffer resource over the whole matrix
+// (n row_bytes < 2^32, checked on the host) with per-lane offsets; rows past
+// n and chunks past the row take an offset past the resource and read zero,
+// as do tokens past M in the activations' resource.  With !ok every load
+// reads zeros (empty resources) without touching memory, so a prefetch past
+// the segment is issued like any other.
+template <int M, int U, int CPL>
+__device__ __forceinline__ void mt_load_pass(const GemvArgs& a, int64_t batch, int pass, int lane,
+                                             MtPassBuf<U, CPL>& bt, bool ok) {
+  constexpr uint32_t kPast = 0xFFFFFFF0u;
+  const int rin = lane & 15, slot = lane >> 4;
+  const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w, ok ? (uint32_t)(a.n * a.row_bytes) : 0u);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = (batch * U + u) * 16 + rin;
+    const bool row_ok = r < a.n;
+    const uint32_t base = (uint32_t)(r * a.row_bytes);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = (pass * CPL + j) * 4 + slot;
+      bt.w[u][j] = buffer_load16_nt(rw, row_ok && c < a.chunks ? base + (uint32_t)c * 16u : kPast);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, ok ? (uint32_t)(M * a.k * 2) : 0u);
+  const uint32_t tok = (uint32_t)(lane & 15) * (uint32_t)(a.k * 2);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = (pass * CPL + j) * 4 + slot;
+    const uint32_t off = c < a.chunks ? tok + (uint32_t)c * 32u : kPast - 16u;
+    bt.x[j][0] = buffer_load16(rx, off);
+    bt.x[j][1] = buffer_load16(rx, off + 16u);
+  }
+  int64_t rs = batch * U * 16 + (lane < 16 * U ? lane : 0);
+  if (rs >= a.n) rs = a.n - 1;
+  bt.sb = (uint32_t)*gmem(a.scale + rs);
+}
+
+// Accumulates one pass of U tiles into acc.
+template <int U, int CPL>
+__device__ __forceinline__ void mt_accumulate(const MtPassBuf<U, CPL>& bt, f32x4 (&acc)[U]) {
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b[4] = {bt.x[j][h][0], bt.x[j][h][1], bt.x[j][h][2], bt.x[j][h][3]};
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        uint32_t av[4];
+        i8_to_bf16x8(bt.w[u][j][2 * h], bt.w[u][j][2 * h + 1], av);
+        acc[u] = mfma_bf16(av, b, acc[u]);
+      }
+    }
+  }
+}
+
+// Scales and stores the 16 U rows x M tokens of batch `batch` (lane l holds
+// rows 4 (l / 16) + r of each tile for token l % 16; `sb` is the scale of
+// row 16 U batch + lane in lanes < 16 U).  Every lane must call it.
+template <int M, int U>
+__device__ __forceinline__ void mt_store(const GemvArgs& a, int64_t batch, int lane, const f32x4 (&acc)[U],
+                                         uint32_t sb) {
+  const int t = lane & 15, slot = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      // the scale of this lane's row r sits in lane 16 u + 4 slot + r
+      const uint32_t sbits = (uint32_t)__builtin_amdgcn_ds_bpermute((16 * u + 4 * slot + r) * 4, (int)sb);
+      const int64_t row = (batch * U + u) * 16 + 4 * slot + r;
+      if (t < M && row < a.n) {
+        const float v = acc[u][r] * __uint_as_float(sbits << 16);
+        if (a.y32) *gmem(a.y32 + (int64_t)t * a.n + row) = v;
+        if (a.y16) *gmem(a.y16 + (int64_t)t * a.n + row) = f32_to_bf16(v);
+      }
+    }
+  }
+}
+
+// Accumulates one pass; after the batch's last pass, stores the batch and
+// clears the accumulators.
+template <int M, int U, int CPL>
+__device__ __forceinline__ void mt_finish_pass(const GemvArgs& a, int64_t batch, int pass, int passes, int lane,
+                                               const MtPassBuf<U, CPL>& bt, f32x4 (&acc)[U]) {
+  mt_accumulate<U, CPL>(bt, acc);
+  if (pass + 1 < passes) return;
+  mt_store<M, U>(a, batch, lane, acc, bt.sb);
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// The waves' share of one matrix segment: batches [lb, le) of `a`, claimed
+// one at a time from `ctr` (zeroed by the caller).  Two pass buffers
+// alternate, so the next pass's request is always in flight while one is
+// consumed (the same discipline as the one-token kernel's stream_segment).
+template <int M, int U, int CPL>
+__device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb, int64_t le, int* ctr, int lane) {
+  const int passes = a.cpl;
+  int64_t cur = lb + claim_batch(ctr, lane);
+  if (cur >= le) return;
+  int64_t nxt = lb + claim_batch(ctr, lane);
+  int pass = 0;
+  f32x4 acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  MtPassBuf<U, CPL> A, B;
+  mt_load_pass<M, U, CPL>(a, cur, 0, lane, A, true);
+  for (;;) {
+    int64_t c2 = cur;
+    int p2 = pass + 1;
+    if (p2 == passes) {
+      c2 = nxt;
+      p2 = 0;
+    }
+    bool more = c2 < le;
+    mt_load_pass<M, U, CPL>(a, c2, p2, lane, B, more);
+    if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
+    mt_finish_pass<M, U, CPL>(a, cur, pass, passes, lane, A, acc);
+    if (!more) {
+      wait_vmem_all();   // no path reaches the loop head with the last request in flight
+      break;
+    }
+    cur = c2;
+    pass = p2;
+
+    c2 = cur;
+    p2 = pass + 1;
+    if (p2 == passes) {
+      c2 = nxt;
+      p2 = 0;
+    }
+    more = c2 < le;
+    mt_load_pass<M, U, CPL>(a, c2, p2, lane, A, more);
+    if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
+    mt_finish_pass<M, U, CPL>(a, cur, pass, passes, lane, B, acc);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+    cur = c2;
+    pass = p2;
+  }
+}
+
+// mats: per-matrix descriptors (batch = U tiles of 16 rows; `cpl` holds the
+// number of passes per row); ranges and XCD balance as in the one-token step.
+template <int M, int U, int CPL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_i8_step_kernel(const GemvArgs* __restrict__ mats, StepCuts cuts) {
+  __shared__ int ctr;
+  const int lane = lane_id();
+  step_frame<WAVES>(mats, cuts, [&](const GemvArgs& a, int64_t lb, int64_t le) {
+    __syncthreads();   // every wave has left the previous segment
+    if (threadIdx.x == 0) ctr = 0;
+    __syncthreads();
+    mt_stream_segment<M, U, CPL>(a, lb, le, &ctr, lane);
+  });
+}
+
+// One matrix (wq_gemm_smallM_int8): workgroup b takes tiles b, b + grid, ...
+// (batches of one 16-row tile); its waves split the tile's passes (wave w:
+// passes w, w + WAVES, ...), and their sums meet in LDS, added in wave order,
+// so results do not depend on timing.
+template <int M, int CPL, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_i8_smallm_kernel(GemvArgs a) {
+  __shared__ f32x4 red[WAVES][kWave];
+  const int lane = lane_id();
+  const int wave = (int)(threadIdx.x >> 6);
+  const int passes = a.cpl;
+  for (int64_t batch = blockIdx.x; batch < a.batches; batch += gridDim.x) {
+    f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+    MtPassBuf<1, CPL> A, B;
+    int p = wave;
+    mt_load_pass<M, 1, CPL>(a, batch, p, lane, A, p < passes);
+    for (;;) {
+      p += WAVES;
+      bool more = p < passes;
+      mt_load_pass<M, 1, CPL>(a, batch, p, lane, B, more);
+      mt_accumulate<1, CPL>(A, acc);
+      if (!more) {
+        wait_vmem_all();
+        break;
+      }
+      p += WAVES;
+      more = p < passes;
+      mt_load_pass<M, 1, CPL>(a, batch, p, lane, A, more);
+      mt_accumulate<1, CPL>(B, acc);
+      if (!more) {
+        wait_vmem_all();
+        break;
+      }
+    }
+    red[wave][lane] = acc[0];
+    __syncthreads();
+    if (wave == 0) {
+      f32x4 tot[1] = {red[0][lane]};
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) tot[0] += red[w][lane];
+      int64_t rs = batch * 16 + (lane < 16 ? lane : 0);
+      if (rs >= a.n) rs = a.n - 1;
+      mt_store<M, 1>(a, batch, lane, tot, (uint32_t)*gmem(a.scale + rs));
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace wq

@@ -259,18 +259,16 @@ __device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8
   return c.prefix[c.count] * (before / all);
 }
 
-// mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of
-// passes per row).  Each workgroup cuts its own contiguous range of the
-// step's batches from the cost prefix and the XCD speed weights.
-template <class F, int U, int CPL, int WAVES, bool PF>
-__global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const GemvArgs* __restrict__ mats,
-                                                                      StepCuts cuts) {
-  constexpr int CMAX = shared_x_cmax<F, CPL>();
-  __shared__ __attribute__((aligned(16))) uint32_t xs[kSharedXWords];
-  __shared__ int ctr;
+// The persistent step's frame.  Each workgroup cuts its own contiguous range
+// of the step's batches from the cost prefix and the XCD speed weights,
+// hands each matrix's part of it, batches [lb, le) of `a`, to
+// `segment(a, lb, le)` (called by every thread of the workgroup), and then
+// reports the cost it streamed and the time it took to the XCD balance.
+template <int WAVES, class Segment>
+__device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, const StepCuts& cuts,
+                                           Segment&& segment) {
   __shared__ int64_t range[2];
   __shared__ int first_mat;
-  const int lane = lane_id();
   const long long t_start = wall_clock64();
   float w[8];
 #pragma unroll
@@ -313,12 +311,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
     const int64_t mend = a.batch_begin + a.batches;
     const int64_t lb = gb - a.batch_begin;
     const int64_t le = (gend < mend ? gend : mend) - a.batch_begin;
-    const int cpad = a.cpl * CPL * kWave;
-    __syncthreads();   // every wave is done with the previous segment's LDS
-    for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
-    if (threadIdx.x == 0) ctr = 0;
-    __syncthreads();
-    stream_segment<F, U, CPL, CMAX, PF>(a, lb, le, xs, &ctr, lane);
+    segment(a, lb, le);
     gb = a.batch_begin + le;
     ++mi;
   }
@@ -361,6 +354,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
       atomicExch(&b->done, 0);
     }
   }
+}
+
+// mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of
+// passes per row).  Each segment's activations are staged in LDS, then the
+// waves claim its batches one at a time.
+template <class F, int U, int CPL, int WAVES, bool PF>
+__global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const GemvArgs* __restrict__ mats,
+                                                                      StepCuts cuts) {
+  constexpr int CMAX = shared_x_cmax<F, CPL>();
+  __shared__ __attribute__((aligned(16))) uint32_t xs[kSharedXWords];
+  __shared__ int ctr;
+  const int lane = lane_id();
+  step_frame<WAVES>(mats, cuts, [&](const GemvArgs& a, int64_t lb, int64_t le) {
+    const int cpad = a.cpl * CPL * kWave;
+    __syncthreads();   // every wave is done with the previous segment's LDS
+    for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
+    if (threadIdx.x == 0) ctr = 0;
+    __syncthreads();
+    stream_segment<F, U, CPL, CMAX, PF>(a, lb, le, xs, &ctr, lane);
+  });
 }
 
 }  // namespace wq

@@ -75,8 +75,10 @@ class QuantMatrix:
         y16 = self.y16
         if self.fmt == "bf16":
             wq.wq_gemv_bf16(self.x, self.w, self.n, self.k, y32, y16, stream)
-        elif self.fmt == "int8":
+        elif self.fmt == "int8" and self.m == 1:
             wq.wq_gemv_int8(self.x, self.w, self.aux, self.n, self.k, y32, y16, stream)
+        elif self.fmt == "int8":
+            wq.wq_gemm_smallM_int8(self.x, self.m, self.w, self.aux, self.n, self.k, y32, y16, stream)
         elif self.m == 1:
             wq.wq_gemv_int4(self.x, self.w, self.aux, self.n, self.k, int4_group(self.fmt, self.k), y32, y16, stream)
         else:

@@ -59,7 +59,10 @@ static void i8mt_launch(int grid, const StepLaunch& l, hipStream_t stream) {
                      l.mats, l.cuts);
 }
 
-template <int M, int U = 2, int CPL = 4, int WAVES = 8>
+// 4 tiles (64 rows) per batch share each activation load; 2 pieces per lane
+// per pass; 8 waves (chosen by timing the Llama-3.1-70B set at 5 tokens:
+// 64 % of HBM peak against 60 % for 2 tiles x 4 pieces and 52 % for 1 tile)
+template <int M, int U = 4, int CPL = 2, int WAVES = 8>
 static StepVariant i8mt_variant() {
   StepVariant v{CPL, WAVES, 16 * U, reinterpret_cast<const void*>(gemm_i8_step_kernel<M, U, CPL, WAVES>),
                 &i8mt_launch<M, U, CPL, WAVES>, 0, false};

@@ -29,6 +29,8 @@ namespace wq {
 
 template <int U, int CPL>
 struct MtPassBuf {
+  // one lane per row of the batch holds that row's scale
+  static_assert(16 * U <= kWave, "at most 4 tiles per batch");
   u32x4 w[U][CPL];   // codes: tile u, piece j
   u32x4 x[CPL][2];   // B operands: piece j, MFMA h
   uint32_t sb;       // bf16 bits of the scale of row 16 U batch + lane (lanes < 16 U; clamped)

@@ -117,6 +117,46 @@ __global__ __launch_bounds__(1024) void int4_rows(const uint8_t* __restrict__ bu
   if (acc == 0x12345678u) out[0] = acc;
 }
 
+// the matrix-core kernels' shape: rows of 8 KiB (int8, k = 8192); waves
+// claim batches of BR rows and stream them in passes of 8 KiB per wave (BPP
+// bytes of each row, 8 loads of 16 B per lane).  One load instruction spans
+// RPI rows x 1024 / RPI contiguous bytes: lane l reads row l % RPI of its
+// group at byte 16 (l / RPI) of the span.  RPI = 16 is the MFMA tile
+// layout (lane l supplies row l % 16); RPI = 1 reads 1 KiB of one row.
+template <int BR, int BPP, int RPI>
+__global__ __launch_bounds__(1024) void tile_rows(const uint8_t* __restrict__ buf, size_t rows, uint32_t* out) {
+  static_assert(BR * BPP == 8192 && BPP % (1024 / RPI) == 0 && BR % RPI == 0, "8 KiB per pass");
+  constexpr size_t RB = 8192;
+  constexpr int SPAN = 1024 / RPI, PIECES = BPP / SPAN;
+  __shared__ int ctr;
+  uint32_t acc = 0;
+  const int lane = threadIdx.x & 63;
+  const size_t per_wg = rows / gridDim.x / BR * BR;
+  const size_t r0 = (size_t)blockIdx.x * per_wg;
+  if (threadIdx.x == 0) ctr = 0;
+  __syncthreads();
+  for (;;) {
+    int bidx = 0;
+    if (lane == 0) bidx = atomicAdd(&ctr, 1);
+    bidx = __builtin_amdgcn_readfirstlane(bidx);
+    if ((size_t)bidx * BR >= per_wg) break;
+    const uint8_t* base = buf + (r0 + (size_t)bidx * BR) * RB;
+    for (size_t pass = 0; pass < RB / BPP; ++pass) {
+      u32x4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int g = i / PIECES, q = i % PIECES;
+        const size_t row = (size_t)g * RPI + (size_t)(lane % RPI);
+        const size_t byte = pass * BPP + (size_t)q * SPAN + (size_t)(lane / RPI) * 16;
+        v[i] = ldnt(reinterpret_cast<const u32x4*>(base + row * RB + byte));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc ^= v[i][i & 3];
+    }
+  }
+  if (acc == 0x12345678u) out[0] = acc;
+}
+
 int main() {
   const size_t bytes = (size_t)4 << 30, n16 = bytes / 16;
   u32x4* b;
@@ -152,6 +192,35 @@ int main() {
     }
     const double moved = k >= 3 ? (double)rows_used * 2560 : (double)bytes;
     printf("  %-44s %.3f ms  %7.1f GB/s\n", names[k], best, moved / best / 1e6);
+  }
+  printf("part 1b: tile patterns over 4 GiB of 8 KiB rows, %d workgroups x 16 waves (best of 5)\n", cus);
+  const size_t trows = bytes / 8192;
+  const char* tnames[7] = {"64 rows/batch, 128 B/row/pass, 16 rows/load", "64 rows/batch, 128 B/row/pass,  8 rows/load",
+                           "32 rows/batch, 256 B/row/pass, 16 rows/load", "32 rows/batch, 256 B/row/pass,  4 rows/load",
+                           "16 rows/batch, 512 B/row/pass, 16 rows/load", "16 rows/batch, 512 B/row/pass,  2 rows/load",
+                           " 8 rows/batch,  1 KiB/row/pass, 1 row/load"};
+  for (int k = 0; k < 7; ++k) {
+    float best = 1e30f;
+    for (int it = 0; it < 5; ++it) {
+      CHECK(hipEventRecord(e0));
+      const uint8_t* bb = reinterpret_cast<const uint8_t*>(b);
+      if (k == 0) tile_rows<64, 128, 16><<<cus, 1024>>>(bb, trows, out);
+      if (k == 1) tile_rows<64, 128, 8><<<cus, 1024>>>(bb, trows, out);
+      if (k == 2) tile_rows<32, 256, 16><<<cus, 1024>>>(bb, trows, out);
+      if (k == 3) tile_rows<32, 256, 4><<<cus, 1024>>>(bb, trows, out);
+      if (k == 4) tile_rows<16, 512, 16><<<cus, 1024>>>(bb, trows, out);
+      if (k == 5) tile_rows<16, 512, 2><<<cus, 1024>>>(bb, trows, out);
+      if (k == 6) tile_rows<8, 1024, 1><<<cus, 1024>>>(bb, trows, out);
+      CHECK(hipGetLastError());
+      CHECK(hipEventRecord(e1));
+      CHECK(hipEventSynchronize(e1));
+      float ms;
+      CHECK(hipEventElapsedTime(&ms, e0, e1));
+      if (ms < best) best = ms;
+    }
+    const size_t br = k < 2 ? 64 : (k < 4 ? 32 : (k < 6 ? 16 : 8));
+    const double moved = (double)(trows / cus / br * br * cus) * 8192;
+    printf("  %-44s %.3f ms  %7.1f GB/s\n", tnames[k], best, moved / best / 1e6);
   }
   printf("part 2: back-to-back launches over one buffer size (grid-stride, %d x 1024 threads)\n", cus * 2);
   for (size_t mb = 8; mb <= 512; mb *= 2) {

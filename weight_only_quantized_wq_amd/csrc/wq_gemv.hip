@@ -291,17 +291,17 @@ extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpack
 
 namespace wq {
 
-// int8 with 2..8 token rows: 16-row tiles, passes of 4 CPL 16-input chunks
-// per row, the passes split over WAVES waves.
-constexpr int kI8mCPL = 4, kI8mWaves = 8;
+// int8 with 2..8 token rows: 16-row tiles, passes of kMtPassChunks 16-input
+// chunks per row, the passes split over kI8mWaves waves.
+constexpr int kI8mWaves = 8;
 constexpr int64_t kI8mMaxBytes = (int64_t)0xFFFFFF00u;   // codes addressed with 32-bit offsets
 
 template <int M>
 int launch_i8m(GemvArgs a, hipStream_t stream) {
   static int resident = 0;
-  auto kern = gemm_i8_smallm_kernel<M, kI8mCPL, kI8mWaves>;
+  auto kern = gemm_i8_smallm_kernel<M, kI8mWaves>;
   if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
-  const int64_t chunks = a.k / 16, per_pass = 4 * kI8mCPL;
+  const int64_t chunks = a.k / 16, per_pass = kMtPassChunks;
   a.cpl = (int32_t)((chunks + per_pass - 1) / per_pass);
   a.batches = (a.n + 15) / 16;
   const int64_t grid = balanced_grid(a.batches, resident);

@@ -28,7 +28,7 @@ struct StepLaunch {
 // token row; batch = u rows of one wave), the matrix-core verify kernel
 // (int4, 2..8 token rows; batch = u rows in 16-row tiles) or the int8
 // matrix-core kernel (2..8 token rows; batch = u rows in 16-row tiles that
-// one wave streams, 4 cpl_max chunks of each row per pass).
+// one wave streams, cpl_max chunks of each row per pass).
 struct StepVariant {
   int cpl_max;
   int waves;
@@ -53,19 +53,17 @@ static StepVariant shared_variant() {
                      &shared_launch<F, U, CPL, WAVES, PF>, shared_x_cmax<F, CPL>(), false};
 }
 
-template <int M, int U, int CPL, int WAVES>
+template <int M, int U, int WAVES>
 static void i8mt_launch(int grid, const StepLaunch& l, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_i8_step_kernel<M, U, CPL, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
+  hipLaunchKernelGGL((gemm_i8_step_kernel<M, U, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
                      l.mats, l.cuts);
 }
 
-// 4 tiles (64 rows) per batch share each activation load; 2 pieces per lane
-// per pass; 8 waves (chosen by timing the Llama-3.1-70B set at 5 tokens:
-// 64 % of HBM peak against 60 % for 2 tiles x 4 pieces and 52 % for 1 tile)
-template <int M, int U = 4, int CPL = 2, int WAVES = 8>
+// 4 tiles (64 rows) per batch share each activation load; 8 waves
+template <int M, int U = 4, int WAVES = 8>
 static StepVariant i8mt_variant() {
-  StepVariant v{CPL, WAVES, 16 * U, reinterpret_cast<const void*>(gemm_i8_step_kernel<M, U, CPL, WAVES>),
-                &i8mt_launch<M, U, CPL, WAVES>, 0, false};
+  StepVariant v{kMtPassChunks, WAVES, 16 * U, reinterpret_cast<const void*>(gemm_i8_step_kernel<M, U, WAVES>),
+                &i8mt_launch<M, U, WAVES>, 0, false};
   v.tiled = true;
   return v;
 }
@@ -234,7 +232,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
                   name, i, (long long)mt.n, (long long)mt.k, kmult);
     const int64_t chunks = mt.k / wpc;
     // chunks of a row one pass covers
-    const int64_t per_wave_max = v.tiled ? (int64_t)4 * v.cpl_max : (int64_t)kWave * v.cpl_max;
+    const int64_t per_wave_max = v.tiled ? (int64_t)v.cpl_max : (int64_t)kWave * v.cpl_max;
     const int64_t passes = (chunks + per_wave_max - 1) / per_wave_max;
     if ((v.verify && mt.k > kVerifyMaxK) || (v.cmax && passes * per_wave_max > v.cmax) ||
         (v.tiled && (mt.k > kTiledMaxK || mt.n * row_bytes_of(format, mt.k) > kTiledMaxBytes)))

@@ -9,14 +9,19 @@
 //     read straight from memory -- the same M x K values serve every tile of
 //     the matrix, so they stay in L2.
 //   * D[row][t] accumulates in fp32 over the whole row; y = scale * D.
-// A wave streams a batch of U tiles (16 U rows) over K in passes.  In pass p
-// lane l loads CPL 16-byte pieces of its row: piece j is input chunk
-// c = (p CPL + j) 4 + l / 16 (16 inputs), so each load instruction reads 64
-// contiguous bytes of each of the 16 rows.  Chunk c feeds two MFMAs (its
-// first and its last 8 inputs); B of MFMA h for lane l is inputs
-// 16 c + 8 h .. + 7 of token l % 16, matching A element by element.  The
-// MACs cost one MFMA per 512 weight bytes (about a tenth of the matrix
-// cores' rate at full HBM bandwidth) and the decode 1.5 VALU ops per byte.
+// A wave streams a batch of U tiles (16 U rows) over K in passes of 128
+// inputs (bytes) per row.  The A layout puts 16 rows in the lanes of one
+// register, but a load instruction reaches full HBM rate only when it reads
+// whole 128-byte lines: with 64 bytes of each of 16 rows per instruction a
+// pure stream of this shape runs at ~70 % of peak, with 128 bytes of each of
+// 8 rows at ~87 %.  So a tile-pass is loaded as two instructions of 8 rows x
+// 128 bytes (lane l: row l / 8 (+ 8), bytes 16 (l % 8) .. + 15), stored into
+// a per-wave LDS tile and read back in the A layout: MFMA m of the pass takes
+// bytes 32 m + 8 s .. + 7 of its row in k-slot s.  The 16-byte slots of a
+// row are XOR-swizzled by the row (slot p of row r at p ^ (r % 8)), so both
+// the stores (two rows of 8 slots per 16 lanes) and the 8-byte reads (16 rows
+// of one slot) fall in distinct banks.  The MACs cost one MFMA per 512
+// weight bytes, the decode 1.5 VALU ops per byte.
 #pragma once
 
 #include <stdint.h>
@@ -27,13 +32,16 @@
 
 namespace wq {
 
-template <int U, int CPL>
+constexpr int kMtPassChunks = 8;      // 16-byte chunks of a row per pass (128 inputs)
+constexpr int kMtTileLds = 16 * 128;  // LDS bytes of one tile-pass
+
+template <int U>
 struct MtPassBuf {
   // one lane per row of the batch holds that row's scale
   static_assert(16 * U <= kWave, "at most 4 tiles per batch");
-  u32x4 w[U][CPL];   // codes: tile u, piece j
-  u32x4 x[CPL][2];   // B operands: piece j, MFMA h
-  uint32_t sb;       // bf16 bits of the scale of row 16 U batch + lane (lanes < 16 U; clamped)
+  u32x4 w[U][2];   // codes: tile u, rows (lane / 8) + 8 j, bytes 16 (lane % 8) .. + 15 of the pass
+  u32x4 x[4];      // B operands of the pass's four MFMAs
+  uint32_t sb;     // bf16 bits of the scale of row 16 U batch + lane (lanes < 16 U; clamped)
 };
 
 // bf16 pairs of the 8 codes in words d0, d1 (code 2i in the low half of pair i)
@@ -50,58 +58,63 @@ __device__ __forceinline__ void i8_to_bf16x8(uint32_t d0, uint32_t d1, uint32_t 
   }
 }
 
-// Loads pass `pass` of batch `batch`.  The lanes of a wave read 16 different
-// rows, so the codes go through one buffer resource over the whole matrix
-// (n row_bytes < 2^32, checked on the host) with per-lane offsets; rows past
-// n and chunks past the row take an offset past the resource and read zero,
-// as do tokens past M in the activations' resource.  With !ok every load
-// reads zeros (empty resources) without touching memory, so a prefetch past
-// the segment is issued like any other.
-template <int M, int U, int CPL>
-__device__ __forceinline__ void mt_load_pass(const GemvArgs& a, int64_t batch, int pass, int lane,
-                                             MtPassBuf<U, CPL>& bt, bool ok) {
+// Loads pass `pass` of batch `batch`.  The lanes of a wave read 8 different
+// rows per instruction, so the codes go through one buffer resource over the
+// whole matrix (n row_bytes < 2^32, checked on the host) with per-lane
+// offsets; rows past n and chunks past the row take an offset past the
+// resource and read zero, as do tokens past M and inputs past k in the
+// activations' resource.  With !ok every load reads zeros (empty resources)
+// without touching memory, so a prefetch past the segment is issued like any
+// other.
+template <int M, int U>
+__device__ __forceinline__ void mt_load_pass(const GemvArgs& a, int64_t batch, int pass, int lane, MtPassBuf<U>& bt,
+                                             bool ok) {
   constexpr uint32_t kPast = 0xFFFFFFF0u;
-  const int rin = lane & 15, slot = lane >> 4;
   const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w, ok ? (uint32_t)(a.n * a.row_bytes) : 0u);
+  const int c = pass * kMtPassChunks + (lane & 7);   // this lane's chunk of the row
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t r = (batch * U + u) * 16 + rin;
-    const bool row_ok = r < a.n;
-    const uint32_t base = (uint32_t)(r * a.row_bytes);
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = (pass * CPL + j) * 4 + slot;
-      bt.w[u][j] = buffer_load16_nt(rw, row_ok && c < a.chunks ? base + (uint32_t)c * 16u : kPast);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t r = (batch * U + u) * 16 + 8 * j + (lane >> 3);
+      const bool in = r < a.n && c < a.chunks;
+      bt.w[u][j] = buffer_load16_nt(rw, in ? (uint32_t)(r * a.row_bytes) + (uint32_t)c * 16u : kPast);
     }
   }
+  // B of MFMA m, lane 16 s + t: inputs pass 128 + 32 m + 8 s .. + 7 of token t
   const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, ok ? (uint32_t)(M * a.k * 2) : 0u);
   const uint32_t tok = (uint32_t)(lane & 15) * (uint32_t)(a.k * 2);
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = (pass * CPL + j) * 4 + slot;
-    const uint32_t off = c < a.chunks ? tok + (uint32_t)c * 32u : kPast - 16u;
-    bt.x[j][0] = buffer_load16(rx, off);
-    bt.x[j][1] = buffer_load16(rx, off + 16u);
+  for (int m = 0; m < 4; ++m) {
+    const int64_t e = (int64_t)pass * 128 + 32 * m + 8 * (lane >> 4);
+    bt.x[m] = buffer_load16(rx, e < a.k ? tok + (uint32_t)e * 2u : kPast);
   }
   int64_t rs = batch * U * 16 + (lane < 16 * U ? lane : 0);
   if (rs >= a.n) rs = a.n - 1;
   bt.sb = (uint32_t)*gmem(a.scale + rs);
 }
 
-// Accumulates one pass of U tiles into acc.
-template <int U, int CPL>
-__device__ __forceinline__ void mt_accumulate(const MtPassBuf<U, CPL>& bt, f32x4 (&acc)[U]) {
+// Accumulates one pass of U tiles into acc, through the wave's LDS tile
+// `lds` (kMtTileLds bytes, reused for each tile: the wave's LDS accesses
+// complete in order).
+template <int U>
+__device__ __forceinline__ void mt_accumulate(const MtPassBuf<U>& bt, f32x4 (&acc)[U], uint8_t* lds, int lane) {
+  const int wr = lane >> 3, ws = lane & 7;          // stored row (+ 8 j) and 16-byte slot
+  const int rr = lane & 15, rs = lane >> 4;         // A row and k-slot read back
+  uint8_t* st0 = lds + wr * 128 + ((ws ^ (wr & 7)) << 4);
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
+  for (int u = 0; u < U; ++u) {
+    *reinterpret_cast<u32x4*>(st0) = bt.w[u][0];
+    *reinterpret_cast<u32x4*>(st0 + 8 * 128) = bt.w[u][1];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t b[4] = {bt.x[j][h][0], bt.x[j][h][1], bt.x[j][h][2], bt.x[j][h][3]};
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        uint32_t av[4];
-        i8_to_bf16x8(bt.w[u][j][2 * h], bt.w[u][j][2 * h + 1], av);
-        acc[u] = mfma_bf16(av, b, acc[u]);
-      }
+    for (int m = 0; m < 4; ++m) {
+      // bytes 32 m + 8 s of row rr: slot 2 m + s / 2, half s % 2
+      const uint2 v = *reinterpret_cast<const uint2*>(lds + rr * 128 + (((2 * m + (rs >> 1)) ^ (rr & 7)) << 4) +
+                                                      ((rs & 1) << 3));
+      uint32_t av[4];
+      i8_to_bf16x8(v.x, v.y, av);
+      const uint32_t b[4] = {bt.x[m][0], bt.x[m][1], bt.x[m][2], bt.x[m][3]};
+      acc[u] = mfma_bf16(av, b, acc[u]);
     }
   }
 }
@@ -131,10 +144,10 @@ __device__ __forceinline__ void mt_store(const GemvArgs& a, int64_t batch, int l
 
 // Accumulates one pass; after the batch's last pass, stores the batch and
 // clears the accumulators.
-template <int M, int U, int CPL>
+template <int M, int U>
 __device__ __forceinline__ void mt_finish_pass(const GemvArgs& a, int64_t batch, int pass, int passes, int lane,
-                                               const MtPassBuf<U, CPL>& bt, f32x4 (&acc)[U]) {
-  mt_accumulate<U, CPL>(bt, acc);
+                                               const MtPassBuf<U>& bt, f32x4 (&acc)[U], uint8_t* lds) {
+  mt_accumulate<U>(bt, acc, lds, lane);
   if (pass + 1 < passes) return;
   mt_store<M, U>(a, batch, lane, acc, bt.sb);
 #pragma unroll
@@ -145,8 +158,9 @@ __device__ __forceinline__ void mt_finish_pass(const GemvArgs& a, int64_t batch,
 // one at a time from `ctr` (zeroed by the caller).  Two pass buffers
 // alternate, so the next pass's request is always in flight while one is
 // consumed (the same discipline as the one-token kernel's stream_segment).
-template <int M, int U, int CPL>
-__device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb, int64_t le, int* ctr, int lane) {
+template <int M, int U>
+__device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb, int64_t le, int* ctr, int lane,
+                                                  uint8_t* lds) {
   const int passes = a.cpl;
   int64_t cur = lb + claim_batch(ctr, lane);
   if (cur >= le) return;
@@ -155,8 +169,8 @@ __device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb,
   f32x4 acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  MtPassBuf<U, CPL> A, B;
-  mt_load_pass<M, U, CPL>(a, cur, 0, lane, A, true);
+  MtPassBuf<U> A, B;
+  mt_load_pass<M, U>(a, cur, 0, lane, A, true);
   for (;;) {
     int64_t c2 = cur;
     int p2 = pass + 1;
@@ -165,9 +179,9 @@ __device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb,
       p2 = 0;
     }
     bool more = c2 < le;
-    mt_load_pass<M, U, CPL>(a, c2, p2, lane, B, more);
+    mt_load_pass<M, U>(a, c2, p2, lane, B, more);
     if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
-    mt_finish_pass<M, U, CPL>(a, cur, pass, passes, lane, A, acc);
+    mt_finish_pass<M, U>(a, cur, pass, passes, lane, A, acc, lds);
     if (!more) {
       wait_vmem_all();   // no path reaches the loop head with the last request in flight
       break;
@@ -182,9 +196,9 @@ __device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb,
       p2 = 0;
     }
     more = c2 < le;
-    mt_load_pass<M, U, CPL>(a, c2, p2, lane, A, more);
+    mt_load_pass<M, U>(a, c2, p2, lane, A, more);
     if (more && p2 == 0) nxt = lb + claim_batch(ctr, lane);
-    mt_finish_pass<M, U, CPL>(a, cur, pass, passes, lane, B, acc);
+    mt_finish_pass<M, U>(a, cur, pass, passes, lane, B, acc, lds);
     if (!more) {
       wait_vmem_all();
       break;
@@ -196,15 +210,17 @@ __device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb,
 
 // mats: per-matrix descriptors (batch = U tiles of 16 rows; `cpl` holds the
 // number of passes per row); ranges and XCD balance as in the one-token step.
-template <int M, int U, int CPL, int WAVES>
+template <int M, int U, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemm_i8_step_kernel(const GemvArgs* __restrict__ mats, StepCuts cuts) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[WAVES][kMtTileLds];
   __shared__ int ctr;
   const int lane = lane_id();
+  uint8_t* lds = tiles[threadIdx.x >> 6];
   step_frame<WAVES>(mats, cuts, [&](const GemvArgs& a, int64_t lb, int64_t le) {
     __syncthreads();   // every wave has left the previous segment
     if (threadIdx.x == 0) ctr = 0;
     __syncthreads();
-    mt_stream_segment<M, U, CPL>(a, lb, le, &ctr, lane);
+    mt_stream_segment<M, U>(a, lb, le, &ctr, lane, lds);
   });
 }
 
@@ -212,30 +228,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_i8_step_kernel(const GemvArgs
 // (batches of one 16-row tile); its waves split the tile's passes (wave w:
 // passes w, w + WAVES, ...), and their sums meet in LDS, added in wave order,
 // so results do not depend on timing.
-template <int M, int CPL, int WAVES>
+template <int M, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemm_i8_smallm_kernel(GemvArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[WAVES][kMtTileLds];
   __shared__ f32x4 red[WAVES][kWave];
   const int lane = lane_id();
   const int wave = (int)(threadIdx.x >> 6);
+  uint8_t* lds = tiles[wave];
   const int passes = a.cpl;
   for (int64_t batch = blockIdx.x; batch < a.batches; batch += gridDim.x) {
     f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-    MtPassBuf<1, CPL> A, B;
+    MtPassBuf<1> A, B;
     int p = wave;
-    mt_load_pass<M, 1, CPL>(a, batch, p, lane, A, p < passes);
+    mt_load_pass<M, 1>(a, batch, p, lane, A, p < passes);
     for (;;) {
       p += WAVES;
       bool more = p < passes;
-      mt_load_pass<M, 1, CPL>(a, batch, p, lane, B, more);
-      mt_accumulate<1, CPL>(A, acc);
+      mt_load_pass<M, 1>(a, batch, p, lane, B, more);
+      mt_accumulate<1>(A, acc, lds, lane);
       if (!more) {
         wait_vmem_all();
         break;
       }
       p += WAVES;
       more = p < passes;
-      mt_load_pass<M, 1, CPL>(a, batch, p, lane, A, more);
-      mt_accumulate<1, CPL>(B, acc);
+      mt_load_pass<M, 1>(a, batch, p, lane, A, more);
+      mt_accumulate<1>(B, acc, lds, lane);
       if (!more) {
         wait_vmem_all();
         break;

@@ -18,10 +18,11 @@
 // 128 bytes (lane l: row l / 8 (+ 8), bytes 16 (l % 8) .. + 15), stored into
 // a per-wave LDS tile and read back in the A layout: MFMA m of the pass takes
 // bytes 32 m + 8 s .. + 7 of its row in k-slot s.  The 16-byte slots of a
-// row are XOR-swizzled by the row (slot p of row r at p ^ (r % 8)), so both
-// the stores (two rows of 8 slots per 16 lanes) and the 8-byte reads (16 rows
-// of one slot) fall in distinct banks.  The MACs cost one MFMA per 512
-// weight bytes, the decode 1.5 VALU ops per byte.
+// row are XOR-swizzled (slot p of row r at p ^ (r / 2 % 8)): rows 2 i and
+// 2 i + 1 fill the two halves of one 256-byte bank span, so the stores (two
+// rows of 8 slots per 16 lanes) and the 8-byte reads (one slot of 16 rows)
+// fall in distinct banks.  The MACs cost one MFMA per 512 weight bytes, the
+// decode 1.5 VALU ops per byte.
 #pragma once
 
 #include <stdint.h>
@@ -101,16 +102,17 @@ template <int U>
 __device__ __forceinline__ void mt_accumulate(const MtPassBuf<U>& bt, f32x4 (&acc)[U], uint8_t* lds, int lane) {
   const int wr = lane >> 3, ws = lane & 7;          // stored row (+ 8 j) and 16-byte slot
   const int rr = lane & 15, rs = lane >> 4;         // A row and k-slot read back
-  uint8_t* st0 = lds + wr * 128 + ((ws ^ (wr & 7)) << 4);
+  uint8_t* st0 = lds + wr * 128 + ((ws ^ ((wr >> 1) & 7)) << 4);               // row wr
+  uint8_t* st1 = lds + (wr + 8) * 128 + ((ws ^ (((wr + 8) >> 1) & 7)) << 4);   // row wr + 8
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     *reinterpret_cast<u32x4*>(st0) = bt.w[u][0];
-    *reinterpret_cast<u32x4*>(st0 + 8 * 128) = bt.w[u][1];
+    *reinterpret_cast<u32x4*>(st1) = bt.w[u][1];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // bytes 32 m + 8 s of row rr: slot 2 m + s / 2, half s % 2
-      const uint2 v = *reinterpret_cast<const uint2*>(lds + rr * 128 + (((2 * m + (rs >> 1)) ^ (rr & 7)) << 4) +
-                                                      ((rs & 1) << 3));
+      const uint2 v = *reinterpret_cast<const uint2*>(lds + rr * 128 +
+                                                      (((2 * m + (rs >> 1)) ^ ((rr >> 1) & 7)) << 4) + ((rs & 1) << 3));
       uint32_t av[4];
       i8_to_bf16x8(v.x, v.y, av);
       const uint32_t b[4] = {bt.x[m][0], bt.x[m][1], bt.x[m][2], bt.x[m][3]};

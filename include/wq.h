@@ -202,12 +202,12 @@ enum {
   WQ_FORMAT_BF16 = 1,
   WQ_FORMAT_INT8 = 2,
   WQ_FORMAT_INT4G32 = 3,
-  /* int4 with larger groups (wq_quantize_int4); one token row per step */
+  /* int4 with larger groups (wq_quantize_int4) */
   WQ_FORMAT_INT4G64 = 4,
   WQ_FORMAT_INT4G128 = 5,
   WQ_FORMAT_INT4G256 = 6,
   /* int4 with one group per row (wq_quantize_int4 with group == k): each
-     matrix's sz is [n][1][2]; k % 32 == 0; one token row per step */
+     matrix's sz is [n][1][2]; k % 32 == 0 */
   WQ_FORMAT_INT4PC = 7
 };
 
@@ -242,8 +242,8 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
 
 /*
  * Plans `count` independent matvecs of one format (m token rows each: m = 1
- * for bf16, int4 with groups of 64/128/256 and int4 with one group per row,
- * 1 <= m <= 8 for int8 and int4 G=32) as ONE persistent launch: every
+ * for bf16, 1 <= m <= 8 for int8 and for int4 with any group size) as ONE
+ * persistent launch: every
  * workgroup streams an equal share of the step's weight bytes as a contiguous
  * range of row batches across the matrices, so no matrix pays its own
  * launch, ramp-up and drain.  Results equal the single-matrix calls' to fp32

@@ -34,6 +34,13 @@ SHAPES = {
     ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128)],
     ("int4g256", 1): [(300, 4096), (37, 11008 // 256 * 256), (1, 256), (9, 28672)],
     ("int4pc", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 32), (129, 1056), (3, 28672)],
+    # larger int4 groups with 2..8 token rows: words per 32-input chunk of the
+    # (scale, zero) window, one- and multi-window rows (k > 8192), ragged n
+    ("int4g64", 2): [(45, 4096), (9, 16384), (1, 64)],
+    ("int4g128", 5): [(70, 8192), (19, 28672), (33, 1024), (8, 128), (40, 8320)],
+    ("int4g256", 8): [(45, 4096), (9, 16384), (3, 28672)],
+    ("int4pc", 5): [(70, 8192), (19, 28672), (33, 1056), (8, 32)],
+    ("int4pc", 3): [(40, 8288), (5, 96)],
     # int8 with 2..8 token rows: 16-row tiles, passes of 256 inputs (ragged
     # row counts, k not a multiple of a pass, one 16-input chunk)
     ("int8", 2): [(300, 4096), (37, 11008), (1, 16)],
@@ -139,9 +146,9 @@ def test_step_argument_errors():
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
     assert ei.value.status == 2
-    # wider int4 groups: one token row only, k a multiple of the group
+    # wider int4 groups: k a multiple of the group
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int4g128", 2, [good], ws)
+        wq.wq_decode_step_prepare("bf16", 2, [good], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g128", 1, [(buf, buf, buf, 4, 192, buf, None)], ws)
@@ -156,7 +163,7 @@ def test_step_argument_errors():
         wq.wq_decode_step_prepare("int8", 5, [(buf, buf, buf, 4, 40, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int4pc", 5, [good], ws)
+        wq.wq_decode_step_prepare("int4g64", 5, [(buf, buf, buf, 4, 2 ** 20, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4pc", 1, [(buf, buf, buf, 4, 80, buf, None)], ws)
@@ -164,7 +171,7 @@ def test_step_argument_errors():
 
 
 @pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 1), ("bf16", 1), ("int4g128", 1), ("int4pc", 1), ("int4g32", 2), ("int4g32", 5),
-                                  ("int8", 5)])
+                                  ("int8", 5), ("int4g128", 5)])
 def test_step_balance_never_changes_results(fmt, m):
     """Each launch re-cuts the workgroups' ranges from the balance state the
     previous launches measured (XCD speed weights for one token row, the

@@ -94,6 +94,10 @@ static StepVariant verify_variant() {
                      &verify_launch<M, WAVES, PF, RT, OCT, KW, QL, SB>, 0, true, KW};
 }
 
+static bool is_int4(int format) {
+  return (format >= WQ_FORMAT_INT4G32 && format <= WQ_FORMAT_INT4G256) || format == WQ_FORMAT_INT4PC;
+}
+
 static bool pick_variant(int format, int m, StepVariant& v) {
   // chosen by timing candidates on the Llama-2-7B / Llama-3.1-8B / -70B sets
   if (format == WQ_FORMAT_BF16 && m == 1) {
@@ -111,13 +115,9 @@ static bool pick_variant(int format, int m, StepVariant& v) {
       case 8: v = i8mt_variant<8>(); break;
       default: return false;
     }
-  } else if ((format == WQ_FORMAT_INT4G64 || format == WQ_FORMAT_INT4G128 || format == WQ_FORMAT_INT4G256 ||
-              format == WQ_FORMAT_INT4PC) &&
-             m == 1) {
-    // larger groups (up to one per row): the same kernel, each chunk reading
-    // its group's word
-    v = shared_variant<FmtInt4, 2, 2, 16, true>();
-  } else if (format == WQ_FORMAT_INT4G32) {
+  } else if (is_int4(format)) {
+    // every group size (up to one group per row) runs the same kernels, each
+    // 32-input chunk reading its group's (scale, zero) word
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
       case 2: v = verify_variant<2, 8, true, 2, 4, 512>(); break;
@@ -137,10 +137,6 @@ static bool pick_variant(int format, int m, StepVariant& v) {
 
 static int weights_per_chunk(int format) {
   return format == WQ_FORMAT_BF16 ? 8 : (format == WQ_FORMAT_INT8 ? 16 : 32);
-}
-
-static bool is_int4(int format) {
-  return (format >= WQ_FORMAT_INT4G32 && format <= WQ_FORMAT_INT4G256) || format == WQ_FORMAT_INT4PC;
 }
 
 // int4: log2(group / 32), or kPerRowShift for one group per row
@@ -213,7 +209,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   if (count < 1) return fail(WQ_ERR_SHAPE, "%s: count = %d must be >= 1", name, count);
   StepVariant v{};
   if (!pick_variant(format, m, v))
-    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, int4 G64/128/256 and per-row int4, 1..8 for int8 and int4 G32)", name,
+    return fail(WQ_ERR_SHAPE, "%s: unsupported format %d with m = %d (m = 1 for bf16, 1..8 for int8 and int4)", name,
                 format, m);
   const int wpc = weights_per_chunk(format);
   std::vector<GemvArgs> desc((size_t)count);

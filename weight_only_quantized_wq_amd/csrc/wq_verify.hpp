@@ -143,12 +143,17 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
   }
 }
 
-// Loads the (scale, zero) words of groups [gw, gw + kSzWin) of block `blk`
-// (zeros with !any).
+// Loads the (scale, zero) words of chunks [gw, gw + kSzWin) of block `blk`
+// (zeros with !any).  With groups of G = 32 << gshift inputs (gshift =
+// kPerRowShift: one group per row) chunk c uses word c >> gshift of its row;
+// gw is a multiple of kSzWin, so the window's words start at word
+// gw >> gshift and chunk gw + i uses word i >> gshift of the window (the
+// window then holds more words than its chunks use).
 template <int RT>
 __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, int lane, SzWindow<RT>& z,
                                         bool any = true) {
-  const int g = gw + 4 * (lane % kSzLanesPerRow);
+  const uint32_t words = (uint32_t)int4_row_words(a.chunks, a.gshift);
+  const int g = (gw >> a.gshift) + 4 * (lane % kSzLanesPerRow);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = (blk * RT + rt) * 16;
@@ -156,23 +161,24 @@ __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, 
     const bool live = any && left > 0;
     const uint32_t rows_ok = !live ? 0u : (left >= 16 ? 16u : (uint32_t)left);
     const int64_t rb = live ? rbase : 0;
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.chunks, rows_ok * (uint32_t)a.chunks * 4u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * words, rows_ok * words * 4u);
 #pragma unroll
     for (int h = 0; h < kSzLoads; ++h) {
       const uint32_t row = (uint32_t)(kSzRowsPerLoad * h + lane / kSzLanesPerRow);
       z.r[rt][h] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rs, g < a.chunks ? (int)((row * (uint32_t)a.chunks + (uint32_t)g) * 4u) : (int)0x80000000, 0, 2));
+                     rs, (uint32_t)g < words ? (int)((row * words + (uint32_t)g) * 4u) : (int)0x80000000, 0, 2));
     }
   }
 }
 
-// Writes a loaded window into the wave's LDS buffer; words of groups past
-// the row's end (which belong to the next row) become zero.
+// Writes a loaded window into the wave's LDS buffer; words past the row's
+// last (which belong to the next row) become zero.
 template <int RT>
 __device__ __forceinline__ void sz_put(const GemvArgs& a, int gw, int lane, const SzWindow<RT>& z,
                                        uint32_t (*buf)[16][kSzRow]) {
-  const int g = gw + 4 * (lane % kSzLanesPerRow);
+  const int64_t words = int4_row_words(a.chunks, a.gshift);
+  const int g = (gw >> a.gshift) + 4 * (lane % kSzLanesPerRow);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -180,7 +186,7 @@ __device__ __forceinline__ void sz_put(const GemvArgs& a, int gw, int lane, cons
       u32x4 v = z.r[rt][h];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (g + e >= a.chunks) v[e] = 0u;
+        if (g + e >= words) v[e] = 0u;
       *reinterpret_cast<u32x4*>(&buf[rt][kSzRowsPerLoad * h + lane / kSzLanesPerRow][4 * (lane % kSzLanesPerRow)]) = v;
     }
 }
@@ -215,11 +221,11 @@ __device__ __forceinline__ void verify_a(const VerifyShared<M, KW>& sh, int ga, 
 }
 
 // Accumulates one item into y[tile][set][token]; `il` is the item's first
-// group within the staged activation window and `iz` within the (scale,
-// zero) window held in `szb`.
+// chunk within the staged activation window and `iz` within the (scale,
+// zero) window held in `szb`, where chunk iz + i takes word (iz + i) >> gshift.
 template <int M, int KW, int RT, int OCT, bool QL, bool SB>
-__device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il, int iz, int rq, int col,
-                                            const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
+__device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il, int iz, int gshift, int rq,
+                                            int col, const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
                                             const FmtInt4::K& kc, uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
                                             float (&y)[RT][VerifyShared<M, KW>::kSets][4]) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
@@ -238,7 +244,7 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
         w = u32x4{to_mfma_lane(w[0], src), to_mfma_lane(w[1], src), to_mfma_lane(w[2], src),
                   to_mfma_lane(w[3], src)};
       }
-      const uint32_t szw = szb[rt][col][iz + 4 * o + rq];
+      const uint32_t szw = szb[rt][col][(iz + 4 * o + rq) >> gshift];
       FmtInt4::D d;
       FmtInt4::decode(w, d, kc);
       const float s = __uint_as_float(szw << 16);
@@ -364,7 +370,7 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
     more = b2 < nb;
     verify_load<RT, OCT, QL>(a, b0 + b2, g0, i2, lane, nx, more);
     if (more && i2 == 0) nxt = claim_batch(ctr, lane);
-    verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, rq, col, sh, szb, kc, av, y);
+    verify_item<M, KW, RT, OCT, QL, SB>(cur, it * GI, (it % IW) * GI, a.gshift, rq, col, sh, szb, kc, av, y);
     if (it + 1 == items) verify_fold<M, RT, SETS, SR>(a, b0 + bi, (int)bi, first, last, rq, col, y, part);
     bi = b2;
     it = i2;

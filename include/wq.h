@@ -158,6 +158,16 @@ int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const u
                    int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
 
 /*
+ * The same verify product through int4 weights with groups of `group`
+ * inputs (32, 64, 128, 256, or k: one group per row), qpacked and sz as
+ * written by wq_quantize_int4 with that group -- [TAGS] "Grouped
+ * Quantization".  k % group == 0 (k % 32 == 0 for a per-row group); limits
+ * as wq_gemm_smallM.  group == 32 is wq_gemm_smallM.
+ */
+int wq_gemm_smallM_int4(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
+                        int64_t k, int32_t group, float* y_f32, uint16_t* y_bf16, void* stream);
+
+/*
  * Speculative-decoding verify through an int8 linear -- [GUIDE] "Key
  * Features", [README] "推测采样" (the verify pass), with the int8 weights of
  * [README] "Int8 仅权重量化".  x bf16 [m][k], 1 <= m <= 8; q, scale as written

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["wq_quantize_int8", "wq_quantize_int4g32", "wq_quantize_int4", "wq_gemv_bf16", "wq_gemv_int8",
                  "wq_gemv_int4g32", "wq_gemv_int4",
-                 "wq_gemm_smallM", "wq_gemm_smallM_int8", "moe_top2_gemv", "wq_status_string", "wq_last_error",
+                 "wq_gemm_smallM", "wq_gemm_smallM_int4", "wq_gemm_smallM_int8", "moe_top2_gemv", "wq_status_string", "wq_last_error",
                  "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
                  "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run"]:
         assert want in names
@@ -112,6 +112,10 @@ def test_per_row_group_errors(wq):
     assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 0, 0, BAD, None, None) == 2
     assert _rc("wq_gemv_int4", BAD, BAD, BAD, 4, 64, 0, BAD, None, None) == 2
     assert "group" in wq.last_error()
+    assert _rc("wq_gemm_smallM_int4", BAD, 5, BAD, BAD, 4, 80, 80, BAD, None, None) == 2
+    assert _rc("wq_gemm_smallM_int4", BAD, 5, BAD, BAD, 4, 192, 128, BAD, None, None) == 2
+    assert _rc("wq_gemm_smallM_int4", BAD, 9, BAD, BAD, 4, 256, 128, BAD, None, None) == 2
+    assert _rc("wq_gemm_smallM_int4", BAD, 5, BAD, None, 4, 256, 128, BAD, None, None) == 1
     # a valid per-row group passes the size checks and reaches alignment
     assert _rc("wq_quantize_int4", BAD, 0, 96, 96, 0x2000, 0x2000, None) == 3
     assert _rc("wq_gemv_int4", BAD, 0x2000, 0x2000, 0, 96, 96, 0x2000, None, None) == 3

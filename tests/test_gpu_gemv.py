@@ -257,3 +257,25 @@ def test_gemm_small_m_int8(wq, m, n, k):
             wq.wq_gemv_int8(xd[i], qd, sd, n, k, one, None)
             assert rel_err(host(one), got[i]) <= 1e-5
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+GROUP_SMALLM_CASES = [(2, 64, 45, 4096), (3, 128, 70, 8192), (5, 128, 19, 28672), (5, 256, 33, 1024),
+                      (8, 64, 21, 16384), (5, 0, 40, 8288), (4, 0, 7, 96), (6, 256, 9, 131072 // 2)]
+
+
+@pytest.mark.parametrize("m,group,n,k", GROUP_SMALLM_CASES)
+def test_gemm_small_m_int4_groups(wq, m, group, n, k):
+    """m token rows through int4 weights with groups of 64/128/256 inputs or
+    one group per row (group 0 here: group = k), vs the oracle."""
+    from oracle.quant import quantize_int4
+    g = group or k
+    say(f"gemm_smallM_int4 m={m} group={g} n={n} k={k}")
+    w = host_normal((n, k), 0.015, 952, m, n, k)
+    p, sz = quantize_int4(w, g)
+    x = host_bf16_normal((m, k), 952, m, n, k + 1)
+    ref = gemm_small_m(x, p, sz)
+    (b32, y32), (b16, y16) = _outputs(n, m)
+    wq.wq_gemm_smallM_int4(dev(x), m, dev(p), dev(sz), n, k, g, y32, y16)
+    e = _compare(y32, y16, ref, (m, n))
+    _check_guards(b32, b16, m * n)
+    say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")

@@ -10,7 +10,7 @@ module itself imports without it.
 _EXPORTS = (
     "LIB_PATH", "WQError", "WQ_STATUS", "lib", "status_string", "last_error",
     "wq_quantize_int8", "wq_quantize_int4g32", "wq_quantize_int4",
-    "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32", "wq_gemv_int4", "wq_gemm_smallM", "wq_gemm_smallM_int8",
+    "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32", "wq_gemv_int4", "wq_gemm_smallM", "wq_gemm_smallM_int4", "wq_gemm_smallM_int8",
     "moe_top2_gemv",
     "WQ_FORMAT", "wq_matrix", "wq_step_plan",
     "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",

@@ -31,6 +31,7 @@ _SIGNATURES = {
     "wq_gemv_int4": [_P, _P, _P, _I64, _I64, _I32, _P, _P, _P],
     "wq_gemm_smallM": [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P],
     "wq_gemm_smallM_int8": [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P],
+    "wq_gemm_smallM_int4": [_P, _I64, _P, _P, _I64, _I64, _I32, _P, _P, _P],
     "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
 }
 
@@ -173,6 +174,12 @@ def wq_gemv_int4(x, qpacked, sz, n, k, group, y_f32=None, y_bf16=None, stream=No
 
 def wq_gemm_smallM(x, m, qpacked, sz, n, k, y_f32=None, y_bf16=None, stream=None):
     _call("wq_gemm_smallM", _ptr(x), m, _ptr(qpacked), _ptr(sz), n, k, _ptr(y_f32), _ptr(y_bf16),
+          _stream(stream))
+
+
+def wq_gemm_smallM_int4(x, m, qpacked, sz, n, k, group, y_f32=None, y_bf16=None, stream=None):
+    """m token rows x [m, k] through int4 weights with groups of `group` inputs -> y [m, n]."""
+    _call("wq_gemm_smallM_int4", _ptr(x), m, _ptr(qpacked), _ptr(sz), n, k, group, _ptr(y_f32), _ptr(y_bf16),
           _stream(stream))
 
 

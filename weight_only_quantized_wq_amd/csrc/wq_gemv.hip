@@ -256,6 +256,8 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   a.n = g.n;
   a.k = g.k;
   a.groups = (int32_t)(g.k / 32);
+  a.gshift = g.gshift;
+  a.words = int4_row_words(a.groups, g.gshift);
   a.blocks = (g.n + 16 * RT - 1) / (16 * RT);
   const int64_t grid = balanced_grid(a.blocks, resident);
   if (grid <= 0) return WQ_OK;
@@ -265,17 +267,17 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
 
 }  // namespace wq
 
-extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
-                              int64_t k, float* y_f32, uint16_t* y_bf16, void* stream) {
+static int gemm_small_m_int4(const char* name, const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
+                             int64_t n, int64_t k, int64_t group, float* y_f32, uint16_t* y_bf16, void* stream) {
   GemvArgs a;
-  int rc = int4_args("wq_gemm_smallM", x, qpacked, sz, n, k, y_f32, y_bf16, a, m);
+  int rc = int4_args(name, x, qpacked, sz, n, k, y_f32, y_bf16, a, m, group);
   if (rc) return rc;
   if (n == 0) return WQ_OK;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
   if (m >= 3) {
     if (k > kMfmaMaxK)
-      return fail(WQ_ERR_SHAPE, "wq_gemm_smallM: k = %lld is larger than %d", (long long)k, kMfmaMaxK);
+      return fail(WQ_ERR_SHAPE, "%s: k = %lld is larger than %d", name, (long long)k, kMfmaMaxK);
     switch (m) {
       case 3: return launch_mfma<3>(a, s);
       case 4: return launch_mfma<4>(a, s);
@@ -285,8 +287,18 @@ extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpack
       default: return launch_mfma<8>(a, s);
     }
   }
-  if (m == 2) return run_gemv<FmtInt4, 2>(a, s, "wq_gemm_smallM");
-  return run_gemv<FmtInt4, 1>(a, s, "wq_gemm_smallM");
+  if (m == 2) return run_gemv<FmtInt4, 2>(a, s, name);
+  return run_gemv<FmtInt4, 1>(a, s, name);
+}
+
+extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
+                              int64_t k, float* y_f32, uint16_t* y_bf16, void* stream) {
+  return gemm_small_m_int4("wq_gemm_smallM", x, m, qpacked, sz, n, k, 32, y_f32, y_bf16, stream);
+}
+
+extern "C" int wq_gemm_smallM_int4(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
+                                   int64_t k, int32_t group, float* y_f32, uint16_t* y_bf16, void* stream) {
+  return gemm_small_m_int4("wq_gemm_smallM_int4", x, m, qpacked, sz, n, k, group, y_f32, y_bf16, stream);
 }
 
 namespace wq {

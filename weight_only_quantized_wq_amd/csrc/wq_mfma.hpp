@@ -40,13 +40,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct MfmaArgs {
   const uint16_t* x;     // [m][k] bf16
   const uint8_t* w;      // [n][k/2]
-  const uint32_t* sz;    // [n][k/32]
+  const uint32_t* sz;    // [n][words]: group c >> gshift of 32-input chunk c
   float* y32;            // [m][n] or null
   uint16_t* y16;         // [m][n] or null
   int64_t n;
   int64_t k;
   int64_t blocks;        // ceil(n / (16 * RT))
-  int32_t groups;        // k / 32
+  int32_t groups;        // k / 32 (32-input chunks)
+  int32_t gshift;        // log2(G / 32) for groups of G inputs; a per-row group's shift exceeds any chunk index
+  int64_t words;         // (scale, zero) words per row
 };
 
 template <int M, int RT, int KW, int WAVES>
@@ -111,7 +113,7 @@ __device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t
     const uint32_t rows_ok = rows_left <= 0 ? 0u : (rows_left >= 16 ? 16u : (uint32_t)rows_left);
     const int64_t rb = rows_left > 0 ? rbase : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * (a.k / 2), rows_ok * row_bytes);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.groups, rows_ok * (uint32_t)a.groups * 4u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.words, rows_ok * (uint32_t)a.words * 4u);
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
       const int64_t g = gb + OCT * rq + o;
@@ -122,8 +124,9 @@ __device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t
       const int64_t ge = gb + OCT * slot + o;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t offs =
-            ge < a.groups ? ((uint32_t)(4 * rq + r) * (uint32_t)a.groups + (uint32_t)ge) * 4u : 0x80000000u;
+        const uint32_t offs = ge < a.groups
+                                  ? ((uint32_t)(4 * rq + r) * (uint32_t)a.words + (uint32_t)(ge >> a.gshift)) * 4u
+                                  : 0x80000000u;
         q.sz[rt][o][r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)offs, 0, 0);
       }
     }
@@ -181,6 +184,8 @@ __device__ __forceinline__ MfmaArgs uniform_args(const MfmaArgs& a) {
   u.k = uniform64(a.k);
   u.blocks = uniform64(a.blocks);
   u.groups = __builtin_amdgcn_readfirstlane(a.groups);
+  u.gshift = __builtin_amdgcn_readfirstlane(a.gshift);
+  u.words = uniform64(a.words);
   return u;
 }
 

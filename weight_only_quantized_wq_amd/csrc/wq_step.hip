@@ -129,7 +129,7 @@ static bool pick_variant(int format, int m, StepVariant& v) {
       case 5: v = verify_variant<5, 8, true, 2, 4, kVerifyKW, true>(); break;
       case 6: v = verify_variant<6, 8, true, 2, 4>(); break;
       case 7: v = verify_variant<7, 6, true, 2, 4>(); break;
-      case 8: v = verify_variant<8, 8, true, 2, 4, 192>(); break;
+      case 8: v = verify_variant<8, 8, true, 2, 4, 160, true>(); break;   // window of 160 groups leaves room for the tile
       default: return false;
     }
   } else {

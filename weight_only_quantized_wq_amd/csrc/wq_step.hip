@@ -80,21 +80,20 @@ constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 // launch refines it
 constexpr double kVerifyLongRowPrior = 1.2;
 
-template <int M, int WAVES, bool PF, int RT, int OCT, int KW, bool QL, bool SB, bool LT>
+template <int M, int WAVES, int RT, int OCT, int KW, bool LT>
 static void verify_launch(int grid, const StepLaunch& l, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB, LT>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, LT>), dim3((unsigned)grid),
                      dim3(WAVES * 64), 0, stream, l.mats, l.vcuts);
 }
 
 // LT: codes loaded line-wide and moved to the MFMA layout through a per-wave
 // LDS tile (2 KiB per wave on top of the activation window; fits up to 5
 // tokens), else quad-row loads and cross-lane permutes.
-template <int M, int WAVES, bool PF, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool LT = false>
+template <int M, int WAVES, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool LT = false>
 static StepVariant verify_variant() {
-  constexpr bool QL = true, SB = false;
   return StepVariant{1, WAVES, 16 * RT,
-                     reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, PF, QL, SB, LT>),
-                     &verify_launch<M, WAVES, PF, RT, OCT, KW, QL, SB, LT>, 0, true, KW};
+                     reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, LT>),
+                     &verify_launch<M, WAVES, RT, OCT, KW, LT>, 0, true, KW};
 }
 
 static bool is_int4(int format) {
@@ -123,13 +122,13 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     // 32-input chunk reading its group's (scale, zero) word
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
-      case 2: v = verify_variant<2, 8, true, 2, 4, 512, true>(); break;
-      case 3: v = verify_variant<3, 8, true, 2, 4, kVerifyKW, true>(); break;
-      case 4: v = verify_variant<4, 12, true, kVerifyRT, kVerifyOct, kVerifyKW, true>(); break;
-      case 5: v = verify_variant<5, 8, true, 2, 4, kVerifyKW, true>(); break;
-      case 6: v = verify_variant<6, 8, true, 2, 4>(); break;
-      case 7: v = verify_variant<7, 6, true, 2, 4>(); break;
-      case 8: v = verify_variant<8, 8, true, 2, 4, 160, true>(); break;   // window of 160 groups leaves room for the tile
+      case 2: v = verify_variant<2, 8, 2, 4, 512, true>(); break;
+      case 3: v = verify_variant<3, 8, 2, 4, kVerifyKW, true>(); break;
+      case 4: v = verify_variant<4, 12, kVerifyRT, kVerifyOct, kVerifyKW, true>(); break;
+      case 5: v = verify_variant<5, 8, 2, 4, kVerifyKW, true>(); break;
+      case 6: v = verify_variant<6, 8, 2, 4>(); break;
+      case 7: v = verify_variant<7, 6, 2, 4>(); break;
+      case 8: v = verify_variant<8, 8, 2, 4, 160, true>(); break;   // window of 160 groups leaves room for the tile
       default: return false;
     }
   } else {

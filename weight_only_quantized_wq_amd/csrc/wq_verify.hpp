@@ -112,20 +112,19 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
 // Loads the codes of item `it` of window [g0, ...) of block `blk` (tiles
 // RT blk .. RT blk + RT - 1): OCT quads of 4 consecutive groups (k-slot s of
 // quad o = group 4 o + s of the item) for the 16 rows of each tile, in one of
-// three layouts:
+// two layouts:
 //   * LT (line-wide; OCT even): load o reads rows 8 (o % 2) + lane / 8,
 //     group 8 (o / 2) + lane % 8 -- 128 contiguous bytes of each of 8 rows,
 //     the shape that streams at full rate -- and verify_item moves the codes
 //     to their MFMA lanes through a per-wave LDS tile;
-//   * QL: each quad of lanes reads ONE row (lane (row = lane / 4, k-slot =
-//     lane % 4)), 64 bytes of each of 16 rows per load, and verify_item moves
-//     each word to the MFMA lane (k-slot = lane / 16, row = lane % 16) with a
-//     cross-lane permute;
-//   * otherwise each lane loads its own MFMA chunk.
+//   * otherwise each quad of lanes reads ONE row (lane (row = lane / 4,
+//     k-slot = lane % 4)), 64 bytes of each of 16 rows per load, and
+//     verify_item moves each word to the MFMA lane (k-slot = lane / 16, row =
+//     lane % 16) with a cross-lane permute.
 // Rows past n and groups past the row read as zero, and so does everything
 // with !any: the loads are issued on every path, so code after a conditional
 // prefetch waits only for the item it consumes.
-template <int RT, int OCT, bool QL, bool LT>
+template <int RT, int OCT, bool LT>
 __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int g0, int it, int lane,
                                             VerifyItem<RT, OCT>& q, bool any = true) {
   static_assert(!LT || OCT % 2 == 0, "line-wide loads come in pairs");
@@ -143,8 +142,8 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * a.row_bytes, rows_ok * row_bytes);
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
-      const int lrow = LT ? 8 * (o & 1) + (lane >> 3) : (QL ? lane >> 2 : lane & 15);
-      const int g = LT ? g_item + 8 * (o >> 1) + (lane & 7) : g_item + 4 * o + (QL ? lane & 3 : lane >> 4);
+      const int lrow = LT ? 8 * (o & 1) + (lane >> 3) : lane >> 2;
+      const int g = LT ? g_item + 8 * (o >> 1) + (lane & 7) : g_item + 4 * o + (lane & 3);
       const bool ok = g < a.chunks;
       q.w[rt][o] = buffer_load16_nt(rw, ok ? (uint32_t)lrow * row_bytes + (uint32_t)g * 16u : 0x80000000u);
     }
@@ -243,13 +242,13 @@ __device__ __forceinline__ int verify_tile_at(int row, int slot) { return row * 
 // back its (row col, group 4 (o % 2) + rq) chunks of the two quads; the
 // wave's LDS accesses complete in order, so the next tile's stores never
 // overtake these reads.
-template <int M, int KW, int RT, int OCT, bool QL, bool SB, bool LT>
+template <int M, int KW, int RT, int OCT, bool LT>
 __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il, int iz, int gshift, int rq,
                                             int col, const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
                                             const FmtInt4::K& kc, uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
                                             float (&y)[RT][VerifyShared<M, KW>::kSets][4], uint8_t* tile) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
-  const int src = (4 * col + rq) * 4;   // byte address of the lane holding this lane's codes (QL)
+  const int src = (4 * col + rq) * 4;   // byte address of the lane holding this lane's codes (!LT)
   const int wr = rq * 2 + (col >> 3), ws = col & 7;   // LT store: row wr (+ 8), slot ws (lane = 16 rq + col)
   u32x4 wl[RT][2];
 #pragma unroll
@@ -275,7 +274,7 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
       u32x4 w = q.w[rt][o];
       if constexpr (LT) {
         w = wl[rt][o & 1];
-      } else if constexpr (QL) {
+      } else {
         w = u32x4{to_mfma_lane(w[0], src), to_mfma_lane(w[1], src), to_mfma_lane(w[2], src),
                   to_mfma_lane(w[3], src)};
       }
@@ -297,9 +296,6 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
           if (4 * st + r < M) y[rt][st][r] = fmaf(zb, xs4[st][r], fmaf(s, acc[r], y[rt][st][r]));
         }
       }
-      // SB: finish one chunk before the next is decoded, which bounds the
-      // registers in flight (the other waves of the CU hide the latency)
-      if constexpr (SB) __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -366,7 +362,7 @@ __device__ __forceinline__ void verify_fold(const GemvArgs& a, int64_t blk, int 
 // (verify_fold).  The next item's loads are issued before the current one is
 // reduced, across block boundaries too; the two item buffers alternate, so
 // no loaded value is copied (a copy would wait for the loads just issued).
-template <int M, int KW, int WAVES, int RT, int OCT, bool QL, bool SB, int SR, bool LT>
+template <int M, int KW, int WAVES, int RT, int OCT, int SR, bool LT>
 __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int64_t b1, int g0, int items,
                                               bool first, bool last, int* ctr, int lane, int rq, int col,
                                               const VerifyShared<M, KW>& sh, uint32_t (*szb)[16][kSzRow],
@@ -386,7 +382,7 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
   VerifyItem<RT, OCT> A, B;
   SzWindow<RT> Z;
   sz_load<RT>(a, b0 + bi, g0, lane, Z);   // first: it is consumed first
-  verify_load<RT, OCT, QL, LT>(a, b0 + bi, g0, 0, lane, A);
+  verify_load<RT, OCT, LT>(a, b0 + bi, g0, 0, lane, A);
   // consumes item (bi, it) from `cur` after requesting the next one into `nx`
   auto step = [&](const VerifyItem<RT, OCT>& cur, VerifyItem<RT, OCT>& nx) {
     if (it % IW == 0) {
@@ -403,9 +399,9 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
       i2 = 0;
     }
     more = b2 < nb;
-    verify_load<RT, OCT, QL, LT>(a, b0 + b2, g0, i2, lane, nx, more);
+    verify_load<RT, OCT, LT>(a, b0 + b2, g0, i2, lane, nx, more);
     if (more && i2 == 0) nxt = claim_batch(ctr, lane);
-    verify_item<M, KW, RT, OCT, QL, SB, LT>(cur, it * GI, (it % IW) * GI, a.gshift, rq, col, sh, szb, kc, av, y, tile);
+    verify_item<M, KW, RT, OCT, LT>(cur, it * GI, (it % IW) * GI, a.gshift, rq, col, sh, szb, kc, av, y, tile);
     if (it + 1 == items) verify_fold<M, RT, SETS, SR>(a, b0 + bi, (int)bi, first, last, rq, col, y, part);
     bi = b2;
     it = i2;
@@ -454,7 +450,7 @@ struct VerifyCuts {
 // mats: per-matrix descriptors (batch = one block of RT 16-row tiles;
 // `chunks` = groups per row).  Each workgroup cuts its own contiguous range
 // of the step's blocks from the cost prefixes and the balance factor.
-template <int M, int KW, int WAVES, int RT, int OCT, bool PF, bool QL, bool SB, bool LT>
+template <int M, int KW, int WAVES, int RT, int OCT, bool LT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const GemvArgs* __restrict__ mats,
                                                                       VerifyCuts cuts) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
@@ -558,7 +554,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
         verify_stage<M, KW, WAVES * 64>(a, g0, items * GI, sh);
         if (threadIdx.x == 0) ctr = 0;
         __syncthreads();
-        verify_window<M, KW, WAVES, RT, OCT, QL, SB, SR, LT>(a, r0, r1, g0, items, g0 == 0, g0 + KW >= groups, &ctr,
+        verify_window<M, KW, WAVES, RT, OCT, SR, LT>(a, r0, r1, g0, items, g0 == 0, g0 + KW >= groups, &ctr,
                                                          lane, rq, col, sh, szb, kc, av, y, part,
                                                          tiles[LT ? wave : 0]);
       }

@@ -85,7 +85,7 @@ struct FmtInt8 {
   static constexpr int kWeightsPerChunk = 16;
   static constexpr bool kGroupAux = false;
   static constexpr bool kRowScale = true;
-  static constexpr bool kLaneBias = true;
+  static constexpr bool kLaneBias = false;
   struct X {
     float v[16];
   };
@@ -117,19 +117,13 @@ struct FmtInt8 {
     }
     return r;
   }
-  // -128 * sum of the chunk's x: added once per row per lane
-  __device__ static float lane_bias(const X& x) {
-    float s = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += x.v[i];
-    return -128.0f * s;
-  }
+  __device__ static float lane_bias(const X&) { return 0.0f; }
 
   // Activations staged in LDS for a whole workgroup: 17 words per chunk over
   // `cmax` chunks, four 16-byte planes of fp32 values (plane h of chunk c at
-  // word 4 * (h * cmax + c)) followed by the chunk's bias, -128 times the sum
-  // of its 16 values (word 16 * cmax + c).  Chunks at or past `chunks` are
-  // zero.
+  // word 4 * (h * cmax + c)) followed by a bias word (word 16 * cmax + c;
+  // zero: the codes decode signed, so no per-row correction is needed).
+  // Chunks at or past `chunks` are zero.
   static constexpr int kLdsWordsPerChunk = 17;
   template <class T>
   __device__ static void stage(const T* x, int chunks, int c, uint32_t* xs, int cmax) {
@@ -157,18 +151,18 @@ struct FmtInt8 {
 
   struct K {};
   __device__ static K consts() { return K{}; }
-  // decoded chunk: u = q + 128 as fp32, one per weight
+  // decoded chunk: the codes q as fp32, one per weight (a sign-extending
+  // byte conversion each: v_cvt_f32_i32 with a sign-extended byte operand)
   struct D {
     float u[16];
   };
   __device__ static void decode(const u32x4& w, D& d, const K&) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      uint32_t u = w[t] ^ 0x80808080u;
-      d.u[4 * t] = (float)(u & 0xFFu);
-      d.u[4 * t + 1] = (float)((u >> 8) & 0xFFu);
-      d.u[4 * t + 2] = (float)((u >> 16) & 0xFFu);
-      d.u[4 * t + 3] = (float)(u >> 24);
+      d.u[4 * t] = (float)(int8_t)(w[t]);
+      d.u[4 * t + 1] = (float)(int8_t)(w[t] >> 8);
+      d.u[4 * t + 2] = (float)(int8_t)(w[t] >> 16);
+      d.u[4 * t + 3] = (float)(int8_t)(w[t] >> 24);
     }
   }
   __device__ static float dot(const D& d, uint32_t, const X& x, float acc) {

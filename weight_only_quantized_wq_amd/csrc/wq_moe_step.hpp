@@ -219,7 +219,8 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
     }
     __syncthreads();
     float bias = 0.0f;
-    for (int c = lane; c < passes * CPL * kWave; c += kWave) bias += FmtInt8::lds_bias(xs, CMAX, c);
+    if constexpr (FmtInt8::kLaneBias)
+      for (int c = lane; c < passes * CPL * kWave; c += kWave) bias += FmtInt8::lds_bias(xs, CMAX, c);
 
     // batch b: units j0 .. j0 + U - 1 of expert slot b / half
     auto rows = [&](int64_t b, const int8_t* (&base)[NR], bool (&ok)[NR]) {
@@ -309,9 +310,11 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerD
     if (threadIdx.x == 0) ctr = 0;
     __syncthreads();
     float bias[2] = {0.0f, 0.0f};
-    for (int c = lane; c < passes * CPL * kWave; c += kWave) {
-      bias[0] += FmtInt8::lds_bias(xs, CMAX, c);
-      bias[1] += FmtInt8::lds_bias(xs + PLANE, CMAX, c);
+    if constexpr (FmtInt8::kLaneBias) {
+      for (int c = lane; c < passes * CPL * kWave; c += kWave) {
+        bias[0] += FmtInt8::lds_bias(xs, CMAX, c);
+        bias[1] += FmtInt8::lds_bias(xs + PLANE, CMAX, c);
+      }
     }
 
     // batch b: output rows n0 .. n0 + U - 1, row n of expert a (rows 0..U-1)

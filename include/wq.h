@@ -173,8 +173,9 @@ int wq_gemm_smallM_int4(const uint16_t* x, int64_t m, const uint8_t* qpacked, co
  * [README] "Int8 仅权重量化".  x bf16 [m][k], 1 <= m <= 8; q, scale as written
  * by wq_quantize_int8; y [m][n] with y[t][r] = scale[r] * sum_k x[t][k] q[r][k];
  * row t of y equals wq_gemv_int8 applied to row t of x (to fp32 rounding).
- * Each weight is read once (m >= 2: on the matrix cores).  k % 16 == 0,
- * k <= 2^24, n * k <= 0xFFFFFF00.  scale 2-byte aligned.
+ * Each weight is read once (m >= 2: on the matrix cores).  k % 16 == 0;
+ * k <= 65536 for m == 1 (the one-token matvec), k <= 2^24 and
+ * n * k <= 0xFFFFFF00 for m >= 2.  scale 2-byte aligned.
  */
 int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q, const uint16_t* scale, int64_t n,
                         int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);

@@ -1,0 +1,113 @@
+"""Host logic of the benchmark and its profile summaries (CPU only).
+
+The roofline arithmetic, the traffic lookup's source-hash check, the
+counter calibration of the profile summaries, the algorithmic byte counts
+per format and the workloads' matrix sets -- none of which needs a GPU.
+"""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_roofline_takes_the_class_with_the_most_time():
+    import bench
+    launches = [("a", 0, 1000.0), ("a", 0, 1000.0), ("b", 0, 6000.0)]
+    dur = {"a": (0.001, [0, 1]), "b": (0.003, [2])}      # ms per launch: a 0.002 ms per step, b 0.003
+    dom, roof = bench.roofline(launches, dur)
+    assert dom == "b"
+    assert roof["achieved"] == pytest.approx(6000.0 / 3e-6 / 1e9, rel=1e-3)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / bench.HBM_PEAK_GBS, rel=1e-3)
+    assert roof["launches_per_step"] == 1 and roof["bound"] == "hbm"
+    assert roof["avg_launch_us"] == pytest.approx(3.0)
+    assert roof["all_kernels_gbs"] == pytest.approx(8000.0 / 5e-6 / 1e9, rel=1e-3)
+
+
+def test_traffic_is_reported_only_for_the_counted_sources(tmp_path, monkeypatch):
+    import bench
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps({"source_sha": "abc", "kernels": {"k": {"bytes_per_launch": 123}}}))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.traffic_for("k", "abc") == 123
+    assert bench.traffic_for("k", "abd") is None
+    assert bench.traffic_for("other", "abc") is None
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
+    assert bench.traffic_for("k", "abc") is None
+
+
+def _counter_csv(path, name, rows):
+    with open(path, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for kern, value in rows:
+            w.writerow({"Kernel_Name": kern, "Counter_Name": name, "Counter_Value": value})
+
+
+def test_traffic_summary_scales_counters_by_the_copy_kernel(tmp_path, monkeypatch):
+    import bench_profile
+    # the 1 GiB copy reads 0.5 GiB of FETCH_SIZE (scale 2) and 1 GiB of WRITE_SIZE (scale 1), in KiB
+    copy = "__amd_rocclr_copyBuffer"
+    kern = "void wq::some_kernel<1>(args)"
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", [(copy, 524288), (kern, 1000), (kern, 1002)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", [(copy, 1048576), (kern, 10), (kern, 10)])
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench_profile, "ROOT", str(tmp_path))
+    args = type("A", (), {})()
+    args.fetch, args.write, args.sha = str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "s1"
+    args.klass = ["cls=some_kernel<1>"]
+    args.cmd, args.title, args.out = ["c1", "c2"], "t", str(tmp_path / "profiles" / "x.md")
+    bench_profile.traffic(args)
+    doc = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
+    assert doc["source_sha"] == "s1"
+    assert doc["fetch_scale"] == pytest.approx(2.0) and doc["write_scale"] == pytest.approx(1.0)
+    e = doc["kernels"]["cls"]
+    assert e["fetch_bytes_per_launch"] == int(1001 * 1024 * 2.0)
+    assert e["write_bytes_per_launch"] == 10 * 1024
+    assert e["dispatches"] == 2
+
+
+@pytest.mark.parametrize("fmt,group", [("int4g32", 32), ("int4g64", 64), ("int4g128", 128), ("int4g256", 256),
+                                       ("int4pc", None), ("int8", None), ("bf16", None)])
+def test_weight_bytes_match_what_the_quantizers_write(fmt, group):
+    """The bench's byte count per format equals the sizes of the arrays the
+    (oracle) quantizers produce for that format."""
+    from weight_only_quantized_wq_amd.layerset import weight_bytes, matrix_bytes
+    from oracle.quant import quantize_int4, quantize_int8
+    n, k = 3, 512
+    w = np.zeros((n, k), np.float32)
+    if fmt.startswith("int4"):
+        p, sz = quantize_int4(w, group or k)
+        want = p.nbytes + sz.nbytes
+    elif fmt == "int8":
+        q, s = quantize_int8(w)
+        want = q.nbytes + s.nbytes
+    else:
+        want = 2 * n * k
+    assert weight_bytes(fmt, n, k) == want
+    assert matrix_bytes(fmt, n, k, m=5) == want + 2 * 5 * k + 2 * 5 * n
+
+
+def test_workload_matrix_sets():
+    from synth.workloads import WORKLOADS
+    assert len(WORKLOADS["llama2-7b-int4"].matrices()) == 32 * 4 + 1
+    assert len(WORKLOADS["llama3.1-70b-int4-m5"].matrices()) == 80 * 4 + 1
+    assert WORKLOADS["llama3.1-70b-int8-m5"].matrices() == WORKLOADS["llama3.1-70b-int4-m5"].matrices()
+    assert len(WORKLOADS["int8-4096"].matrices()) == 64
+    shapes = {(m.n, m.k) for m in WORKLOADS["llama2-7b-int4"].matrices()}
+    assert shapes == {(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)}

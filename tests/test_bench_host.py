@@ -28,15 +28,15 @@ def test_bench_refuses_more_than_one_gpu():
 
 def test_roofline_takes_the_class_with_the_most_time():
     import bench
-    launches = [("a", 0, 1000.0), ("a", 0, 1000.0), ("b", 0, 6000.0)]
-    dur = {"a": (0.001, [0, 1]), "b": (0.003, [2])}      # ms per launch: a 0.002 ms per step, b 0.003
+    launches = [("a", 0, 1e9), ("a", 0, 1e9), ("b", 0, 6e9)]
+    dur = {"a": (0.4, [0, 1]), "b": (1.0, [2])}      # ms per launch: a 0.8 ms per step, b 1.0 ms
     dom, roof = bench.roofline(launches, dur)
     assert dom == "b"
-    assert roof["achieved"] == pytest.approx(6000.0 / 3e-6 / 1e9, rel=1e-3)
-    assert roof["frac"] == pytest.approx(roof["achieved"] / bench.HBM_PEAK_GBS, rel=1e-3)
+    assert roof["achieved"] == pytest.approx(6000.0)          # 6 GB in 1 ms
+    assert roof["frac"] == pytest.approx(6000.0 / bench.HBM_PEAK_GBS)
     assert roof["launches_per_step"] == 1 and roof["bound"] == "hbm"
-    assert roof["avg_launch_us"] == pytest.approx(3.0)
-    assert roof["all_kernels_gbs"] == pytest.approx(8000.0 / 5e-6 / 1e9, rel=1e-3)
+    assert roof["avg_launch_us"] == pytest.approx(1000.0)
+    assert roof["all_kernels_gbs"] == pytest.approx(8e9 / 1.8e-3 / 1e9, abs=0.1)
 
 
 def test_traffic_is_reported_only_for_the_counted_sources(tmp_path, monkeypatch):

@@ -1,11 +1,12 @@
 """HIP graph capture of decode-step launches: every replay must reproduce the
 eager result bitwise, with the program's own eager work and synchronisations
-between replays (bf16, int8, int4 and 5-token int4 sets, and a MoE layer)."""
+between replays (bf16, int8, int4 at several group sizes, 3- and 5-token
+int4 and int8 sets, one launch per matrix, and a MoE layer)."""
 
 import numpy as np
 import pytest
 
-from gpu_util import say
+from gpu_util import say, TOL_BF16
 from synth.configs import Matrix
 from synth.workloads import Workload, gen_w_device, gen_x_device
 from synth.gen import device_normal, device_bf16_normal
@@ -23,7 +24,8 @@ def _capture(fn):
     return g
 
 
-@pytest.mark.parametrize("fmt,m", [("bf16", 1), ("int8", 1), ("int4g32", 1), ("int4g32", 5)])
+@pytest.mark.parametrize("fmt,m", [("bf16", 1), ("int8", 1), ("int4g32", 1), ("int4g32", 5), ("int8", 5),
+                                   ("int4g128", 1), ("int4g128", 5), ("int4pc", 3)])
 def test_layerset_graph_replays_match_eager(fmt, m):
     import torch
     from weight_only_quantized_wq_amd.layerset import LayerSet
@@ -34,6 +36,15 @@ def test_layerset_graph_replays_match_eager(fmt, m):
     ls.step()
     torch.cuda.synchronize()
     want = [q.y16.clone() for q in ls.mats]
+    # the per-matrix calls agree with the fused step (parity-tested against
+    # the oracle) to bf16 output rounding: same format, group size and token rows
+    ls.prepare_fused()
+    ls.step_fused()
+    torch.cuda.synchronize()
+    for q, w in zip(ls.mats, want):
+        a = w.view(torch.bfloat16).float()
+        b = q.y16.view(torch.bfloat16).float()
+        assert float((a - b).abs().max() / b.abs().max()) <= TOL_BF16, f"{q.n}x{q.k}: per-matrix and fused differ"
     g = _capture(ls.step)
     junk = torch.randn(1 << 20, device="cuda")
     for rep in range(4):

@@ -82,7 +82,8 @@ class QuantMatrix:
         elif self.m == 1:
             wq.wq_gemv_int4(self.x, self.w, self.aux, self.n, self.k, int4_group(self.fmt, self.k), y32, y16, stream)
         else:
-            wq.wq_gemm_smallM(self.x, self.m, self.w, self.aux, self.n, self.k, y32, y16, stream)
+            wq.wq_gemm_smallM_int4(self.x, self.m, self.w, self.aux, self.n, self.k, int4_group(self.fmt, self.k),
+                                   y32, y16, stream)
 
 
 class LayerSet:

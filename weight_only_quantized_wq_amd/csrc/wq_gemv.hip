@@ -244,8 +244,9 @@ namespace wq {
 template <int M>
 int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   constexpr int RT = kMfmaRT, KW = kMfmaKW, WAVES = kMfmaWaves, PF = kMfmaPF, OCT = kMfmaOct;
+  constexpr bool LT = M <= 7;   // the code tile fits beside the activation window
   static int resident = 0;
-  auto kern = gemm_mfma_kernel<M, RT, KW, WAVES, PF, OCT>;
+  auto kern = gemm_mfma_kernel<M, RT, KW, WAVES, PF, OCT, LT>;
   if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
   MfmaArgs a{};
   a.x = g.x;

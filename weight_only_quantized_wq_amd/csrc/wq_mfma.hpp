@@ -72,6 +72,11 @@ __device__ __forceinline__ f32x4 mfma_bf16(const uint32_t (&a)[4], const uint32_
                                                  0, 0, 0);
 }
 
+// Byte offset of 16-byte slot `slot` of row `row` in a 16-row x 128-byte
+// LDS tile: slots XOR-swizzled by row pair, so 16 lanes storing two rows of
+// 8 slots, or reading one slot of 16 rows, touch distinct banks.
+__device__ __forceinline__ int mfma_tile_at(int row, int slot) { return row * 128 + ((slot ^ ((row >> 1) & 7)) << 4); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -102,9 +107,14 @@ struct ItemData {
   uint32_t sz[RT][OCT][4];
 };
 
-template <int RT, int OCT>
+// LT (line-wide, OCT = 2): the item's codes are read as two loads of 8 rows
+// x 128 bytes per tile (lane l: row l / 8 (+ 8), group gb + l % 8) and reach
+// the layout above through a per-wave LDS tile (mfma_blocks).
+template <int RT, int OCT, bool LT>
 __device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t gb, int rq, int col, int slot,
                                           ItemData<RT, OCT>& q) {
+  static_assert(!LT || OCT == 2, "a line-wide item is 8 groups of 16 rows");
+  const int lane = 16 * rq + col;
   const uint32_t row_bytes = (uint32_t)(a.k / 2);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -116,8 +126,9 @@ __device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rb * a.words, rows_ok * (uint32_t)a.words * 4u);
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
-      const int64_t g = gb + OCT * rq + o;
-      q.w[rt][o] = buffer_load16_nt(rw, g < a.groups ? (uint32_t)col * row_bytes + (uint32_t)g * 16u : 0x80000000u);
+      const int64_t g = LT ? gb + (lane & 7) : gb + OCT * rq + o;
+      const uint32_t row = LT ? (uint32_t)(8 * o + (lane >> 3)) : (uint32_t)col;
+      q.w[rt][o] = buffer_load16_nt(rw, g < a.groups ? row * row_bytes + (uint32_t)g * 16u : 0x80000000u);
     }
 #pragma unroll
     for (int o = 0; o < OCT; ++o) {
@@ -189,9 +200,9 @@ __device__ __forceinline__ MfmaArgs uniform_args(const MfmaArgs& a) {
   return u;
 }
 
-template <int M, int RT, int KW, int WAVES, int PF, int OCT>
+template <int M, int RT, int KW, int WAVES, int PF, int OCT, bool LT>
 __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_first, int64_t b_end, int64_t b_step,
-                                            MfmaShared<M, RT, KW, WAVES>& sh) {
+                                            MfmaShared<M, RT, KW, WAVES>& sh, uint8_t* tile) {
   constexpr int SETS = (M + 3) / 4;
   const MfmaArgs a = uniform_args(a_in);
   b_first = uniform64(b_first);
@@ -212,7 +223,7 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
   bool pending = false;
   if (PF && pblk < b_end) {
     pending = next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
-    if (pending) load_item<RT, OCT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
+    if (pending) load_item<RT, OCT, LT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
   }
   bool staged = false;
   uint32_t bop[SETS][4][4];          // B operands of the current quad (see below)
@@ -248,9 +259,24 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
         if (PF) {
           cur = nxt;
           pending = next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
-          if (pending) load_item<RT, OCT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
+          if (pending) load_item<RT, OCT, LT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
         } else {
-          load_item<RT, OCT>(a, n0, gb, rq, col, slot, cur);
+          load_item<RT, OCT, LT>(a, n0, gb, rq, col, slot, cur);
+        }
+        // LT: each tile's 16 rows x 8 groups pass through the wave's LDS
+        // tile (slots XOR-swizzled by row pair; the wave's LDS accesses
+        // complete in order, so the next tile's stores follow these reads);
+        // lane (rq, col) reads back groups OCT rq + o of row col
+        u32x4 wl[RT][OCT];
+        if constexpr (LT) {
+          const int lane = 16 * rq + col, wr = lane >> 3, ws = lane & 7;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            *reinterpret_cast<u32x4*>(tile + mfma_tile_at(wr, ws)) = cur.w[rt][0];
+            *reinterpret_cast<u32x4*>(tile + mfma_tile_at(wr + 8, ws)) = cur.w[rt][1];
+#pragma unroll
+            for (int o = 0; o < OCT; ++o) wl[rt][o] = *reinterpret_cast<const u32x4*>(tile + mfma_tile_at(col, OCT * rq + o));
+          }
         }
 #pragma unroll
         for (int o = 0; o < OCT; ++o) {
@@ -275,7 +301,7 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
             FmtInt4::D d;
-            FmtInt4::decode(cur.w[rt][o], d, kc);
+            FmtInt4::decode(LT ? wl[rt][o] : cur.w[rt][o], d, kc);
 #pragma unroll
             for (int s = 0; s < SETS; ++s) {
               f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -331,11 +357,14 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
 }
 
 // One matrix: workgroups take blocks blockIdx.x, blockIdx.x + gridDim.x, ...
-template <int M, int RT, int KW, int WAVES, int PF, int OCT>
+// LT: line-wide code loads through a 2 KiB LDS tile per wave (fits beside
+// the activation window up to 7 tokens).
+template <int M, int RT, int KW, int WAVES, int PF, int OCT, bool LT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_mfma_kernel(MfmaArgs a) {
   __shared__ MfmaShared<M, RT, KW, WAVES> sh;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[LT ? WAVES : 1][LT ? 16 * 128 : 16];
   if (threadIdx.x < 16) sh.zero[threadIdx.x] = 0u;
-  mfma_blocks<M, RT, KW, WAVES, PF, OCT>(a, blockIdx.x, a.blocks, gridDim.x, sh);
+  mfma_blocks<M, RT, KW, WAVES, PF, OCT, LT>(a, blockIdx.x, a.blocks, gridDim.x, sh, tiles[LT ? threadIdx.x >> 6 : 0]);
 }
 
 }  // namespace wq

@@ -229,7 +229,9 @@ def test_gemv_int4_per_row(wq, n, k):
 
 
 I8M_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 16), (70, 8192)]] + \
-    [(m, 19, 28672) for m in (2, 5, 8)] + [(5, 300, 4112), (3, 17, 57344), (8, 5, 1 << 17), (5, 7, 0)]
+    [(m, 19, 28672) for m in (2, 5, 8)] + [(5, 300, 4112), (3, 17, 57344), (8, 5, 1 << 17), (5, 7, 0),
+    (5, 16411, 272), (2, 16448, 1024), (8, 20000, 528), (4, 16384, 0),
+    (8, 8200, 16400), (3, 9000, 16384)]
 
 
 @pytest.mark.parametrize("m,n,k", I8M_CASES)

@@ -309,18 +309,31 @@ namespace wq {
 constexpr int kI8mWaves = 8;
 constexpr int64_t kI8mMaxBytes = (int64_t)0xFFFFFF00u;   // codes addressed with 32-bit offsets
 
-template <int M>
-int launch_i8m(GemvArgs a, hipStream_t stream) {
+// U tiles per batch share each activation load.  Fewer tiles per batch
+// keep more batches in the grid: 4 from kI8mWideRows rows on; 2 from
+// kI8mMidRows rows on when the matrix holds at least kI8mMidBytes (rows
+// long enough that one batch per CU streams for a while); else 1.
+constexpr int64_t kI8mWideRows = 16384, kI8mMidRows = 8192, kI8mMidBytes = int64_t(1) << 27;
+
+template <int M, int U>
+int launch_i8m_u(GemvArgs a, hipStream_t stream) {
   static int resident = 0;
-  auto kern = gemm_i8_smallm_kernel<M, kI8mWaves>;
+  auto kern = gemm_i8_smallm_kernel<M, U, kI8mWaves>;
   if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
   const int64_t chunks = a.k / 16, per_pass = kMtPassChunks;
   a.cpl = (int32_t)((chunks + per_pass - 1) / per_pass);
-  a.batches = (a.n + 15) / 16;
+  a.batches = (a.n + 16 * U - 1) / (16 * U);
   const int64_t grid = balanced_grid(a.batches, resident);
   if (grid <= 0) return WQ_OK;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kI8mWaves * kWave), 0, stream, a);
   return launch_status("wq_gemm_smallM_int8");
+}
+
+template <int M>
+int launch_i8m(const GemvArgs& a, hipStream_t stream) {
+  if (a.n >= kI8mWideRows) return launch_i8m_u<M, 4>(a, stream);
+  if (a.n >= kI8mMidRows && a.n * a.k >= kI8mMidBytes) return launch_i8m_u<M, 2>(a, stream);
+  return launch_i8m_u<M, 1>(a, stream);
 }
 
 }  // namespace wq

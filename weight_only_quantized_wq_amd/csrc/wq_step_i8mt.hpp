@@ -226,50 +226,57 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_i8_step_kernel(const GemvArgs
   });
 }
 
-// One matrix (wq_gemm_smallM_int8): workgroup b takes tiles b, b + grid, ...
-// (batches of one 16-row tile); its waves split the tile's passes (wave w:
-// passes w, w + WAVES, ...), and their sums meet in LDS, added in wave order,
-// so results do not depend on timing.
-template <int M, int WAVES>
+// One matrix (wq_gemm_smallM_int8): workgroup b takes batches b, b + grid,
+// ... of U 16-row tiles (one activation load serves the U tiles); its waves
+// split the batch's passes (wave w: passes w, w + WAVES, ...), and their sums
+// meet in LDS, added in wave order, so results do not depend on timing.
+template <int M, int U, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemm_i8_smallm_kernel(GemvArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[WAVES][kMtTileLds];
-  __shared__ f32x4 red[WAVES][kWave];
+  __shared__ f32x4 red[WAVES][U][kWave];
   const int lane = lane_id();
   const int wave = (int)(threadIdx.x >> 6);
   uint8_t* lds = tiles[wave];
   const int passes = a.cpl;
   for (int64_t batch = blockIdx.x; batch < a.batches; batch += gridDim.x) {
-    f32x4 acc[1] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
-    MtPassBuf<1> A, B;
+    f32x4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    MtPassBuf<U> A, B;
     int p = wave;
-    mt_load_pass<M, 1>(a, batch, p, lane, A, p < passes);
+    mt_load_pass<M, U>(a, batch, p, lane, A, p < passes);
     for (;;) {
       p += WAVES;
       bool more = p < passes;
-      mt_load_pass<M, 1>(a, batch, p, lane, B, more);
-      mt_accumulate<1>(A, acc, lds, lane);
+      mt_load_pass<M, U>(a, batch, p, lane, B, more);
+      mt_accumulate<U>(A, acc, lds, lane);
       if (!more) {
         wait_vmem_all();
         break;
       }
       p += WAVES;
       more = p < passes;
-      mt_load_pass<M, 1>(a, batch, p, lane, A, more);
-      mt_accumulate<1>(B, acc, lds, lane);
+      mt_load_pass<M, U>(a, batch, p, lane, A, more);
+      mt_accumulate<U>(B, acc, lds, lane);
       if (!more) {
         wait_vmem_all();
         break;
       }
     }
-    red[wave][lane] = acc[0];
+#pragma unroll
+    for (int u = 0; u < U; ++u) red[wave][u][lane] = acc[u];
     __syncthreads();
     if (wave == 0) {
-      f32x4 tot[1] = {red[0][lane]};
+      f32x4 tot[U];
 #pragma unroll
-      for (int w = 1; w < WAVES; ++w) tot[0] += red[w][lane];
-      int64_t rs = batch * 16 + (lane < 16 ? lane : 0);
+      for (int u = 0; u < U; ++u) {
+        tot[u] = red[0][u][lane];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) tot[u] += red[w][u][lane];
+      }
+      int64_t rs = batch * 16 * U + (lane < 16 * U ? lane : 0);
       if (rs >= a.n) rs = a.n - 1;
-      mt_store<M, 1>(a, batch, lane, tot, (uint32_t)*gmem(a.scale + rs));
+      mt_store<M, U>(a, batch, lane, tot, (uint32_t)*gmem(a.scale + rs));
     }
     __syncthreads();
   }

@@ -128,10 +128,12 @@ def test_gemv_int4g32(wq, n, k):
 
 
 # m >= 3 runs on the matrix cores with K windows of 256 groups: the cases
-# cover one window, several, and a ragged last window (k = 8288, 12352)
+# cover one window, several, a ragged last window (k = 8288, 12352, 8224),
+# matrices with more row blocks than resident workgroups, and k = 0
 SMALLM_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 32), (70, 8192)]] + \
     [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 3, 4, 5, 7, 8)] + \
-    [(5, 8, 32768), (1, 10, 131072), (5, 6, 131072), (5, 50, 8288), (7, 37, 12352), (3, 100, 8224)]
+    [(5, 8, 32768), (1, 10, 131072), (5, 6, 131072), (5, 50, 8288), (7, 37, 12352), (3, 100, 8224),
+    (2, 9, 0), (6, 9, 0), (5, 16411, 512), (3, 18000, 8224), (8, 17000, 4128), (2, 20000, 16416)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALLM_CASES)
@@ -142,7 +144,7 @@ def test_gemm_small_m(wq, m, n, k):
     x = host_bf16_normal((m, k), 950, m, n, k + 1)
     ref = gemm_small_m(x, p, sz)
     (b32, y32), (b16, y16) = _outputs(n, m)
-    pd, szd, xd = dev(p), dev(sz), dev(x)
+    pd, szd, xd = _d(p), _d(sz), _d(x)
     wq.wq_gemm_smallM(xd, m, pd, szd, n, k, y32, y16)
     e = _compare(y32, y16, ref, (m, n))
     _check_guards(b32, b16, m * n)
@@ -151,7 +153,7 @@ def test_gemm_small_m(wq, m, n, k):
     one = torch.empty(n, dtype=torch.float32, device="cuda")
     got = host(y32).reshape(m, n)
     for i in range(m):
-        wq.wq_gemv_int4g32(xd[i * k:(i + 1) * k] if xd.dim() == 1 else xd[i], pd, szd, n, k, one, None)
+        wq.wq_gemv_int4g32(xd if k == 0 else xd[i], pd, szd, n, k, one, None)
         assert rel_err(host(one), got[i]) <= 1e-5
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 

@@ -22,7 +22,8 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every buffer is DEVICE memory owned by the caller.  The library allocates
- *   nothing and keeps no state besides a thread-local error text.  Passing a
+ *   nothing.  Its only state: a thread-local error text and per-device host
+ *   caches (device check, occupancy; safe across host threads).  Passing a
  *   host pointer is outside the contract (the kernel would fault).
  * - Row-major layouts; bf16 values are passed as their uint16 bit patterns.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work

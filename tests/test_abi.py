@@ -208,3 +208,81 @@ def test_moe_step_plan_errors_before_any_device_work(wq):
     junk = wq_moe_plan(64, 64, 4, 1, 1, 1, BAD)
     assert lib.wq_moe_step_run(ctypes.byref(junk), None) == 2
     assert wq.wq_moe_step_workspace_bytes(32) >= 32 * 88
+
+
+def test_binding_checks_buffer_extents(wq):
+    """The binding refuses a tensor shorter than the sizes imply (the kernels
+    would access past it), naming the buffer, before the C call; a tensor of
+    the right extent passes that check and stops at the device check."""
+    import torch
+    n, k = 8, 64
+    x = torch.zeros(k, dtype=torch.int16)
+    short = torch.zeros(k - 1, dtype=torch.int16)
+    q = torch.zeros(n * k, dtype=torch.int8)
+    s = torch.zeros(n, dtype=torch.int16)
+    y = torch.zeros(n, dtype=torch.float32)
+    with pytest.raises(ValueError, match="x holds 126 bytes"):
+        wq.wq_gemv_int8(short, q, s, n, k, y, stream=0)
+    with pytest.raises(ValueError, match="q holds"):
+        wq.wq_gemv_int8(x, q[:-1], s, n, k, y, stream=0)
+    with pytest.raises(ValueError, match="y_f32 holds"):
+        wq.wq_gemv_int8(x, q, s, n, k, y[:-1], stream=0)
+    with pytest.raises(ValueError, match="must be GPU tensors"):
+        wq.wq_gemv_int8(x, q, s, n, k, y, stream=0)
+    # int4: the (scale, zero) words follow the group size
+    p = torch.zeros(n * k // 2, dtype=torch.uint8)
+    sz = torch.zeros(n * (k // 32) * 2, dtype=torch.int16)
+    with pytest.raises(ValueError, match="sz holds"):
+        wq.wq_gemv_int4(x, p, sz[:-1], n, k, 32, y, stream=0)
+    with pytest.raises(ValueError, match="must be GPU tensors"):
+        wq.wq_gemv_int4(x, p, sz[: n * (k // 64) * 2], n, k, 64, y, stream=0)
+    # m token rows
+    with pytest.raises(ValueError, match="x holds"):
+        wq.wq_gemm_smallM(torch.zeros(4 * k, dtype=torch.int16), 5, p, sz, n, k, y, stream=0)
+    with pytest.raises(ValueError, match="y_bf16 holds"):
+        wq.wq_gemm_smallM_int8(torch.zeros(5 * k, dtype=torch.int16), 5, q, s, n, k, None,
+                               torch.zeros(5 * n - 1, dtype=torch.int16), stream=0)
+    # decode-step matrices are checked one by one
+    with pytest.raises(ValueError, match="matrix 1 w holds"):
+        wq.wq_decode_step_prepare("int8", 1, [(x, q, s, n, k, y, None), (x, q[:-1], s, n, k, y, None)],
+                                  torch.zeros(1 << 12, dtype=torch.uint8))
+    # MoE layer: expert stacks
+    dim, f = 32, 48
+    with pytest.raises(ValueError, match="w13 holds"):
+        wq.moe_top2_gemv(torch.zeros(dim, dtype=torch.int16), torch.zeros(8), 8,
+                         torch.zeros(8 * 2 * f * dim - 1, dtype=torch.int8), torch.zeros(16 * f, dtype=torch.int16),
+                         torch.zeros(8 * dim * f, dtype=torch.int8), torch.zeros(8 * dim, dtype=torch.int16),
+                         dim, f, torch.zeros(2 * f), torch.zeros(dim), stream=0)
+
+
+def test_argument_errors_from_many_threads(wq):
+    """Host-side checks and the per-thread error text under concurrent calls:
+    every thread sees its own status and detail (the caches behind the
+    checks are shared and must not race)."""
+    import threading
+    lib = wq._binding.lib
+    errors = []
+
+    def worker(i):
+        try:
+            for r in range(300):
+                kk = 48 + 32 * ((i + r) % 5)           # never a multiple of 32 when odd multiple of 16
+                rc = lib.wq_gemv_int4g32(BAD, BAD, BAD, 4, kk if kk % 32 else kk + 16, BAD, None, None)
+                if rc != 2 or b"not a multiple of 32" not in lib.wq_last_error():
+                    errors.append((i, r, rc, lib.wq_last_error()))
+                rc = lib.wq_gemv_bf16(0x2000, BAD, 0, 64, 0x2000, None, None)
+                if rc != 3 or b"aligned" not in lib.wq_last_error():
+                    errors.append((i, r, rc, lib.wq_last_error()))
+                rc = lib.moe_top2_gemv(BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 40 + 16 * i, BAD, BAD, None, None,
+                                       None, None)
+                if rc != 2 or str(40 + 16 * i).encode() not in lib.wq_last_error():
+                    errors.append((i, r, rc, lib.wq_last_error()))
+        except Exception as e:       # pragma: no cover - reported below
+            errors.append((i, repr(e)))
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors[:4]

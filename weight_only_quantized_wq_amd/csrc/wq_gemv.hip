@@ -19,14 +19,12 @@ using LaunchFn = int (*)(const GemvArgs&, int split, hipStream_t);
 
 template <class F, int M, int CPL, int U, int WAVES, bool PF>
 int launch_one(const GemvArgs& a0, int split, hipStream_t stream) {
-  static int resident_by_split[WAVES + 1] = {0};
   auto kern = gemv_kernel<F, M, CPL, U, WAVES, PF>;
   GemvArgs a = a0;
   a.split = split;
   a.groups = WAVES / split;
   const int threads = split * a.groups * kWave;
-  int& resident = resident_by_split[split];
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
   const int64_t rows_per_batch = (int64_t)a.groups * U;
   a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
   int64_t grid = balanced_grid(a.batches, resident);
@@ -245,9 +243,8 @@ template <int M>
 int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   constexpr int RT = kMfmaRT, KW = kMfmaKW, WAVES = kMfmaWaves, PF = kMfmaPF, OCT = kMfmaOct;
   constexpr bool LT = M <= 7;   // the code tile fits beside the activation window
-  static int resident = 0;
   auto kern = gemm_mfma_kernel<M, RT, KW, WAVES, PF, OCT, LT>;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
   MfmaArgs a{};
   a.x = g.x;
   a.w = g.w;
@@ -317,9 +314,8 @@ constexpr int64_t kI8mWideRows = 16384, kI8mMidRows = 8192, kI8mMidBytes = int64
 
 template <int M, int U>
 int launch_i8m_u(GemvArgs a, hipStream_t stream) {
-  static int resident = 0;
   auto kern = gemm_i8_smallm_kernel<M, U, kI8mWaves>;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
   const int64_t chunks = a.k / 16, per_pass = kMtPassChunks;
   a.cpl = (int32_t)((chunks + per_pass - 1) / per_pass);
   a.batches = (a.n + 16 * U - 1) / (16 * U);

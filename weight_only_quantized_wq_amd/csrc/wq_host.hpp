@@ -13,7 +13,7 @@ namespace wq {
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
 // WQ_OK when the current device is a gfx950; otherwise WQ_ERR_DEVICE with
-// the detail recorded.  The answer is cached per device id.
+// the detail recorded.  The answer is cached per device id (thread-safe).
 int check_device();
 
 // Maps the state after a launch to WQ_OK / WQ_ERR_LAUNCH.
@@ -21,8 +21,12 @@ int launch_status(const char* what);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Number of workgroups a kernel can keep resident on the whole device at the
-// given block size (occupancy query, cached by the caller).
+// Devices the per-device host caches track (device ids 0 .. kMaxDevices-1).
+constexpr int kMaxDevices = 64;
+
+// Number of workgroups a kernel can keep resident on the whole current
+// device at the given block size (occupancy query, cached per device,
+// kernel and block size; safe to call from several host threads).
 int resident_groups(const void* kernel, int block_threads);
 
 // Balanced grid: the fewest workgroups that still fill `resident` slots,

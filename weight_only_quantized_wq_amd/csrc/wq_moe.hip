@@ -23,8 +23,8 @@ namespace wq {
 // Host side
 
 template <class K>
-static int launch_grid(K kern, const MoeArgs& a, int threads, hipStream_t stream, int& resident) {
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
+static int launch_grid(K kern, const MoeArgs& a, int threads, hipStream_t stream) {
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), threads);
   int64_t grid = balanced_grid(a.batches, resident);
   if (grid <= 0) return WQ_OK;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), 0, stream, a);
@@ -41,14 +41,12 @@ static int launch_w13(MoeArgs a, hipStream_t stream) {
     a.split = (int)s;
     a.groups = 4 / (int)s;
     a.batches = (2 * a.f + a.groups - 1) / a.groups;
-    static int res = 0;
-    return launch_grid(moe_w13_kernel<4, 4, false>, a, a.split * a.groups * kWave, stream, res);
+    return launch_grid(moe_w13_kernel<4, 4, false>, a, a.split * a.groups * kWave, stream);
   }
   a.split = (int)s;
   a.groups = 8 / (int)s;
   a.batches = (2 * a.f + a.groups - 1) / a.groups;
-  static int res = 0;
-  return launch_grid(moe_w13_kernel<4, 8, false>, a, a.split * a.groups * kWave, stream, res);
+  return launch_grid(moe_w13_kernel<4, 8, false>, a, a.split * a.groups * kWave, stream);
 }
 
 // W2 plans: two teams of `split` waves; chunks per lane 7 (two waves per
@@ -64,16 +62,14 @@ static int launch_w2(MoeArgs a, hipStream_t stream) {
     a.split = (int)(s7 < 1 ? 1 : s7);
     a.groups = 2;
     a.batches = a.dim;
-    static int res = 0;
-    return launch_grid(moe_w2_kernel<7, 4, 1, true>, a, 2 * a.split * kWave, stream, res);
+    return launch_grid(moe_w2_kernel<7, 4, 1, true>, a, 2 * a.split * kWave, stream);
   }
   if (s4 <= 8) {
     constexpr int U = 2;
     a.split = (int)(s4 < 1 ? 1 : s4);
     a.groups = 2;
     a.batches = (a.dim + U - 1) / U;
-    static int res = 0;
-    return launch_grid(moe_w2_kernel<4, 16, U, false>, a, 2 * a.split * kWave, stream, res);
+    return launch_grid(moe_w2_kernel<4, 16, U, false>, a, 2 * a.split * kWave, stream);
   }
   return fail(WQ_ERR_SHAPE, "moe_top2_gemv: f = %lld too large", (long long)a.f);
 }
@@ -82,22 +78,31 @@ static int launch_w2(MoeArgs a, hipStream_t stream) {
 
 using namespace wq;
 
-extern "C" int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
-                             const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim, int64_t f,
-                             float* work, float* y_f32, uint16_t* y_bf16, int32_t* sel, float* gates,
-                             void* stream) {
-  const char* name = "moe_top2_gemv";
-  if (!x || !logits || !w13 || !s13 || !w2 || !s2 || !work)
-    return fail(WQ_ERR_NULL, "%s: x, logits, w13, s13, w2, s2 and work must be non-null", name);
+// Argument checks shared by both entry points (null -> sizes -> alignment,
+// then the device).  `work` is checked only when the caller brings it.
+static int moe_check(const char* name, const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
+                     const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim, int64_t f,
+                     const float* work, bool need_work, const float* y_f32, const uint16_t* y_bf16,
+                     int64_t max_f) {
+  if (!x || !logits || !w13 || !s13 || !w2 || !s2 || (need_work && !work))
+    return fail(WQ_ERR_NULL, "%s: x, logits, w13, s13, w2, s2%s must be non-null", name,
+                need_work ? " and work" : "");
   if (!y_f32 && !y_bf16) return fail(WQ_ERR_NULL, "%s: at least one of y_f32 / y_bf16 must be non-null", name);
   if (e != 8) return fail(WQ_ERR_SHAPE, "%s: e = %lld; only 8 experts (top-2) are supported", name, (long long)e);
   if (dim < 16 || f < 16 || dim % 16 || f % 16 || dim > 32768 || f > 32768)
     return fail(WQ_ERR_SHAPE, "%s: dim = %lld, f = %lld must be multiples of 16 in [16, 32768]", name,
                 (long long)dim, (long long)f);
-  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || !aligned16(work))
-    return fail(WQ_ERR_ALIGN, "%s: x, w13, w2 and work must be 16-byte aligned", name);
-  int rc = check_device();
-  if (rc) return rc;
+  if (f > max_f)
+    return fail(WQ_ERR_SHAPE, "%s: f = %lld exceeds this entry point's limit of %lld", name,
+                (long long)f, (long long)max_f);
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || (need_work && !aligned16(work)))
+    return fail(WQ_ERR_ALIGN, "%s: x, w13, w2%s must be 16-byte aligned", name, need_work ? " and work" : "");
+  return check_device();
+}
+
+static int moe_launch(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13, const uint16_t* s13,
+                      const int8_t* w2, const uint16_t* s2, int64_t dim, int64_t f, float* work, float* y_f32,
+                      uint16_t* y_bf16, int32_t* sel, float* gates, void* stream) {
   MoeArgs a{};
   a.x = x;
   a.logits = logits;
@@ -115,7 +120,17 @@ extern "C" int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, 
   a.e = (int32_t)e;
   hipStream_t s = (hipStream_t)stream;
   a.chunks = (int32_t)(dim / 16);
-  if ((rc = launch_w13(a, s))) return rc;
+  int rc = launch_w13(a, s);
+  if (rc) return rc;
   a.chunks = (int32_t)(f / 16);
   return launch_w2(a, s);
+}
+
+extern "C" int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
+                             const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim, int64_t f,
+                             float* work, float* y_f32, uint16_t* y_bf16, int32_t* sel, float* gates,
+                             void* stream) {
+  int rc = moe_check("moe_top2_gemv", x, logits, e, w13, s13, w2, s2, dim, f, work, true, y_f32, y_bf16, 32768);
+  if (rc) return rc;
+  return moe_launch(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32, y_bf16, sel, gates, stream);
 }

@@ -216,8 +216,7 @@ extern "C" int wq_quantize_int8(const float* w, int64_t n, int64_t k, int8_t* q,
   if (n == 0) return WQ_OK;
   int rc = check_device();
   if (rc) return rc;
-  static int resident = 0;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int8_kernel), 256);
+  const int resident = resident_groups(reinterpret_cast<const void*>(quantize_int8_kernel), 256);
   int64_t grid = balanced_grid((n + 3) / 4, resident);
   hipLaunchKernelGGL(quantize_int8_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, w, n, k, q,
                      scale);
@@ -227,8 +226,7 @@ extern "C" int wq_quantize_int8(const float* w, int64_t n, int64_t k, int8_t* q,
 template <int G>
 static int launch_quantize_int4(const float* w, int64_t n, int64_t k, uint8_t* qpacked, uint16_t* sz,
                                 hipStream_t stream, const char* name) {
-  static int resident = 0;
-  if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int4_kernel<G>), 256);
+  const int resident = resident_groups(reinterpret_cast<const void*>(quantize_int4_kernel<G>), 256);
   const int64_t blocks = (n * (k / G) + 255) / 256;
   const int64_t grid = balanced_grid(blocks, resident);
   hipLaunchKernelGGL(quantize_int4_kernel<G>, dim3((unsigned)grid), dim3(256), 0, stream, w, n, k, qpacked,
@@ -255,8 +253,7 @@ extern "C" int wq_quantize_int4(const float* w, int64_t n, int64_t k, int32_t gr
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (per_row) {
-    static int resident = 0;
-    if (resident == 0) resident = resident_groups(reinterpret_cast<const void*>(quantize_int4_row_kernel), 256);
+    const int resident = resident_groups(reinterpret_cast<const void*>(quantize_int4_row_kernel), 256);
     const int64_t grid = balanced_grid((n + 3) / 4, resident);
     hipLaunchKernelGGL(quantize_int4_row_kernel, dim3((unsigned)grid), dim3(256), 0, st, w, n, k, qpacked,
                        reinterpret_cast<uint32_t*>(sz));

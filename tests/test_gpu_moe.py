@@ -132,13 +132,16 @@ def test_moe_full_mixtral_shape_unselected_not_read(wq):
 
 def test_moe_argument_errors(wq):
     import torch
-    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
-    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    # raw device addresses: the binding passes them through unchecked, so
+    # the library's own host checks decide
+    keep = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    buf = keep.data_ptr()
+    y = torch.zeros(64, dtype=torch.float32, device="cuda").data_ptr()
     with pytest.raises(wq.WQError) as ei:
         wq.moe_top2_gemv(buf, buf, 4, buf, buf, buf, buf, 64, 64, buf, y)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
-        wq.moe_top2_gemv(buf.data_ptr() + 2, buf, 8, buf, buf, buf, buf, 64, 64, buf, y)
+        wq.moe_top2_gemv(buf + 2, buf, 8, buf, buf, buf, buf, 64, 64, buf, y)
     assert ei.value.status == 3
     with pytest.raises(wq.WQError) as ei:
         wq.moe_top2_gemv(buf, buf, 8, buf, buf, buf, buf, 64, 40, buf, y)
@@ -254,15 +257,18 @@ def test_moe_step_full_mixtral_shape_unselected_not_read(wq):
 
 def test_moe_step_argument_errors(wq):
     import torch
-    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
-    y = torch.zeros(64, dtype=torch.float32, device="cuda")
+    # raw device addresses (unchecked by the binding): the library decides
+    keep = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    buf = keep.data_ptr()
+    ykeep = torch.zeros(64, dtype=torch.float32, device="cuda")
+    y = ykeep.data_ptr()
     ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
     good = (buf, buf, buf, buf, buf, buf, buf, y, None, None, None)
     with pytest.raises(wq.WQError) as ei:
         wq.wq_moe_step_prepare(8, 64, 40, [good], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_moe_step_prepare(8, 64, 64, [(buf.data_ptr() + 2,) + good[1:]], ws)
+        wq.wq_moe_step_prepare(8, 64, 64, [(buf + 2,) + good[1:]], ws)
     assert ei.value.status == 3
     with pytest.raises(wq.WQError) as ei:
         wq.wq_moe_step_prepare(8, 64, 64, [good] * 100, ws, 16)

@@ -118,7 +118,9 @@ def test_step_matches_oracle(fmt, m):
 def test_step_argument_errors():
     import torch
     import weight_only_quantized_wq_amd as wq
-    buf = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    # raw device addresses (unchecked by the binding): the library decides
+    keep = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    buf = keep.data_ptr()
     ws = torch.empty(wq.wq_decode_step_workspace_bytes(1), dtype=torch.uint8, device="cuda")
     good = (buf, buf, buf, 4, 64, buf, None)
     with pytest.raises(wq.WQError) as ei:
@@ -131,7 +133,7 @@ def test_step_argument_errors():
         wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, None, 4, 64, buf, None)], ws)
     assert ei.value.status == 1
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int4g32", 1, [(buf.data_ptr() + 2, buf, buf, 4, 64, buf, None)], ws)
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf + 2, buf, buf, 4, 64, buf, None)], ws)
     assert ei.value.status == 3
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int4g32", 1, [good], ws, 64)

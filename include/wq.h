@@ -22,9 +22,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every buffer is DEVICE memory owned by the caller.  The library allocates
- *   nothing.  Its only state: a thread-local error text and per-device host
- *   caches (device check, occupancy; safe across host threads).  Passing a
- *   host pointer is outside the contract (the kernel would fault).
+ *   nothing.  Its only state: a thread-local error text, per-device host
+ *   caches (device check, occupancy; safe across host threads) and the
+ *   static device scratch of moe_top2_gemv_noalloc.  Passing a host pointer
+ *   is outside the contract (the kernel would fault).
  * - Row-major layouts; bf16 values are passed as their uint16 bit patterns.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *   is enqueued and the call returns without synchronising.
@@ -204,6 +205,26 @@ int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, const int8_
                   const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim,
                   int64_t f, float* work, float* y_f32, uint16_t* y_bf16, int32_t* sel,
                   float* gates, void* stream);
+
+/*
+ * moe_top2_gemv without the caller's workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments as moe_top2_gemv minus
+ * `work`, same results (bitwise: the same kernels run); the fp32 [2][f]
+ * SwiGLU intermediate lives in a static device array of the library (one per
+ * device, 128 KiB, held until the process ends), so f <= 16384
+ * (WQ_ERR_SHAPE beyond).  Allocates nothing and calls no allocating routine.
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (different streams, or host threads without ordering) race and
+ * give unspecified results; calls ordered on one stream are safe.  The first
+ * call on a device looks the array's address up once (with that device
+ * current).  The W13 launch writes the whole intermediate before the W2
+ * launch reads it, so no contents carry over from an earlier call.
+ */
+int moe_top2_gemv_noalloc(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
+                          const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim,
+                          int64_t f, float* y_f32, uint16_t* y_bf16, int32_t* sel, float* gates,
+                          void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* A whole decode step in one launch -- [README] "基准测试" (tokens/s of a  */

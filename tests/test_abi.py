@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
                  "wq_gemv_int4g32", "wq_gemv_int4",
                  "wq_gemm_smallM", "wq_gemm_smallM_int4", "wq_gemm_smallM_int8", "moe_top2_gemv", "wq_status_string", "wq_last_error",
                  "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
-                 "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run"]:
+                 "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run", "moe_top2_gemv_noalloc"]:
         assert want in names
 
 
@@ -286,3 +286,17 @@ def test_argument_errors_from_many_threads(wq):
     for t in ts:
         t.join()
     assert not errors, errors[:4]
+
+
+def test_noalloc_moe_argument_errors(wq):
+    """moe_top2_gemv_noalloc checks like moe_top2_gemv (null -> sizes ->
+    alignment) and refuses an f beyond its static scratch (2 x 16384 fp32)
+    before touching a device."""
+    lib = wq._binding.lib
+    assert lib.moe_top2_gemv_noalloc(BAD, None, 8, BAD, BAD, BAD, BAD, 64, 64, BAD, None, None, None, None) == 1
+    assert lib.moe_top2_gemv_noalloc(BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 64, None, None, None, None, None) == 1
+    assert lib.moe_top2_gemv_noalloc(BAD, BAD, 4, BAD, BAD, BAD, BAD, 64, 64, BAD, None, None, None, None) == 2
+    assert lib.moe_top2_gemv_noalloc(BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 16400, BAD, None, None, None, None) == 2
+    assert "scratch" in wq.last_error() and "16384" in wq.last_error()
+    # f = 16384 passes the size checks and stops at alignment
+    assert lib.moe_top2_gemv_noalloc(BAD, BAD, 8, BAD, BAD, BAD, BAD, 64, 16384, BAD, None, None, None, None) == 3

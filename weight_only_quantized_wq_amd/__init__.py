@@ -11,7 +11,7 @@ _EXPORTS = (
     "LIB_PATH", "WQError", "WQ_STATUS", "lib", "status_string", "last_error",
     "wq_quantize_int8", "wq_quantize_int4g32", "wq_quantize_int4",
     "wq_gemv_bf16", "wq_gemv_int8", "wq_gemv_int4g32", "wq_gemv_int4", "wq_gemm_smallM", "wq_gemm_smallM_int4", "wq_gemm_smallM_int8",
-    "moe_top2_gemv",
+    "moe_top2_gemv", "moe_top2_gemv_noalloc",
     "WQ_FORMAT", "wq_matrix", "wq_step_plan",
     "wq_decode_step_workspace_bytes", "wq_decode_step_prepare", "wq_decode_step_run",
     "wq_moe_layer", "wq_moe_plan", "wq_moe_step_workspace_bytes", "wq_moe_step_prepare", "wq_moe_step_run",

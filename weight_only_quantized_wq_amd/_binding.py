@@ -33,6 +33,7 @@ _SIGNATURES = {
     "wq_gemm_smallM_int8": [_P, _I64, _P, _P, _I64, _I64, _P, _P, _P],
     "wq_gemm_smallM_int4": [_P, _I64, _P, _P, _I64, _I64, _I32, _P, _P, _P],
     "moe_top2_gemv": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P, _P],
+    "moe_top2_gemv_noalloc": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P],
 }
 
 WQ_FORMAT = {"bf16": 1, "int8": 2, "int4g32": 3, "int4g64": 4, "int4g128": 5, "int4g256": 6, "int4pc": 7}
@@ -259,6 +260,16 @@ def moe_top2_gemv(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32=None, y_bf
           _ptr(s13, b["s13"], "s13"), _ptr(w2, b["w2"], "w2"), _ptr(s2, b["s2"], "s2"), dim, f,
           _ptr(work, b["work"], "work"), _ptr(y_f32, b["y_f32"], "y_f32"), _ptr(y_bf16, b["y_bf16"], "y_bf16"),
           _ptr(sel, b["sel"], "sel"), _ptr(gates, b["gates"], "gates"), _stream(stream))
+
+
+def moe_top2_gemv_noalloc(x, logits, e, w13, s13, w2, s2, dim, f, y_f32=None, y_bf16=None, sel=None,
+                          gates=None, stream=None):
+    """moe_top2_gemv with the SwiGLU intermediate in the library's static device scratch (f <= 16384)."""
+    b = _moe_bytes(e, dim, f)
+    _call("moe_top2_gemv_noalloc", _ptr(x, b["x"], "x"), _ptr(logits, b["logits"], "logits"), e,
+          _ptr(w13, b["w13"], "w13"), _ptr(s13, b["s13"], "s13"), _ptr(w2, b["w2"], "w2"), _ptr(s2, b["s2"], "s2"),
+          dim, f, _ptr(y_f32, b["y_f32"], "y_f32"), _ptr(y_bf16, b["y_bf16"], "y_bf16"), _ptr(sel, b["sel"], "sel"),
+          _ptr(gates, b["gates"], "gates"), _stream(stream))
 
 
 def wq_decode_step_workspace_bytes(count):

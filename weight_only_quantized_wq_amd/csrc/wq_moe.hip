@@ -4,7 +4,8 @@
 //   1. moe_w13_kernel: every workgroup routes (softmax top-2 of the logits,
 //      equal logits -> lower index; gates renormalised over the pair), then
 //      streams rows j and j + f of W13 for each selected expert and writes
-//      a[slot][j] = silu(h_j) * h_{j+f} (fp32) to the caller's workspace.
+//      a[slot][j] = silu(h_j) * h_{j+f} (fp32) to the caller's workspace
+//      (moe_top2_gemv_noalloc: to a static device array).
 //   2. moe_w2_kernel: two wave teams per workgroup, one per selected expert,
 //      stream row n of their expert's W2 against that expert's a; the
 //      workgroup combines y[n] = g_a o_a[n] + g_b o_b[n].
@@ -13,6 +14,9 @@
 // needed: the routing decision is recomputed (identically) on the device by
 // every workgroup from the 8 logits.
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "wq_host.hpp"
 #include "wq_moe_kernel.hpp"
@@ -93,7 +97,7 @@ static int moe_check(const char* name, const uint16_t* x, const float* logits, i
     return fail(WQ_ERR_SHAPE, "%s: dim = %lld, f = %lld must be multiples of 16 in [16, 32768]", name,
                 (long long)dim, (long long)f);
   if (f > max_f)
-    return fail(WQ_ERR_SHAPE, "%s: f = %lld exceeds this entry point's limit of %lld", name,
+    return fail(WQ_ERR_SHAPE, "%s: f = %lld exceeds this entry point's limit of %lld (its static scratch)", name,
                 (long long)f, (long long)max_f);
   if (!aligned16(x) || !aligned16(w13) || !aligned16(w2) || (need_work && !aligned16(work)))
     return fail(WQ_ERR_ALIGN, "%s: x, w13, w2%s must be 16-byte aligned", name, need_work ? " and work" : "");
@@ -132,5 +136,61 @@ extern "C" int moe_top2_gemv(const uint16_t* x, const float* logits, int64_t e, 
                              void* stream) {
   int rc = moe_check("moe_top2_gemv", x, logits, e, w13, s13, w2, s2, dim, f, work, true, y_f32, y_bf16, 32768);
   if (rc) return rc;
+  return moe_launch(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32, y_bf16, sel, gates, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The same layer for callers that cannot allocate: the SwiGLU intermediate
+// (fp32 [2][f]) lives in a static device array instead of a caller's
+// workspace.  Each device holds its own copy of the array at its own
+// address; host code never passes the array's name to a kernel (on the host
+// it is a stand-in, not a device address) but the address that
+// hipGetSymbolAddress returned for the current device.
+
+constexpr int64_t kMoeScratchMaxF = 16384;    // 2 x 16384 fp32 = 128 KiB per device
+static __device__ __align__(256) float scratch[2 * kMoeScratchMaxF];
+
+static std::atomic<float*> g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up once per device (with
+// that device current) and kept; null with the error recorded on failure.
+static float* scratch_on_current_device(const char* name) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(WQ_ERR_DEVICE, "%s: no usable current device (%d)", name, dev);
+    return nullptr;
+  }
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  void* addr = nullptr;
+  e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !addr) {
+    (void)hipGetLastError();
+    fail(WQ_ERR_DEVICE, "%s: hipGetSymbolAddress of the static scratch failed on device %d: %s", name, dev,
+         hipGetErrorString(e));
+    return nullptr;
+  }
+  p = static_cast<float*>(addr);
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+extern "C" int moe_top2_gemv_noalloc(const uint16_t* x, const float* logits, int64_t e, const int8_t* w13,
+                                     const uint16_t* s13, const int8_t* w2, const uint16_t* s2, int64_t dim,
+                                     int64_t f, float* y_f32, uint16_t* y_bf16, int32_t* sel, float* gates,
+                                     void* stream) {
+  const char* name = "moe_top2_gemv_noalloc";
+  int rc = moe_check(name, x, logits, e, w13, s13, w2, s2, dim, f, nullptr, false, y_f32, y_bf16, kMoeScratchMaxF);
+  if (rc) return rc;
+  float* work = scratch_on_current_device(name);
+  if (!work) return WQ_ERR_DEVICE;
+  // the W13 launch writes every element of work[0..2f) before the W2
+  // launch (same stream) reads it: nothing needs clearing
   return moe_launch(x, logits, e, w13, s13, w2, s2, dim, f, work, y_f32, y_bf16, sel, gates, stream);
 }

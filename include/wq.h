@@ -284,7 +284,7 @@ int64_t wq_decode_step_workspace_bytes(int32_t count);
  * Validates every matrix on the host (null -> sizes -> alignment; k must be a
  * positive multiple of 8 / 16 / G per format (32 for a per-row group) and within the kernel's row
  * limit: with one token row the activations are staged whole in LDS, so
- * k <= 31744 (bf16), 14336 (int8), 28672 (int4); int4 with 2..8 token rows
+ * k <= 80896 (bf16), 36864 (int8), 73728 (int4); int4 with 2..8 token rows
  * k <= 131072; int8 with 2..8 token rows k <= 2^24 and n * k <= 0xFFFFFF00),
  * then writes the launch description into `workspace` (device
  * memory, 16-byte aligned, `workspace_bytes` long, caller-owned; it must

@@ -13,7 +13,14 @@ N(0, 1) bf16 activations standing in for trained checkpoints:
   llama3.1-70b-int4-m5  Llama-3.1-70B set, int4 G=32, 5 tokens per pass,
                         W N(0, 0.015)                       (321 matmuls)
   llama3.1-70b-int8-m5  the same weights in int8, 5 tokens per pass
+  llama3.1-70b-int8     the same weights in int8, batch 1 (one token)
+  llama2-70b-int8 / llama2-70b-int4   Llama-2-70B set, batch 1
   mixtral-int8     Mixtral-8x7B MoE, 32 layers x 8 int8 experts, top-2
+  <set>-tp2 / -tp4 / -tp8   one GPU's shard of the set under P-way tensor
+                   parallelism (Llama-2-7B int4 and int8, Llama-3.1-70B int4
+                   at 5 tokens): column-parallel wqkv and w1|w3 keep 1/P of
+                   their rows, row-parallel wo and w2 1/P of their inputs,
+                   lm_head whole
 
 Generators are keyed by (workload id, layer, matrix id, role) so every
 matrix has its own reproducible values; the key scheme is in ``synth.gen``.
@@ -21,7 +28,7 @@ matrix has its own reproducible values; the key scheme is in ``synth.gen``.
 
 from dataclasses import dataclass
 
-from .configs import LLAMA2_7B, LLAMA31_8B, LLAMA31_70B, MIXTRAL_8X7B, Matrix, linear_set
+from .configs import LLAMA2_7B, LLAMA2_70B, LLAMA31_8B, LLAMA31_70B, MIXTRAL_8X7B, Matrix, linear_set
 from .gen import ROLE_W, ROLE_X, ROLE_LOGITS, device_normal, device_bf16_normal, host_normal, host_bf16_normal
 
 
@@ -37,6 +44,7 @@ class Workload:
     sigma: float
     model: object
     note: str = ""
+    tp: int = 1
 
     def matrices(self, layers=None):
         if self.model is None:
@@ -45,7 +53,7 @@ class Workload:
             # serve a repeat and every launch streams from HBM
             n = COPIES if layers is None else 1
             return [Matrix("w", 0, 0, 4096, 4096) for _ in range(n)]
-        return linear_set(self.model, layers)
+        return linear_set(self.model, layers, self.tp)
 
 
 WORKLOADS = {w.name: w for w in [
@@ -59,7 +67,17 @@ WORKLOADS = {w.name: w for w in [
     Workload("llama3.1-8b-int8", 6, "int8", 1, 0.02, LLAMA31_8B),
     Workload("llama3.1-70b-int4-m5", 4, "int4g32", 5, 0.015, LLAMA31_70B),
     Workload("llama3.1-70b-int8-m5", 4, "int8", 5, 0.015, LLAMA31_70B),
+    Workload("llama3.1-70b-int8", 4, "int8", 1, 0.015, LLAMA31_70B),
+    Workload("llama2-70b-int8", 7, "int8", 1, 0.015, LLAMA2_70B),
+    Workload("llama2-70b-int4", 7, "int4g32", 1, 0.015, LLAMA2_70B),
     Workload("mixtral-int8", 5, "int8", 1, 0.02, MIXTRAL_8X7B),
+] + [
+    # one GPU's shard under P-way tensor parallelism
+    Workload(f"{base}-tp{p}", wid, fmt, m, sigma, model, f"{p}-way tensor-parallel shard", p)
+    for base, wid, fmt, m, sigma, model in [("llama2-7b-int4", 2, "int4g32", 1, 0.02, LLAMA2_7B),
+                                            ("llama2-7b-int8", 3, "int8", 1, 0.02, LLAMA2_7B),
+                                            ("llama3.1-70b-int4-m5", 4, "int4g32", 5, 0.015, LLAMA31_70B)]
+    for p in (2, 4, 8)
 ]}
 
 

@@ -111,3 +111,70 @@ def test_workload_matrix_sets():
     assert len(WORKLOADS["int8-4096"].matrices()) == 64
     shapes = {(m.n, m.k) for m in WORKLOADS["llama2-7b-int4"].matrices()}
     assert shapes == {(12288, 4096), (4096, 4096), (22016, 4096), (4096, 11008), (32000, 4096)}
+
+
+def test_context_figures_are_the_pages_rows():
+    """The bench line's context block repeats the pages' printed figures
+    (tests/golden/pages_benchmark_rows.json, each row cited there)."""
+    import bench
+    rows = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_benchmark_rows.json")))["rows"]
+    key = {("A100", "llama-2-7b"): "a100_llama2_7b", ("A100", "llama-2-70b"): "a100_llama2_70b",
+           ("A100", "llama-3.1-8b"): "a100_llama3_1_8b", ("A100", "llama-3.1-70b"): "a100_llama3_1_70b",
+           ("MI250X-GCD", "llama-2-7b"): "mi250x_gcd_llama2_7b"}
+    seen = 0
+    for r in rows:
+        e = bench.PAGES_CONTEXT[key[(r["hw"], r["model"])]][r["format"]]
+        assert e["tok_per_s"] == r["tok_s"] and e["gbs"] == r["gb_s"]
+        seen += 1
+    assert seen == len(rows) == 10
+    assert bench.PAGES_CONTEXT["a100_mixtral_8x7b"]["int8"]["tok_per_s"] == 97.92
+
+
+def test_host_threads_and_cpu_model(monkeypatch):
+    import bench
+    n = len(os.sched_getaffinity(0))
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_threads() == (1, n)
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.host_threads() == (n, n)
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+
+
+def test_cpu_samples_extrapolate_row_slices_to_the_step(monkeypatch):
+    """A slice of rows stands for its full matrix in proportion n / rows, and
+    each shape counts as often as the step holds it."""
+    import bench
+    from synth.configs import Model
+    from synth.workloads import Workload
+    from weight_only_quantized_wq_amd.layerset import matrix_bytes
+    tiny = Model("tiny", 64, 96, 128, 160, 3)
+    wl = Workload("tiny-int4", 99, "int4g32", 1, 0.02, tiny)
+    monkeypatch.setattr(bench, "_time_repeated", lambda fn, s: (fn(), 1e-3)[1])
+    rows, sample = bench.cpu_samples(wl, 0.01, max_weights=64 * 40)
+    got = {shape: (count, t, b) for shape, count, t, b in rows}
+    assert set(got) == {(96, 64), (64, 64), (256, 64), (64, 128), (160, 64)}
+    assert got[(256, 64)] == (3, pytest.approx(1e-3 * 256 / 40), matrix_bytes("int4g32", 256, 64))
+    assert got[(64, 128)] == (3, pytest.approx(1e-3 * 64 / 20), matrix_bytes("int4g32", 64, 128))
+    assert got[(160, 64)][0] == 1
+    assert "[40x64] of [256x64]" in sample
+
+
+def test_tensor_parallel_shards_split_rows_or_inputs():
+    """One GPU's shard under P-way tensor parallelism: wqkv and w1|w3 keep
+    1/P of their rows, wo and w2 1/P of their inputs, lm_head stays whole."""
+    from synth.workloads import WORKLOADS
+    for p in (2, 4, 8):
+        full = WORKLOADS["llama2-7b-int4"].matrices()
+        shard = WORKLOADS[f"llama2-7b-int4-tp{p}"].matrices()
+        assert len(full) == len(shard)
+        for a, b in zip(full, shard):
+            if a.name in ("wqkv", "w13"):
+                assert (b.n, b.k) == (a.n // p, a.k)
+            elif a.name in ("wo", "w2"):
+                assert (b.n, b.k) == (a.n, a.k // p)
+            else:
+                assert (b.n, b.k) == (a.n, a.k)
+            assert b.k % 32 == 0 and b.n * p in (a.n, a.n * p)
+    s8 = {(m.n, m.k) for m in WORKLOADS["llama3.1-70b-int4-m5-tp8"].matrices()}
+    assert s8 == {(1280, 8192), (8192, 1024), (7168, 8192), (8192, 3584), (128256, 8192)}
+    assert WORKLOADS["llama3.1-70b-int4-m5-tp8"].m == 5

@@ -60,9 +60,13 @@ def _check_matrix(wl, q, mat, gen_w, layer_tag):
     assert e16 <= TOL_BF16 and e32 <= TOL_F32
 
 
-@pytest.mark.parametrize("name", ["llama2-7b-int4", "llama2-7b-int8", "llama2-7b-bf16", "llama3.1-8b-int8",
-                                  "llama3.1-8b-bf16", "llama3.1-70b-int4-m5", "llama3.1-70b-int8-m5",
-                                  "llama2-7b-int4g128", "llama2-7b-int4pc", "int8-4096"])
+LINEAR_SETS = ["llama2-7b-int4", "llama2-7b-int8", "llama2-7b-bf16", "llama3.1-8b-int8", "llama3.1-8b-bf16",
+               "llama3.1-70b-int4-m5", "llama3.1-70b-int8-m5", "llama3.1-70b-int8", "llama2-70b-int8",
+               "llama2-70b-int4", "llama2-7b-int4g128", "llama2-7b-int4pc", "int8-4096"] + \
+              [f"{b}-tp{p}" for b in ("llama2-7b-int4", "llama2-7b-int8", "llama3.1-70b-int4-m5") for p in (2, 4, 8)]
+
+
+@pytest.mark.parametrize("name", LINEAR_SETS)
 def test_workload_full_size_sampled(name):
     import torch
     from synth.workloads import WORKLOADS, gen_w_device, gen_x_device

@@ -19,10 +19,11 @@ from synth.gen import host_normal, host_bf16_normal
 pytestmark = pytest.mark.gpu
 
 SHAPES = {
-    ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8)],
-    ("int8", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 16)],
+    ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8), (2, 65536)],
+    ("int8", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 16), (3, 28672),
+                  (2, 36864)],
     ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32), (3, 28672),
-                     (70, 4160)],
+                     (70, 4160), (2, 73728)],
     ("int4g32", 5): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32)],
     ("int4g32", 2): [(45, 4096), (9, 16384)],
     ("int4g32", 8): [(45, 4096), (9, 16384), (3, 28672)],
@@ -143,10 +144,10 @@ def test_step_argument_errors():
     assert ei.value.status == 2
     # one past the longest int8 / int4 rows the single-token step kernel stages
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int8", 1, [(buf, buf, buf, 4, 14352, buf, None)], ws)
+        wq.wq_decode_step_prepare("int8", 1, [(buf, buf, buf, 4, 36880, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 28704, buf, None)], ws)
+        wq.wq_decode_step_prepare("int4g32", 1, [(buf, buf, buf, 4, 73760, buf, None)], ws)
     assert ei.value.status == 2
     # wider int4 groups: k a multiple of the group
     with pytest.raises(wq.WQError) as ei:
@@ -156,7 +157,7 @@ def test_step_argument_errors():
         wq.wq_decode_step_prepare("int4g128", 1, [(buf, buf, buf, 4, 192, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
-        wq.wq_decode_step_prepare("int4g256", 1, [(buf, buf, buf, 4, 28928, buf, None)], ws)
+        wq.wq_decode_step_prepare("int4g256", 1, [(buf, buf, buf, 4, 73984, buf, None)], ws)
     assert ei.value.status == 2
     with pytest.raises(wq.WQError) as ei:
         wq.wq_decode_step_prepare("int8", 9, [good], ws)

@@ -25,9 +25,7 @@ import pytest
 
 from oracle.quant import quantize_int8, quantize_int4g32
 from oracle.bf16 import round_f32_to_bf16
-from synth.configs import LLAMA2_7B, LLAMA31_8B, LLAMA31_70B, Model, linear_set
-
-LLAMA2_70B = Model("llama-2-70b", 8192, 10240, 28672, 32000, 80)
+from synth.configs import LLAMA2_7B, LLAMA2_70B, LLAMA31_8B, LLAMA31_70B, linear_set
 MODELS = {m.name: m for m in (LLAMA2_7B, LLAMA31_8B, LLAMA31_70B, LLAMA2_70B)}
 HERE = os.path.dirname(os.path.abspath(__file__))
 

@@ -272,8 +272,12 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
           const int lane = 16 * rq + col, wr = lane >> 3, ws = lane & 7;
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
+            // lanes read what other lanes stored: the wave barriers keep the
+            // compiler from reordering these LDS accesses across lanes' roles
+            __builtin_amdgcn_wave_barrier();
             *reinterpret_cast<u32x4*>(tile + mfma_tile_at(wr, ws)) = cur.w[rt][0];
             *reinterpret_cast<u32x4*>(tile + mfma_tile_at(wr + 8, ws)) = cur.w[rt][1];
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int o = 0; o < OCT; ++o) wl[rt][o] = *reinterpret_cast<const u32x4*>(tile + mfma_tile_at(col, OCT * rq + o));
           }

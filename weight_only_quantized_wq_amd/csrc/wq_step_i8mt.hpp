@@ -106,8 +106,13 @@ __device__ __forceinline__ void mt_accumulate(const MtPassBuf<U>& bt, f32x4 (&ac
   uint8_t* st1 = lds + (wr + 8) * 128 + ((ws ^ (((wr + 8) >> 1) & 7)) << 4);   // row wr + 8
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    // Lanes read what other lanes stored: the wave's LDS accesses execute in
+    // program order, and the wave barriers keep the compiler from moving
+    // the reads above these stores or the next tile's stores above them.
+    __builtin_amdgcn_wave_barrier();
     *reinterpret_cast<u32x4*>(st0) = bt.w[u][0];
     *reinterpret_cast<u32x4*>(st1) = bt.w[u][1];
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       // bytes 32 m + 8 s of row rr: slot 2 m + s / 2, half s % 2

@@ -33,8 +33,11 @@
 
 namespace wq {
 
-// LDS words for staged activations (64 KiB minus room for the counter).
-constexpr int kSharedXWords = 16320;
+// LDS words for staged activations: 158 KiB of gfx950's 160 KiB per
+// workgroup (one workgroup per CU), leaving room for the counter and the
+// range.  With 17 words per 16 inputs (int8) a row of up to 36864 inputs
+// stages whole.
+constexpr int kSharedXWords = 40448;
 
 // Chunks of one row the kernel can stage: the largest multiple of a pass
 // (64 * CPL chunks) that fits the LDS budget.

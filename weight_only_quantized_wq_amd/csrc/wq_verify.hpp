@@ -257,8 +257,12 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
       if ((o & 1) == 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
+          // lanes read what other lanes stored: the wave barriers keep the
+          // compiler from reordering these LDS accesses across lanes' roles
+          __builtin_amdgcn_wave_barrier();
           *reinterpret_cast<u32x4*>(tile + verify_tile_at(wr, ws)) = q.w[rt][o];
           *reinterpret_cast<u32x4*>(tile + verify_tile_at(wr + 8, ws)) = q.w[rt][o + 1];
+          __builtin_amdgcn_wave_barrier();
 #pragma unroll
           for (int h = 0; h < 2; ++h) wl[rt][h] = *reinterpret_cast<const u32x4*>(tile + verify_tile_at(col, 4 * h + rq));
         }

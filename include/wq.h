@@ -153,8 +153,11 @@ int wq_gemv_int4(const uint16_t* x, const uint8_t* qpacked, const uint16_t* sz, 
  * through one int4 G=32 linear in one pass, each weight read once:
  *   x bf16 [m][k], 1 <= m <= 8; y [m][n]; row i of y equals
  *   wq_gemv_int4g32 applied to row i of x (to fp32 rounding).
- * k % 32 == 0; k <= 131072 for m == 1, 32768 for m == 2, 131072 for
- * m >= 3 (from three tokens on the matrix cores).
+ * k % 32 == 0, k <= 131072.  From two tokens on the matrix cores (each weight
+ * decoded once for all tokens).  The environment variable
+ * WQ_SMALLM_ENGINE=valu (read at each call) moves 2, 3 and 5 tokens to the
+ * vector ALU where its plans reach (k <= 32768 for int4, 16384 for int8),
+ * for comparison; =mfma or unset keeps the matrix cores (measured faster).
  */
 int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
                    int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);
@@ -175,9 +178,10 @@ int wq_gemm_smallM_int4(const uint16_t* x, int64_t m, const uint8_t* qpacked, co
  * [README] "Int8 仅权重量化".  x bf16 [m][k], 1 <= m <= 8; q, scale as written
  * by wq_quantize_int8; y [m][n] with y[t][r] = scale[r] * sum_k x[t][k] q[r][k];
  * row t of y equals wq_gemv_int8 applied to row t of x (to fp32 rounding).
- * Each weight is read once (m >= 2: on the matrix cores).  k % 16 == 0;
- * k <= 65536 for m == 1 (the one-token matvec), k <= 2^24 and
- * n * k <= 0xFFFFFF00 for m >= 2.  scale 2-byte aligned.
+ * Each weight is read once (m >= 2: on the matrix cores; WQ_SMALLM_ENGINE as
+ * for wq_gemm_smallM).  k % 16 == 0; k <= 65536 for m == 1 (the one-token
+ * matvec), k <= 2^24 and n * k <= 0xFFFFFF00 for m >= 2.  scale 2-byte
+ * aligned.
  */
 int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q, const uint16_t* scale, int64_t n,
                         int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);

@@ -14,6 +14,7 @@ N(0, 1) bf16 activations standing in for trained checkpoints:
                         W N(0, 0.015)                       (321 matmuls)
   llama3.1-70b-int8-m5  the same weights in int8, 5 tokens per pass
   llama3.1-70b-int8     the same weights in int8, batch 1 (one token)
+  llama3.1-70b-int4-m2 / -m3, llama3.1-70b-int8-m2 / -m3   2 and 3 tokens per pass
   llama2-70b-int8 / llama2-70b-int4   Llama-2-70B set, batch 1
   mixtral-int8     Mixtral-8x7B MoE, 32 layers x 8 int8 experts, top-2
   <set>-tp2 / -tp4 / -tp8   one GPU's shard of the set under P-way tensor
@@ -68,6 +69,11 @@ WORKLOADS = {w.name: w for w in [
     Workload("llama3.1-70b-int4-m5", 4, "int4g32", 5, 0.015, LLAMA31_70B),
     Workload("llama3.1-70b-int8-m5", 4, "int8", 5, 0.015, LLAMA31_70B),
     Workload("llama3.1-70b-int8", 4, "int8", 1, 0.015, LLAMA31_70B),
+    # the same sets verifying 2 and 3 draft tokens
+    Workload("llama3.1-70b-int4-m2", 4, "int4g32", 2, 0.015, LLAMA31_70B),
+    Workload("llama3.1-70b-int4-m3", 4, "int4g32", 3, 0.015, LLAMA31_70B),
+    Workload("llama3.1-70b-int8-m2", 4, "int8", 2, 0.015, LLAMA31_70B),
+    Workload("llama3.1-70b-int8-m3", 4, "int8", 3, 0.015, LLAMA31_70B),
     Workload("llama2-70b-int8", 7, "int8", 1, 0.015, LLAMA2_70B),
     Workload("llama2-70b-int4", 7, "int4g32", 1, 0.015, LLAMA2_70B),
     Workload("mixtral-int8", 5, "int8", 1, 0.02, MIXTRAL_8X7B),

@@ -283,3 +283,42 @@ def test_gemm_small_m_int4_groups(wq, m, group, n, k):
     e = _compare(y32, y16, ref, (m, n))
     _check_guards(b32, b16, m * n)
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
+
+
+ENGINE_CASES = [(fmt, m, n, k) for fmt in ("int4", "int8") for m in (2, 3, 5)
+                for (n, k) in [(45, 4096), (70, 8192), (3, 32), (130, 16384), (7, 0)]] + \
+    [("int4", m, 19, 28672) for m in (2, 3, 5)] + [("int4", 5, 2, 32768), ("int8", 2, 9, 28672)]
+
+
+@pytest.mark.parametrize("fmt,m,n,k", ENGINE_CASES)
+def test_gemm_small_m_engines(wq, monkeypatch, fmt, m, n, k):
+    """The vector-ALU and matrix-core kernels for 2, 3 and 5 token rows
+    (WQ_SMALLM_ENGINE forces one; rows past a vector-ALU plan's reach run on
+    the matrix cores) each match the oracle, and each other to fp32
+    rounding."""
+    from oracle.quant import quantize_int8
+    from oracle.matvec import gemm_small_m_int8
+    say(f"engines {fmt} m={m} n={n} k={k}")
+    w = host_normal((n, k), 0.02, 953, m, n, k)
+    x = host_bf16_normal((m, k), 953, m, n, k + 1)
+    if fmt == "int4":
+        p, sz = quantize_int4g32(w)
+        ref = gemm_small_m(x, p, sz) if k else np.zeros((m, n))
+        args = (_d(p), _d(sz))
+    else:
+        q, s = quantize_int8(w)
+        ref = gemm_small_m_int8(x, q, s) if k else np.zeros((m, n))
+        args = (_d(q), dev(s))
+    xd = _d(x)
+    got = {}
+    for engine in ("valu", "mfma"):
+        monkeypatch.setenv("WQ_SMALLM_ENGINE", engine)
+        (b32, y32), (b16, y16) = _outputs(n, m)
+        if fmt == "int4":
+            wq.wq_gemm_smallM(xd, m, args[0], args[1], n, k, y32, y16)
+        else:
+            wq.wq_gemm_smallM_int8(xd, m, args[0], args[1], n, k, y32, y16)
+        _compare(y32, y16, ref, (m, n))
+        _check_guards(b32, b16, m * n)
+        got[engine] = host(y32).reshape(m, n)
+    assert rel_err(got["valu"], got["mfma"]) <= 1e-5

@@ -1,9 +1,11 @@
 // Batch-1 (and small-M) decode matvecs y = x . W^T over bf16, int8 per-row
 // and int4 weights, streamed from HBM: launch planning and the C entry
-// points.  The kernels are in wq_gemv_kernel.hpp (one token row, and two
-// int4 rows), wq_mfma.hpp (3..8 int4 rows) and wq_step_i8mt.hpp (2..8 int8
-// rows).
+// points.  The kernels are in wq_gemv_kernel.hpp (one token row; 2, 3 and 5
+// rows on the vector ALU when WQ_SMALLM_ENGINE=valu asks for them),
+// wq_mfma.hpp (2..8 int4 rows) and wq_step_i8mt.hpp (2..8 int8 rows).
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
@@ -78,13 +80,45 @@ struct Plans<FmtInt4, 1> {
                                        WQ_PLAN(896, 7, 4, 1, true), WQ_PLAN(3584, 7, 8, 1, true),
                                        WQ_PLAN(4096, 8, 8, 1, false)};
 };
-// two-token verify rows: the activations of both tokens stay in registers
-// (from three tokens on the matrix-core kernel of wq_mfma.hpp is faster)
+// Several token rows on the vector ALU: each token's activations stay in
+// registers, one decode serves every token.  These plans are the measured
+// alternative to the matrix-core kernels for 2, 3 and 5 rows (see
+// use_valu for the routing and the timings behind it).
 template <>
 struct Plans<FmtInt4, 2> {
   using F = FmtInt4;
   static constexpr int M = 2;
-  static constexpr PlanEntry list[] = {WQ_PLAN(1024, 2, 8, 2, false)};
+  static constexpr PlanEntry list[] = {WQ_PLAN(1024, 2, 8, 2, false), WQ_PLAN(4096, 1, 16, 1, false)};
+};
+template <>
+struct Plans<FmtInt4, 3> {
+  using F = FmtInt4;
+  static constexpr int M = 3;
+  static constexpr PlanEntry list[] = {WQ_PLAN(512, 1, 8, 2, false), WQ_PLAN(4096, 1, 16, 1, false)};
+};
+template <>
+struct Plans<FmtInt4, 5> {
+  using F = FmtInt4;
+  static constexpr int M = 5;
+  static constexpr PlanEntry list[] = {WQ_PLAN(512, 1, 8, 1, false), WQ_PLAN(4096, 1, 16, 1, false)};
+};
+template <>
+struct Plans<FmtInt8, 2> {
+  using F = FmtInt8;
+  static constexpr int M = 2;
+  static constexpr PlanEntry list[] = {WQ_PLAN(1024, 2, 8, 1, false), WQ_PLAN(4096, 1, 16, 1, false)};
+};
+template <>
+struct Plans<FmtInt8, 3> {
+  using F = FmtInt8;
+  static constexpr int M = 3;
+  static constexpr PlanEntry list[] = {WQ_PLAN(512, 1, 8, 2, false), WQ_PLAN(4096, 1, 16, 1, false)};
+};
+template <>
+struct Plans<FmtInt8, 5> {
+  using F = FmtInt8;
+  static constexpr int M = 5;
+  static constexpr PlanEntry list[] = {WQ_PLAN(512, 1, 8, 1, false), WQ_PLAN(4096, 1, 16, 1, false)};
 };
 #undef WQ_PLAN
 
@@ -265,6 +299,61 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
 
 }  // namespace wq
 
+namespace wq {
+
+// Which kernels serve 2..8 token rows: the matrix cores or, for the row
+// counts that have vector-ALU plans (2, 3, 5), the vector ALU.  "auto" takes
+// the measured choice per format and row count; the environment variable
+// WQ_SMALLM_ENGINE=mfma or =valu forces one side where it exists (read at
+// each call), which is how the two are timed and tested against each other.
+enum class Engine { kAuto, kMfma, kValu };
+
+static Engine smallm_engine() {
+  const char* v = getenv("WQ_SMALLM_ENGINE");
+  if (v && strcmp(v, "mfma") == 0) return Engine::kMfma;
+  if (v && strcmp(v, "valu") == 0) return Engine::kValu;
+  return Engine::kAuto;
+}
+
+// True when the vector-ALU plans of F serve m rows of `chunks` chunks.
+template <class F, int M>
+static bool valu_fits(int64_t chunks) {
+  PlanEntry p{};
+  int split = 0;
+  return choose_plan<F, M>(chunks, p, split);
+}
+
+template <class F>
+static bool valu_fits_m(int64_t m, int64_t chunks) {
+  switch (m) {
+    case 2: return valu_fits<F, 2>(chunks);
+    case 3: return valu_fits<F, 3>(chunks);
+    case 5: return valu_fits<F, 5>(chunks);
+    default: return false;
+  }
+}
+
+template <class F>
+static int run_gemv_m(const GemvArgs& a, int64_t m, hipStream_t s, const char* name) {
+  switch (m) {
+    case 2: return run_gemv<F, 2>(a, s, name);
+    case 3: return run_gemv<F, 3>(a, s, name);
+    default: return run_gemv<F, 5>(a, s, name);
+  }
+}
+
+// The measured routing (auto): the matrix cores for every row count.  Timed
+// on the Llama-3.1-70B shapes (back-to-back single launches), they beat the
+// vector-ALU plans at 2 rows (int4 on all five shapes by 3-14 %, int8 on
+// four of five; only int8 10240 x 8192 was 10 % faster on the vector ALU)
+// and by ~2x at 3 and 5 rows, where the vector ALU runs out of issue slots.
+static bool use_valu(bool int8, int64_t m, int64_t chunks) {
+  if (smallm_engine() != Engine::kValu) return false;
+  return int8 ? valu_fits_m<FmtInt8>(m, chunks) : valu_fits_m<FmtInt4>(m, chunks);
+}
+
+}  // namespace wq
+
 static int gemm_small_m_int4(const char* name, const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
                              int64_t n, int64_t k, int64_t group, float* y_f32, uint16_t* y_bf16, void* stream) {
   GemvArgs a;
@@ -273,20 +362,18 @@ static int gemm_small_m_int4(const char* name, const uint16_t* x, int64_t m, con
   if (n == 0) return WQ_OK;
   if ((rc = check_device())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (m >= 3) {
-    if (k > kMfmaMaxK)
-      return fail(WQ_ERR_SHAPE, "%s: k = %lld is larger than %d", name, (long long)k, kMfmaMaxK);
-    switch (m) {
-      case 3: return launch_mfma<3>(a, s);
-      case 4: return launch_mfma<4>(a, s);
-      case 5: return launch_mfma<5>(a, s);
-      case 6: return launch_mfma<6>(a, s);
-      case 7: return launch_mfma<7>(a, s);
-      default: return launch_mfma<8>(a, s);
-    }
+  if (m == 1) return run_gemv<FmtInt4, 1>(a, s, name);
+  if (k > kMfmaMaxK) return fail(WQ_ERR_SHAPE, "%s: k = %lld is larger than %d", name, (long long)k, kMfmaMaxK);
+  if (use_valu(false, m, a.chunks)) return run_gemv_m<FmtInt4>(a, m, s, name);
+  switch (m) {
+    case 2: return launch_mfma<2>(a, s);
+    case 3: return launch_mfma<3>(a, s);
+    case 4: return launch_mfma<4>(a, s);
+    case 5: return launch_mfma<5>(a, s);
+    case 6: return launch_mfma<6>(a, s);
+    case 7: return launch_mfma<7>(a, s);
+    default: return launch_mfma<8>(a, s);
   }
-  if (m == 2) return run_gemv<FmtInt4, 2>(a, s, name);
-  return run_gemv<FmtInt4, 1>(a, s, name);
 }
 
 extern "C" int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz, int64_t n,
@@ -354,6 +441,7 @@ extern "C" int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q
   a.row_bytes = k;
   a.chunks = (int32_t)(k / 16);
   if (m == 1) return run_gemv<FmtInt8, 1>(a, s, name);
+  if (use_valu(true, m, a.chunks)) return run_gemv_m<FmtInt8>(a, m, s, name);
   // (k == 0: no passes; every output is the empty sum, 0)
   switch (m) {
     case 2: return launch_i8m<2>(a, s);

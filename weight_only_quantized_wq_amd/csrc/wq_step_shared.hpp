@@ -219,22 +219,36 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
   }
 }
 
-// Load balance across XCDs.  Workgroup g runs on XCD g mod 8 (workgroups
-// are dispatched to the XCDs round robin), and under this kernel's mix of
-// streaming and arithmetic the XCDs of one device finish equal shares up to
-// ~8 % apart.  So each launch measures, per XCD, the cost its workgroups
-// streamed and the time they took; the last workgroup to finish turns that
-// into relative speeds (a quarter of the new measurement per launch, clamped
-// to [0.7, 1.3]) and the next launch
-// cuts the step into ranges proportional to them.  Which workgroup computes a
-// row never changes the row's result.
+// Load balance across XCDs.  The workgroups of a launch are dispatched to
+// the 8 XCDs round robin, but the XCD the first one lands on depends on what
+// was dispatched before (back-to-back launches from a HIP graph start one
+// XCD further than the same launches issued directly), so workgroup g runs
+// on XCD (g + off) mod 8 with a per-launch offset `off`.  Each workgroup
+// reads the XCD it actually runs on from the hardware (XCC_ID).  Under this
+// kernel's mix of streaming and arithmetic the XCDs of one device finish
+// equal shares up to ~8 % apart, so each launch measures, per actual XCD,
+// the cost its workgroups streamed and the time they took; the last
+// workgroup to finish turns that into relative speeds (a quarter of the new
+// measurement per launch, clamped to [0.7, 1.3]) and records the offset it
+// observed.  The next launch cuts the step into ranges proportional to the
+// speeds of the XCDs its workgroups are expected on (that offset): every
+// workgroup reads the same state, so the ranges always partition the step,
+// and an offset that changed in between only costs balance for one launch.
+// Which workgroup computes a row never changes the row's result.
 struct StepBalance {
-  float w[8];      // relative speed of each XCD's workgroups (mean 1)
+  float w[8];      // relative speed of each XCD's workgroups (mean 1), by hardware XCD id
   float cost[8];   // this launch: cost streamed by each XCD's workgroups
   float time[8];   // this launch: their summed durations (wall-clock ticks)
   int32_t done;    // workgroups finished in this launch
-  int32_t pad[7];
+  int32_t xoff;    // dispatch offset the last launch observed: workgroup g ran on XCD (g + xoff) mod 8
+  int32_t pad[6];
 };
+
+// Hardware id of the XCD (accelerator complex die) the calling wave runs on.
+__device__ __forceinline__ int hw_xcd_id() {
+  // s_getreg_b32 of HW_REG_XCC_ID (register 20), bits [3:0]
+  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u);
+}
 
 struct StepCuts {
   const double* prefix;   // [count + 1] cost of the step before matrix i
@@ -245,18 +259,17 @@ struct StepCuts {
 };
 
 // Cost at which workgroup g's range starts: the step's cost times the share
-// of the speed weights of workgroups 0 .. g-1.
-__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int g, int groups) {
-  double sw = 0.0, part = 0.0;
+// of the speed weights of workgroups 0 .. g-1, workgroup j weighing the
+// speed of XCD (j + off) mod 8.
+__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int off, int g, int groups) {
+  double sw = 0.0, part = 0.0, full = 0.0;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    sw += (double)w[x];
-    if (x < g % 8) part += (double)w[x];
+  for (int r = 0; r < 8; ++r) {
+    const double v = (double)w[(r + off) & 7];
+    sw += v;
+    if (r < g % 8) part += v;
+    if (r < groups % 8) full += v;
   }
-  double full = 0.0;
-#pragma unroll
-  for (int x = 0; x < 8; ++x)
-    if (x < groups % 8) full += (double)w[x];
   const double before = (double)(g / 8) * sw + part;
   const double all = (double)(groups / 8) * sw + full;
   return c.prefix[c.count] * (before / all);
@@ -276,9 +289,11 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
   float w[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) w[x] = cuts.bal->w[x];
+  const int off = cuts.bal->xoff & 7;
   const int G = (int)gridDim.x;
-  const double c0 = cut_cost(cuts, w, (int)blockIdx.x, G);
-  const double c1 = (int)blockIdx.x + 1 == G ? cuts.prefix[cuts.count] : cut_cost(cuts, w, (int)blockIdx.x + 1, G);
+  const double c0 = cut_cost(cuts, w, off, (int)blockIdx.x, G);
+  const double c1 =
+      (int)blockIdx.x + 1 == G ? cuts.prefix[cuts.count] : cut_cost(cuts, w, off, (int)blockIdx.x + 1, G);
   // the batch at cost c: first batch of matrix i (prefix[i] <= c < prefix[i + 1])
   // whose start is at or past c; every matrix is checked by one thread
   if (threadIdx.x == 0) {
@@ -321,7 +336,7 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
   __syncthreads();
   if (threadIdx.x == 0) {
     StepBalance* b = cuts.bal;
-    const int x = (int)(blockIdx.x % 8);
+    const int x = hw_xcd_id();
     atomicAdd(&b->cost[x], (float)(c1 - c0));
     atomicAdd(&b->time[x], (float)(wall_clock64() - t_start));
     __threadfence();
@@ -354,6 +369,7 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
         atomicExch(&b->cost[y], 0.0f);
         atomicExch(&b->time[y], 0.0f);
       }
+      atomicExch(&b->xoff, (x - (int)(blockIdx.x % 8) + 8) & 7);
       atomicExch(&b->done, 0);
     }
   }

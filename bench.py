@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-calibration", action="store_true", help="skip the 1 GiB copy used to scale PMC counters")
+    p.add_argument("--no-graph", action="store_true",
+                   help="fused steps: skip the HIP-graph replay timed for comparison (kernel traces then hold "
+                        "only the direct launches)")
     return p.parse_args()
 
 
@@ -404,15 +407,16 @@ def main():
         # kernel's average duration (consecutive launches leave no gap)
         wall, ev_ms = timed_steps_events(step, args.steps)
         dur = {launches[0][0]: (ev_ms / args.steps / len(launches), list(range(len(launches))))}
-        # the same step replayed from a HIP graph, for comparison only
-        graph = capture(step)
-        for _ in range(args.warmup):
-            graph.replay()
-        g_wall = timed_steps(graph.replay, args.steps)
-        timing["graph_replay_ms_per_step"] = round(g_wall / args.steps * 1e3, 4)
-        print(f"[bench] same step replayed from a HIP graph: {g_wall / args.steps * 1e3:.3f} ms/step",
-              file=sys.stderr, flush=True)
-        del graph
+        if not args.no_graph:
+            # the same step replayed from a HIP graph, for comparison only
+            graph = capture(step)
+            for _ in range(args.warmup):
+                graph.replay()
+            g_wall = timed_steps(graph.replay, args.steps)
+            timing["graph_replay_ms_per_step"] = round(g_wall / args.steps * 1e3, 4)
+            print(f"[bench] same step replayed from a HIP graph: {g_wall / args.steps * 1e3:.3f} ms/step",
+                  file=sys.stderr, flush=True)
+            del graph
     else:
         eager = timed_steps(step, args.steps)
         timing["eager_ms_per_step"] = round(eager / args.steps * 1e3, 4)

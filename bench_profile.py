@@ -13,9 +13,12 @@
         --class "int4g32 m=1 k=4096=gemv_kernel<wq::FmtInt4, 1, 2, 2, 4, false>" \
         --cmd "<fetch command>" --cmd "<write command>" --out profiles/NAME.md
 
-The traffic summary also writes profiles/traffic.json, which bench.py reads
-for the roofline's `traffic` field while the kernel sources still hash to
-SOURCE_SHA.
+    # other counters (SQ_* instruction mix), one csv per pass
+    python bench_profile.py pmc PASS1.csv PASS2.csv --sha SOURCE_SHA --cmd ... --out profiles/NAME.md
+
+The traffic summary also merges its classes into profiles/traffic.json,
+which bench.py reads for the roofline's `traffic` field while the kernel
+sources still hash to SOURCE_SHA.
 """
 
 import argparse
@@ -33,6 +36,37 @@ def _short(name):
     return name.split("(")[0].replace("void ", "")
 
 
+def _per_matrix(rows, workload, steps):
+    """Per-matrix durations of a `--launch per-matrix` run: the first `steps`
+    steps' dispatches of the step kernels come in the workload's matrix order
+    (warmup and eager steps), so dispatch i is matrix i mod the step's count."""
+    import sys
+    sys.path.insert(0, ROOT)
+    from synth.workloads import WORKLOADS
+    from weight_only_quantized_wq_amd.layerset import matrix_bytes
+    wl = WORKLOADS[workload]
+    mats = wl.matrices()
+    ks = [r for r in rows if "wq::" in r["Kernel_Name"] and "quantize" not in r["Kernel_Name"]]
+    ks.sort(key=lambda r: int(r["Start_Timestamp"]))
+    ks = ks[:steps * len(mats)]
+    per = collections.defaultdict(list)
+    kern = {}
+    for i, r in enumerate(ks):
+        m = mats[i % len(mats)]
+        key = (m.name, m.n, m.k)
+        per[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        kern[key] = _short(r["Kernel_Name"])
+    lines = ["", f"## Per matrix (first {steps} steps of `{workload}`, one launch per matrix, in matrix order)", "",
+             "| matrix | n x k | kernel | launches | median us | GB/s (algorithmic) | % of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, n, k), v in per.items():
+        med = statistics.median(v)
+        b = matrix_bytes(wl.fmt, n, k, wl.m)
+        lines.append(f"| {name} | {n} x {k} | `{kern[(name, n, k)]}` | {len(v)} | {med / 1e3:.2f} | "
+                     f"{b / med:.0f} | {b / med / 8000 * 100:.1f} |")
+    return lines
+
+
 def trace(args):
     stats = list(csv.DictReader(open(args.stats)))
     rows = list(csv.DictReader(open(args.trace)))
@@ -42,7 +76,8 @@ def trace(args):
             continue
         d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
         per[(_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))].append(d)
-    lines = ["# rocprofv3 kernel trace: " + args.title, "", "Command (run from /tmp, repository root in $R):", "",
+    lines = ["# rocprofv3 kernel trace: " + args.title, "", f"Kernel sources: `{args.sha}` (bench.py `source_sha`).",
+             "", "Command (run from /tmp, repository root in $R):", "",
              "    " + args.cmd, "", "## Kernel stats (libwq kernels; all dispatches of the run)", "",
              "| kernel | calls | average ns | min ns | max ns | share of GPU time |", "|---|---|---|---|---|---|"]
     for s in stats:
@@ -53,6 +88,9 @@ def trace(args):
               "| kernel | workgroups | dispatches | mean us | median us |", "|---|---|---|---|---|"]
     for (k, wg), v in sorted(per.items()):
         lines.append(f"| `{k}` | {wg} | {len(v)} | {statistics.mean(v) / 1e3:.2f} | {statistics.median(v) / 1e3:.2f} |")
+    if args.per_matrix:
+        wl, steps = args.per_matrix.split(":")
+        lines += _per_matrix(rows, wl, int(steps))
     if args.bench_log:
         bl = [l.rstrip() for l in open(args.bench_log) if l.startswith("[bench]")]
         lines += ["", "## bench.py lines of the profiled run", ""] + ["    " + l for l in bl]
@@ -90,11 +128,49 @@ def traffic(args):
         table[cls] = {"kernel": kern, "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
                       "bytes_per_launch": int(fb + wb), "dispatches": len(fv)}
         lines.append(f"| {cls} | `{kern}` | {len(fv)} | {fb:.0f} | {wb:.0f} | {fb + wb:.0f} |")
+    lines = lines[:2] + [f"Kernel sources: `{args.sha}` (bench.py `source_sha`).", ""] + lines[2:]
     open(args.out, "w").write("\n".join(lines) + "\n")
-    doc = {"source_sha": args.sha, "fetch_scale": sf, "write_scale": sw, "kernels": table,
-           "summary": os.path.relpath(args.out, ROOT)}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+    # merge into profiles/traffic.json (entries of other sources are dropped)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        doc = json.load(open(path))
+    except (OSError, ValueError):
+        doc = {}
+    if doc.get("source_sha") != args.sha:
+        doc = {"source_sha": args.sha, "kernels": {}, "summaries": []}
+    for cls, e in table.items():
+        e["fetch_scale"], e["write_scale"] = sf, sw
+        e["summary"] = os.path.relpath(args.out, ROOT)
+        doc["kernels"][cls] = e
+    doc.setdefault("summaries", [])
+    if os.path.relpath(args.out, ROOT) not in doc["summaries"]:
+        doc["summaries"].append(os.path.relpath(args.out, ROOT))
+    with open(path, "w") as fh:
         json.dump(doc, fh, indent=1)
+    print(args.out)
+
+
+def pmc(args):
+    """Per-kernel means of arbitrary counters (one or more counter csv files)."""
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in args.csv:
+        for r in csv.DictReader(open(path)):
+            if "wq::" not in r["Kernel_Name"] or "quantize" in r["Kernel_Name"]:
+                continue
+            key = f"{_short(r['Kernel_Name'])} ({int(r['Grid_Size']) // int(r['Workgroup_Size'])} workgroups)"
+            agg[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for k in agg for c in agg[k]})
+    lines = ["# rocprofv3 counters: " + args.title, "", f"Kernel sources: `{args.sha}` (bench.py `source_sha`).", "",
+             "Commands (run from /tmp, repository root in $R):", ""] + ["    " + c for c in args.cmd] + [
+             "", "Mean per dispatch (counters summed over the device).", "",
+             "| kernel | dispatches | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for k in sorted(agg):
+        n = max(len(v) for v in agg[k].values())
+        lines.append(f"| `{k}` | {n} | " + " | ".join(f"{statistics.mean(agg[k][c]):.4g}" if agg[k].get(c) else ""
+                                                   for c in names) + " |")
+    if args.note:
+        lines += ["", args.note]
+    open(args.out, "w").write("\n".join(lines) + "\n")
     print(args.out)
 
 
@@ -107,6 +183,8 @@ def main():
     t.add_argument("--bench-log")
     t.add_argument("--cmd", required=True)
     t.add_argument("--title", default="bench.py")
+    t.add_argument("--sha", default="")
+    t.add_argument("--per-matrix", help="WORKLOAD:STEPS -- per-matrix table of a --launch per-matrix run")
     t.add_argument("--out", required=True)
     c = sub.add_parser("traffic")
     c.add_argument("fetch")
@@ -116,8 +194,15 @@ def main():
     c.add_argument("--cmd", action="append", required=True)
     c.add_argument("--title", default="bench.py")
     c.add_argument("--out", required=True)
+    q = sub.add_parser("pmc")
+    q.add_argument("csv", nargs="+")
+    q.add_argument("--sha", required=True)
+    q.add_argument("--cmd", action="append", required=True)
+    q.add_argument("--title", default="bench.py")
+    q.add_argument("--note", default="")
+    q.add_argument("--out", required=True)
     a = p.parse_args()
-    trace(a) if a.what == "trace" else traffic(a)
+    {"trace": trace, "traffic": traffic, "pmc": pmc}[a.what](a)
 
 
 if __name__ == "__main__":

@@ -75,11 +75,20 @@ def test_traffic_summary_scales_counters_by_the_copy_kernel(tmp_path, monkeypatc
     bench_profile.traffic(args)
     doc = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
     assert doc["source_sha"] == "s1"
-    assert doc["fetch_scale"] == pytest.approx(2.0) and doc["write_scale"] == pytest.approx(1.0)
     e = doc["kernels"]["cls"]
+    assert e["fetch_scale"] == pytest.approx(2.0) and e["write_scale"] == pytest.approx(1.0)
     assert e["fetch_bytes_per_launch"] == int(1001 * 1024 * 2.0)
     assert e["write_bytes_per_launch"] == 10 * 1024
     assert e["dispatches"] == 2
+    # a second summary of the same sources merges; another source starts over
+    args.klass, args.out = ["cls2=some_kernel<1>"], str(tmp_path / "profiles" / "y.md")
+    bench_profile.traffic(args)
+    doc = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
+    assert set(doc["kernels"]) == {"cls", "cls2"} and len(doc["summaries"]) == 2
+    args.sha = "s2"
+    bench_profile.traffic(args)
+    doc = json.loads((tmp_path / "profiles" / "traffic.json").read_text())
+    assert doc["source_sha"] == "s2" and set(doc["kernels"]) == {"cls2"}
 
 
 @pytest.mark.parametrize("fmt,group", [("int4g32", 32), ("int4g64", 64), ("int4g128", 128), ("int4g256", 256),

@@ -305,6 +305,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   memcpy(host.data() + lay.bal, &bal, sizeof(bal));
   VerifyBalance vbal{};
   vbal.f = kVerifyLongRowPrior;
+  for (int x = 0; x < 8; ++x) vbal.w[x] = 1.0f;
   memcpy(host.data() + lay.vbal, &vbal, sizeof(vbal));
   hipError_t e = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {

@@ -258,10 +258,9 @@ struct StepCuts {
   int32_t count;          // matrices
 };
 
-// Cost at which workgroup g's range starts: the step's cost times the share
-// of the speed weights of workgroups 0 .. g-1, workgroup j weighing the
-// speed of XCD (j + off) mod 8.
-__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int off, int g, int groups) {
+// Share of a launch's work before workgroup g when workgroup j weighs the
+// speed of XCD (j + off) mod 8 (`groups` workgroups in all).
+__device__ __forceinline__ double xcd_share(const float (&w)[8], int off, int g, int groups) {
   double sw = 0.0, part = 0.0, full = 0.0;
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
@@ -272,7 +271,48 @@ __device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8
   }
   const double before = (double)(g / 8) * sw + part;
   const double all = (double)(groups / 8) * sw + full;
-  return c.prefix[c.count] * (before / all);
+  return before / all;
+}
+
+// Cost at which workgroup g's range starts: the step's cost times the share
+// of the speed weights of workgroups 0 .. g-1.
+__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int off, int g, int groups) {
+  return c.prefix[c.count] * xcd_share(w, off, g, groups);
+}
+
+// The last workgroup of a launch: new XCD speed weights from the cost each
+// XCD streamed and the time its workgroups took (a quarter of the way to the
+// measured rates, clamped to [0.7, 1.3], mean 1), the dispatch offset this
+// launch saw, and the sums cleared for the next launch.
+__device__ __forceinline__ void xcd_update(float* wv, float* cost, float* time, int32_t* xoff, const float (&w)[8],
+                                           int observed_off) {
+  float r[8], wn[8];
+  float mean = 0.0f;
+  int n = 0;
+  for (int y = 0; y < 8; ++y) {
+    const float cy = __hip_atomic_load(&cost[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float ty = __hip_atomic_load(&time[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    r[y] = (ty > 0.0f && cy > 0.0f) ? cy / ty : 0.0f;
+    if (r[y] > 0.0f) {
+      mean += r[y];
+      ++n;
+    }
+  }
+  mean = n ? mean / (float)n : 0.0f;
+  float sw = 0.0f;
+  for (int y = 0; y < 8; ++y) {
+    float v = w[y];
+    if (mean > 0.0f && r[y] > 0.0f) v = 0.75f * w[y] + 0.25f * (r[y] / mean);
+    v = fminf(fmaxf(v, 0.7f), 1.3f);
+    wn[y] = v;
+    sw += v;
+  }
+  for (int y = 0; y < 8; ++y) {
+    atomicExch(&wv[y], wn[y] * 8.0f / sw);
+    atomicExch(&cost[y], 0.0f);
+    atomicExch(&time[y], 0.0f);
+  }
+  atomicExch(xoff, observed_off);
 }
 
 // The persistent step's frame.  Each workgroup cuts its own contiguous range
@@ -343,33 +383,7 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
     if (atomicAdd(&b->done, 1) == G - 1) {
       // every workgroup has reported: new speed weights for the next launch
       __threadfence();
-      float r[8], wn[8];
-      float mean = 0.0f;
-      int n = 0;
-      for (int y = 0; y < 8; ++y) {
-        const float cy = __hip_atomic_load(&b->cost[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float ty = __hip_atomic_load(&b->time[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        r[y] = (ty > 0.0f && cy > 0.0f) ? cy / ty : 0.0f;
-        if (r[y] > 0.0f) {
-          mean += r[y];
-          ++n;
-        }
-      }
-      mean = n ? mean / (float)n : 0.0f;
-      float sw = 0.0f;
-      for (int y = 0; y < 8; ++y) {
-        float v = w[y];
-        if (mean > 0.0f && r[y] > 0.0f) v = 0.75f * w[y] + 0.25f * (r[y] / mean);
-        v = fminf(fmaxf(v, 0.7f), 1.3f);
-        wn[y] = v;
-        sw += v;
-      }
-      for (int y = 0; y < 8; ++y) {
-        atomicExch(&b->w[y], wn[y] * 8.0f / sw);
-        atomicExch(&b->cost[y], 0.0f);
-        atomicExch(&b->time[y], 0.0f);
-      }
-      atomicExch(&b->xoff, (x - (int)(blockIdx.x % 8) + 8) & 7);
+      xcd_update(b->w, b->cost, b->time, &b->xoff, w, (x - (int)(blockIdx.x % 8) + 8) & 7);
       atomicExch(&b->done, 0);
     }
   }

@@ -435,12 +435,18 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
 // of the way to the measured ratio of the two rates (clamped to [0.5, 4]);
 // the next launch cuts with it.  Which workgroup computes a row never changes
 // the row's result.
+//
+// On top of that, ranges follow the speeds of the XCDs the workgroups run on,
+// measured per launch as in the one-token step (xcd_share / xcd_update).
 struct VerifyBalance {
   double f;
   double t[2];      // this launch: wall-clock ticks spent on short / long rows
   double c[2];      // this launch: bytes of short / long rows streamed
   int32_t done;     // workgroups finished in this launch
-  int32_t pad[3];
+  int32_t xoff;     // dispatch offset the last launch observed (workgroup g on XCD (g + xoff) mod 8)
+  float w[8];       // relative speed of each XCD's workgroups (mean 1), by hardware XCD id
+  float xcost[8];   // this launch: cost (units of the cut) streamed by each XCD's workgroups
+  float xtime[8];   // this launch: their summed durations (wall-clock ticks)
 };
 
 struct VerifyCuts {
@@ -475,12 +481,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   uint32_t (*szb)[16][kSzRow] = szs[wave];
   const FmtInt4::K kc = FmtInt4::consts();
 
-  // this workgroup's range: equal shares of the step's cost
+  // this workgroup's range: its XCD-speed-weighted share of the step's cost
+  const long long t_start = wall_clock64();
   const double f = cuts.bal->f;
+  float xw[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) xw[x] = cuts.bal->w[x];
+  const int xoff = cuts.bal->xoff & 7;
   const int G = (int)gridDim.x;
   const double total = cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count];
-  const double c0 = total * (double)blockIdx.x / (double)G;
-  const double c1 = (int)blockIdx.x + 1 == G ? total : total * (double)(blockIdx.x + 1) / (double)G;
+  const double c0 = total * xcd_share(xw, xoff, (int)blockIdx.x, G);
+  const double c1 = (int)blockIdx.x + 1 == G ? total : total * xcd_share(xw, xoff, (int)blockIdx.x + 1, G);
   if (threadIdx.x == 0) {
     range[0] = mats[cuts.count - 1].batch_begin + mats[cuts.count - 1].batches;
     range[1] = range[0];
@@ -575,10 +586,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
       atomicAdd(&b->t[e], tk[e]);
       atomicAdd(&b->c[e], ck[e]);
     }
+    const int x = hw_xcd_id();
+    atomicAdd(&b->xcost[x], (float)(c1 - c0));
+    atomicAdd(&b->xtime[x], (float)(wall_clock64() - t_start));
     __threadfence();
     if (atomicAdd(&b->done, 1) == G - 1) {
-      // every workgroup has reported: the factor for the next launch
+      // every workgroup has reported: the factors for the next launch
       __threadfence();
+      xcd_update(b->w, b->xcost, b->xtime, &b->xoff, xw, (x - (int)(blockIdx.x % 8) + 8) & 7);
       double t[2], c[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {

@@ -109,8 +109,10 @@ def _counter(path, cname):
 def traffic(args):
     f = _counter(args.fetch, "FETCH_SIZE")
     w = _counter(args.write, "WRITE_SIZE")
-    copy_f = statistics.mean(f["__amd_rocclr_copyBuffer"]) * 1024
-    copy_w = statistics.mean(w["__amd_rocclr_copyBuffer"]) * 1024
+    # the calibration copy is the largest device copy of the run (a workload
+    # may copy smaller buffers while it is built)
+    copy_f = max(f["__amd_rocclr_copyBuffer"]) * 1024
+    copy_w = max(w["__amd_rocclr_copyBuffer"]) * 1024
     sf, sw = COPY_BYTES / copy_f, COPY_BYTES / copy_w
     table = {}
     lines = ["# rocprofv3 HBM traffic: " + args.title, "", "Commands (run from /tmp, repository root in $R):", ""]

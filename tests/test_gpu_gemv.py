@@ -127,13 +127,15 @@ def test_gemv_int4g32(wq, n, k):
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 
 
-# m >= 3 runs on the matrix cores with K windows of 256 groups: the cases
+# m >= 2 runs on the matrix cores with K windows of 256 groups: the cases
 # cover one window, several, a ragged last window (k = 8288, 12352, 8224),
-# matrices with more row blocks than resident workgroups, and k = 0
+# matrices with more row blocks than resident workgroups (3 to 7 blocks per
+# workgroup with 1 to 16 items each, ragged last blocks), and k = 0
 SMALLM_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 32), (70, 8192)]] + \
     [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 3, 4, 5, 7, 8)] + \
     [(5, 8, 32768), (1, 10, 131072), (5, 6, 131072), (5, 50, 8288), (7, 37, 12352), (3, 100, 8224),
-    (2, 9, 0), (6, 9, 0), (5, 16411, 512), (3, 18000, 8224), (8, 17000, 4128), (2, 20000, 16416)]
+    (2, 9, 0), (6, 9, 0), (5, 16411, 512), (3, 18000, 8224), (8, 17000, 4128), (2, 20000, 16416),
+    (5, 31990, 1024), (6, 55999, 1024), (2, 23999, 4096), (4, 39995, 256), (3, 40000, 2048)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALLM_CASES)

@@ -207,3 +207,47 @@ def test_step_balance_never_changes_results(fmt, m):
     torch.cuda.synchronize()
     for mt, (f32, _) in zip(mats, first):
         assert np.array_equal(host(mt[5]), f32), "a fresh plan differs"
+
+
+# The balance state sits at the end of a step workspace: the XCD state of
+# the one-token and int8 2..8-row kernels (128 bytes: float w[8], cost[8],
+# time[8], int32 done, xoff, pad[6]), then the verify kernel's (144 bytes:
+# double f, t[2], c[2], int32 done, xoff, float w[8], xcost[8], xtime[8]).
+_STEP_BAL, _VERIFY_BAL = 128, 144
+
+
+@pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 5), ("int4g32", 5)])
+def test_step_balance_feedback_runs(fmt, m):
+    """The last workgroup of every launch turns the launch's reports into the
+    next launch's factors and clears the sums: after several launches the
+    counters and sums are zero again, the XCD weights keep mean 1 within
+    their clamp's range, and (verify kernel, short and long rows in one plan) the
+    long-row factor has left its prior of 1.2.  A report lost or counted
+    twice would leave `done` non-zero."""
+    import torch
+    import weight_only_quantized_wq_amd as wq
+    say(f"balance feedback {fmt} m={m}")
+    mats, _ = _build(fmt, m, 3)
+    nbytes = wq.wq_decode_step_workspace_bytes(len(mats))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    plan = wq.wq_decode_step_prepare(fmt, m, mats, ws)
+    for _ in range(12):
+        wq.wq_decode_step_run(plan)
+    torch.cuda.synchronize()
+    tail = ws[nbytes - _STEP_BAL - _VERIFY_BAL:].cpu().numpy()
+    sb, vb = tail[:_STEP_BAL], tail[_STEP_BAL:]
+    verify = fmt.startswith("int4") and m > 1
+    if verify:
+        f, t0, t1, c0, c1 = np.frombuffer(vb[:40].tobytes(), dtype=np.float64)
+        done, xoff = np.frombuffer(vb[40:48].tobytes(), dtype=np.int32)
+        w, xcost, xtime = np.frombuffer(vb[48:144].tobytes(), dtype=np.float32).reshape(3, 8)
+        assert (t0, t1, c0, c1) == (0.0, 0.0, 0.0, 0.0)
+        assert 0.5 <= f <= 4.0 and f != 1.2, f"long-row factor {f}"
+    else:
+        w, xcost, xtime = np.frombuffer(sb[:96].tobytes(), dtype=np.float32).reshape(3, 8)
+        done, xoff = np.frombuffer(sb[96:104].tobytes(), dtype=np.int32)
+    assert done == 0, f"{done} reports left over"
+    assert 0 <= xoff < 8
+    assert not xcost.any() and not xtime.any()
+    # clamped to [0.7, 1.3], then scaled to mean 1
+    assert np.all((w >= 0.57) & (w <= 1.68)) and abs(float(w.sum()) - 8.0) < 1e-3, w

@@ -280,6 +280,16 @@ __device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8
   return c.prefix[c.count] * xcd_share(w, off, g, groups);
 }
 
+// A workgroup's balance report: its sums are atomics, counted in by the
+// `done` atomic after them, and the last workgroup reads them back with
+// agent-scope atomic loads.  The only order needed is "sums performed before
+// the count", which a wait for this wave's outstanding memory operations
+// gives; an agent-scope fence would add an L2 write-back and invalidate per
+// workgroup (several microseconds at the end of every launch).  A report
+// that came late would only blur one launch's weights: the cuts are valid
+// for any weights.
+__device__ __forceinline__ void report_in_order() { wait_vmem_all(); }
+
 // The last workgroup of a launch: new XCD speed weights from the cost each
 // XCD streamed and the time its workgroups took (a quarter of the way to the
 // measured rates, clamped to [0.7, 1.3], mean 1), the dispatch offset this
@@ -379,10 +389,9 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
     const int x = hw_xcd_id();
     atomicAdd(&b->cost[x], (float)(c1 - c0));
     atomicAdd(&b->time[x], (float)(wall_clock64() - t_start));
-    __threadfence();
+    report_in_order();
     if (atomicAdd(&b->done, 1) == G - 1) {
       // every workgroup has reported: new speed weights for the next launch
-      __threadfence();
       xcd_update(b->w, b->cost, b->time, &b->xoff, w, (x - (int)(blockIdx.x % 8) + 8) & 7);
       atomicExch(&b->done, 0);
     }

@@ -589,10 +589,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
     const int x = hw_xcd_id();
     atomicAdd(&b->xcost[x], (float)(c1 - c0));
     atomicAdd(&b->xtime[x], (float)(wall_clock64() - t_start));
-    __threadfence();
+    report_in_order();
     if (atomicAdd(&b->done, 1) == G - 1) {
       // every workgroup has reported: the factors for the next launch
-      __threadfence();
       xcd_update(b->w, b->xcost, b->xtime, &b->xoff, xw, (x - (int)(blockIdx.x % 8) + 8) & 7);
       double t[2], c[2];
 #pragma unroll

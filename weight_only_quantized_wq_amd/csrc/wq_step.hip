@@ -126,8 +126,8 @@ static bool pick_variant(int format, int m, StepVariant& v) {
       case 3: v = verify_variant<3, 8, 2, 4, kVerifyKW, true>(); break;
       case 4: v = verify_variant<4, 12, kVerifyRT, kVerifyOct, kVerifyKW, true>(); break;
       case 5: v = verify_variant<5, 8, 2, 4, kVerifyKW, true>(); break;
-      case 6: v = verify_variant<6, 8, 2, 4>(); break;
-      case 7: v = verify_variant<7, 6, 2, 4>(); break;
+      case 6: v = verify_variant<6, 8, 2, 4, 224, true>(); break;   // windows of 224 / 192 groups leave room
+      case 7: v = verify_variant<7, 8, 2, 4, 192, true>(); break;   // for the code tiles
       case 8: v = verify_variant<8, 8, 2, 4, 160, true>(); break;   // window of 160 groups leaves room for the tile
       default: return false;
     }

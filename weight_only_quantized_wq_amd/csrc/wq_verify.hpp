@@ -16,9 +16,13 @@
 //   * So D[4 * slot + t][n] is token t's dot product with ONE group of row n,
 //     and lane l holds D rows 4 (l / 16) + r, column l % 16: the four tokens'
 //     sums for exactly the (row, group) whose codes and (scale, zero) word it
-//     loaded itself.  The group's scale and zero are applied exactly:
-//     y_t += s * D + (z - 128 s) * (sum of the group's activations of t).
-// Tokens 4..7 use a second set of MFMAs (same B, second A).
+//     loaded itself, and it adds s * D with the group's scale.
+// With 5..8 tokens A rows 8 s + t cover all tokens over TWO group slots
+// (k-slots 2 s, 2 s + 1; verify_a_wide), which halves the MFMAs.  Each
+// MFMA sum starts at -128 X (X the group's activation sum of the token), so
+// the decode's 128 offset cancels inside it, group by group; the lane adds
+// s * (D - 128 X), and the zero points, z X summed over 32 groups, are one
+// more MFMA per 32 groups (verify_zero_term).
 //
 // Work decomposition: one workgroup per CU owns a contiguous range of the
 // step's blocks of RT 16-row tiles (equal weight bytes per workgroup, cut on
@@ -45,15 +49,29 @@ constexpr int kVerifyMaxK = 131072;
 
 typedef __bf16 vbf16x8 __attribute__((ext_vector_type(8)));
 typedef float vf32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Activations of one K window for up to M tokens.  Token rows are padded by
 // 16 bytes so the four tokens one k-slot reads sit in different banks.
 template <int M, int KW>
 struct alignas(16) VerifyShared {
   static constexpr int kSets = (M + 3) / 4;
+  // 5..8 tokens: one MFMA serves all tokens over two group slots ("wide");
+  // A operands [pair][half] instead of [set][MFMA], one accumulator set per
+  // lane (its four tokens)
+  static constexpr bool kWide = M > 4;
+  static constexpr int kA1 = kWide ? 2 : kSets;
+  static constexpr int kA2 = kWide ? 2 : 4;
+  static constexpr int kYS = kWide ? 1 : kSets;
   static constexpr int kRow = KW * 16 + 4;
+  static constexpr int kZRows = kWide ? 16 : 8;   // A rows of the zero-point product: lo * kZLo + token
+  static constexpr int kZLo = kWide ? 8 : 4;
+  static constexpr int kSumRow = KW + 8;          // bf16 per row of xz (rows 16 bytes apart in bank)
   uint32_t xs[M][kRow];          // pre-permuted bf16 pairs, 16 words per group
-  float gs[KW][kSets][4];        // per-group activation sums, [group][set][token in set]
+  float gs[KW][kSets][4];        // -128 x the per-group activation sums, [group][set][token in set]
+  // the per-group activation sums X as an exact bf16 pair hi + lo
+  // (|X - hi - lo| <= 2^-18 |X|); rows of tokens past M are zero
+  alignas(16) uint16_t xz[kZRows][kSumRow];
 };
 
 template <int RT, int OCT>
@@ -86,26 +104,84 @@ __device__ __forceinline__ vf32x4 mfma16x16x32(const uint32_t (&a)[4], const uin
                                                  0, 0, 0);
 }
 
-// Stages groups [g0, g0 + kpad) of every token; groups at or past the row's
-// end are zero.
+// Stages groups [g0, g0 + kpad) of every token and their sums over whole
+// (scale, zero) windows (kpad rounded up to kSzWin); groups at or past the
+// row's end are zero.
 template <int M, int KW, int THREADS>
 __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad, VerifyShared<M, KW>& sh) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
+  constexpr int ZLO = VerifyShared<M, KW>::kZLo;
+  const int kz = (kpad + kSzWin - 1) / kSzWin * kSzWin;
 #pragma unroll 1
-  for (int it = threadIdx.x; it < 4 * SETS * kpad; it += THREADS) {
-    const int t = it / kpad;
-    const int g = it - t * kpad;
+  for (int it = threadIdx.x; it < ZLO * kz; it += THREADS) {
+    const int t = it / kz;
+    const int g = it - t * kz;
     const int gg = g0 + g;
+    uint16_t hi = 0, lo = 0;
+    float gsum = 0.0f;
     if (t < M) {
-      const FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, gg, gg < a.chunks);
+      const FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, gg, gg < a.chunks && g < kpad);
+      if (g < kpad) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        *reinterpret_cast<u32x4*>(&sh.xs[t][16 * g + 4 * h]) =
-            u32x4{xv.p[4 * h], xv.p[4 * h + 1], xv.p[4 * h + 2], xv.p[4 * h + 3]};
-      sh.gs[g][t >> 2][t & 3] = xv.gsum;
-    } else {
-      sh.gs[g][t >> 2][t & 3] = 0.0f;
+        for (int h = 0; h < 4; ++h)
+          *reinterpret_cast<u32x4*>(&sh.xs[t][16 * g + 4 * h]) =
+              u32x4{xv.p[4 * h], xv.p[4 * h + 1], xv.p[4 * h + 2], xv.p[4 * h + 3]};
+      }
+      gsum = xv.gsum;
+      hi = f32_to_bf16(gsum);
+      lo = f32_to_bf16(gsum - __uint_as_float((uint32_t)hi << 16));
     }
+    if (t < 4 * SETS && g < kpad) sh.gs[g][t >> 2][t & 3] = -128.0f * gsum;
+    sh.xz[t][g] = hi;
+    sh.xz[ZLO + t][g] = lo;
+  }
+}
+
+// The zero points of a (scale, zero) window for the wave's block.  A group
+// contributes s * (D - 128 X) + z * X to each token (D = sum of (128 + q) x
+// from the MFMAs, whose accumulators start at -128 X, X the group's
+// activation sum); the z * X terms of the window's 32 groups are one more
+// MFMA: A = X (rows kZLo lo + t: its hi and lo bf16 parts, exact), B = the
+// groups' zero points (bf16, exact).  Lane (rq, col) receives rows 4 rq + r:
+// in the wide layout tokens 4 (rq % 2) + r, hi for rq < 2 and lo otherwise;
+// with up to four tokens token r, hi for rq = 0 and lo for rq = 1 (rows 8..15
+// zero) -- in both the tokens of its own accumulators, so the slot sums of
+// the fold add hi and lo.  il: the window's first group in the activation
+// window; chunk i of the window uses (scale, zero) word i >> gshift.
+template <int M, int KW, int RT, int YS>
+__device__ __forceinline__ void verify_zero_term(const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
+                                                 int il, int gshift, int rq, int col, float (&y)[RT][YS][4]) {
+  static_assert(YS == 1, "one accumulator set per lane (at most four tokens, or the wide layout)");
+  // the window's words were stored by other lanes of the wave (sz_put)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int ZR = VerifyShared<M, KW>::kZRows;
+  uint32_t av[4] = {0u, 0u, 0u, 0u};
+  if (col < ZR) {
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(&sh.xz[col < ZR ? col : 0][il + 8 * rq]);
+    av[0] = xa[0];
+    av[1] = xa[1];
+    av[2] = xa[2];
+    av[3] = xa[3];
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    uint32_t w[8];
+    if (gshift == 0) {
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(&szb[rt][col][8 * rq]);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(&szb[rt][col][8 * rq + 4]);
+      w[0] = w0[0]; w[1] = w0[1]; w[2] = w0[2]; w[3] = w0[3];
+      w[4] = w1[0]; w[5] = w1[1]; w[6] = w1[2]; w[7] = w1[3];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = szb[rt][col][(8 * rq + i) >> gshift];
+    }
+    uint32_t bz[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bz[j] = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x07060302u);   // (z_2j, z_2j+1)
+    const vf32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const vf32x4 dz = mfma16x16x32(av, bz, zero4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[rt][0][r] += dz[r];
   }
 }
 
@@ -209,7 +285,7 @@ __device__ __forceinline__ uint32_t to_mfma_lane(uint32_t v, int src_addr) {
 // keeps the zeros it was created with, so they touch no LDS.
 template <int M, int KW>
 __device__ __forceinline__ void verify_a(const VerifyShared<M, KW>& sh, int ga, int rq, int col,
-                                         uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4]) {
+                                         uint32_t (&av)[VerifyShared<M, KW>::kA1][VerifyShared<M, KW>::kA2][4]) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
 #pragma unroll
   for (int st = 0; st < SETS; ++st) {
@@ -227,12 +303,98 @@ __device__ __forceinline__ void verify_a(const VerifyShared<M, KW>& sh, int ga, 
   }
 }
 
+// Wide layout (5..8 tokens): A row 8 s + t is token t restricted to group
+// slot s (k-slots 2 s and 2 s + 1).  MFMA (pair p, half h) of quad [gq, gq +
+// 4) covers groups gq + 2 p + s, k-slot 2 s + e holding 32-bit code word
+// 2 e + h of its group -- inputs 8 (2 e + h) .. + 7, activation pair words
+// 4 (2 e + h) .. + 3.  Lane (rq, col) carries data when col / 8 == rq / 2
+// (its slot) and token col % 8 exists; the others keep zeros and read nothing.
+template <int M, int KW>
+__device__ __forceinline__ void verify_a_wide(const VerifyShared<M, KW>& sh, int gq, int rq, int col,
+                                              uint32_t (&av)[2][2][4]) {
+  const int s = rq >> 1, e = rq & 1, t = col & 7;
+  if ((col >> 3) == s && t < M) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int ga = gq + 2 * p + s;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&sh.xs[t < M ? t : 0][16 * ga + 8 * e + 4 * h]);
+        av[p][h][0] = v[0];
+        av[p][h][1] = v[1];
+        av[p][h][2] = v[2];
+        av[p][h][3] = v[3];
+      }
+    }
+  }
+}
+
 // LT: a 16-row x 128-byte tile of codes per wave.  The 16-byte slots of a
 // row are XOR-swizzled by row pair (slot p of row r at p ^ (r / 2 % 8)), so
 // the stores (two rows of 8 slots per 16 lanes) and the reads (one slot of
 // 16 rows) fall in distinct banks.
 constexpr int kVerifyTile = 16 * 128;
 __device__ __forceinline__ int verify_tile_at(int row, int slot) { return row * 128 + ((slot ^ ((row >> 1) & 7)) << 4); }
+
+// Wide layout (5..8 tokens; see verify_a_wide): before quads o and o + 1
+// (o even) each tile's loads o and o + 1 pass through the wave's LDS tile as
+// in the four-token layout, and lane (rq, col) reads back, for quad o + h and
+// pair p, bytes 8 e .. 8 e + 7 (code words 2 e and 2 e + 1) of group
+// 4 h + 2 p + rq / 2 of row col (e = rq % 2).  D rows 8 s + 4 e + r of column
+// col: tokens 4 e + r of (row col, group 2 p + s) minus 128 X, scaled by the
+// lane's own scale (z X comes from verify_zero_term).  Tokens past M have
+// zero activations and sums, so their accumulators stay zero and are never
+// stored.
+template <int M, int KW, int RT, int OCT>
+__device__ __forceinline__ void verify_item_wide(const VerifyItem<RT, OCT>& q, int il, int iz, int gshift, int rq,
+                                                 int col, const VerifyShared<M, KW>& sh,
+                                                 const uint32_t (*szb)[16][kSzRow], const FmtInt4::K& kc,
+                                                 uint32_t (&av)[2][2][4], float (&y)[RT][1][4], uint8_t* tile) {
+  static_assert(OCT % 2 == 0, "line-wide loads come in pairs");
+  const int wr = rq * 2 + (col >> 3), ws = col & 7;   // tile store: row wr (+ 8), slot ws (lane = 16 rq + col)
+  const int s = rq >> 1, e = rq & 1;
+  u32x2 wl[RT][2][2];
+#pragma unroll
+  for (int o = 0; o < OCT; ++o) {
+    if ((o & 1) == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        // lanes read what other lanes stored: the wave barriers keep the
+        // compiler from reordering these LDS accesses across lanes' roles
+        __builtin_amdgcn_wave_barrier();
+        *reinterpret_cast<u32x4*>(tile + verify_tile_at(wr, ws)) = q.w[rt][o];
+        *reinterpret_cast<u32x4*>(tile + verify_tile_at(wr + 8, ws)) = q.w[rt][o + 1];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            wl[rt][h][p] = *reinterpret_cast<const u32x2*>(tile + verify_tile_at(col, 4 * h + 2 * p + s) + 8 * e);
+      }
+    }
+    verify_a_wide<M, KW>(sh, il + 4 * o, rq, col, av);
+    vf32x4 c0[2];   // -128 X of the lane's tokens and group: the MFMA sums start there
+#pragma unroll
+    for (int p = 0; p < 2; ++p) c0[p] = *reinterpret_cast<const vf32x4*>(&sh.gs[il + 4 * o + 2 * p + s][e][0]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const float sc = __uint_as_float(szb[rt][col][(iz + 4 * o + 2 * p + s) >> gshift] << 16);
+        vf32x4 acc = c0[p];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t v = wl[rt][o & 1][p][h];
+          const uint32_t bv[4] = {(v & kc.mask) | FmtInt4::kMagic, ((v >> 4) & kc.mask) | FmtInt4::kMagic,
+                                  ((v >> 8) & kc.mask) | FmtInt4::kMagic, ((v >> 12) & kc.mask) | FmtInt4::kMagic};
+          acc = mfma16x16x32(av[p][h], bv, acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[rt][0][r] = fmaf(sc, acc[r], y[rt][0][r]);
+      }
+    }
+  }
+}
 
 // Accumulates one item into y[tile][set][token]; `il` is the item's first
 // chunk within the staged activation window and `iz` within the (scale,
@@ -245,9 +407,16 @@ __device__ __forceinline__ int verify_tile_at(int row, int slot) { return row * 
 template <int M, int KW, int RT, int OCT, bool LT>
 __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il, int iz, int gshift, int rq,
                                             int col, const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
-                                            const FmtInt4::K& kc, uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
-                                            float (&y)[RT][VerifyShared<M, KW>::kSets][4], uint8_t* tile) {
+                                            const FmtInt4::K& kc,
+                                            uint32_t (&av)[VerifyShared<M, KW>::kA1][VerifyShared<M, KW>::kA2][4],
+                                            float (&y)[RT][VerifyShared<M, KW>::kYS][4], uint8_t* tile) {
   constexpr int SETS = VerifyShared<M, KW>::kSets;
+  if (iz == 0) verify_zero_term<M, KW, RT, VerifyShared<M, KW>::kYS>(sh, szb, il, gshift, rq, col, y);
+  if constexpr (VerifyShared<M, KW>::kWide) {
+    static_assert(LT, "the wide layout reads its codes from the LDS tile");
+    verify_item_wide<M, KW, RT, OCT>(q, il, iz, gshift, rq, col, sh, szb, kc, av, y, tile);
+    return;
+  } else {
   const int src = (4 * col + rq) * 4;   // byte address of the lane holding this lane's codes (!LT)
   const int wr = rq * 2 + (col >> 3), ws = col & 7;   // LT store: row wr (+ 8), slot ws (lane = 16 rq + col)
   u32x4 wl[RT][2];
@@ -268,11 +437,10 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
         }
       }
     }
-    const int g = il + 4 * o + rq;              // this lane's group (activation window)
     verify_a<M, KW>(sh, il + 4 * o + (col >> 2), rq, col, av);
-    vf32x4 xs4[SETS];
+    vf32x4 c0[SETS];   // -128 X of the lane's tokens and group: the MFMA sums start there
 #pragma unroll
-    for (int st = 0; st < SETS; ++st) xs4[st] = *reinterpret_cast<const vf32x4*>(&sh.gs[g][st][0]);
+    for (int st = 0; st < SETS; ++st) c0[st] = *reinterpret_cast<const vf32x4*>(&sh.gs[il + 4 * o + rq][st][0]);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       u32x4 w = q.w[rt][o];
@@ -286,10 +454,9 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
       FmtInt4::D d;
       FmtInt4::decode(w, d, kc);
       const float s = __uint_as_float(szw << 16);
-      const float zb = fmaf(-128.0f, s, __uint_as_float(szw & 0xFFFF0000u));
 #pragma unroll
       for (int st = 0; st < SETS; ++st) {
-        vf32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        vf32x4 acc = c0[st];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t bv[4] = {d.t[4 * j], d.t[4 * j + 1], d.t[4 * j + 2], d.t[4 * j + 3]};
@@ -297,10 +464,11 @@ __device__ __forceinline__ void verify_item(const VerifyItem<RT, OCT>& q, int il
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (4 * st + r < M) y[rt][st][r] = fmaf(zb, xs4[st][r], fmaf(s, acc[r], y[rt][st][r]));
+          if (4 * st + r < M) y[rt][st][r] = fmaf(s, acc[r], y[rt][st][r]);
         }
       }
     }
+  }
   }
 }
 
@@ -320,9 +488,38 @@ struct VerifyPart {
 // fixed order, adds the block's earlier windows (!first) and stores the rows
 // (last) or keeps the running sum for the next window; zeroes y.  The sum of
 // a row is taken window by window in order, whichever wave streams them.
+// Wide layout: lanes col + 16 e and col + 16 (2 + e) hold the two group
+// slots of tokens 4 e + r.
 template <int M, int RT, int SETS, int SR>
 __device__ __forceinline__ void verify_fold(const GemvArgs& a, int64_t blk, int bi, bool first, bool last, int rq,
                                             int col, float (&y)[RT][SETS][4], VerifyPart<M, RT, SR>& part) {
+  if constexpr (M > 4) {
+    static_assert(SETS == 1, "wide accumulators: one set of four tokens per lane");
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[rt][0][r] += __shfl_xor(y[rt][0][r], 32);
+      const int64_t row = (blk * RT + rt) * 16 + col;
+      if (rq < 2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * rq + r;
+          if (t >= M) continue;
+          float v = y[rt][0][r];
+          if (!first) v = part.v[bi][rt * 16 + col][t] + v;
+          if (!last) {
+            part.v[bi][rt * 16 + col][t] = v;
+          } else if (row < a.n) {
+            if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = v;
+            if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(v);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[rt][0][r] = 0.0f;
+    }
+    return;
+  }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -371,10 +568,10 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
                                               bool first, bool last, int* ctr, int lane, int rq, int col,
                                               const VerifyShared<M, KW>& sh, uint32_t (*szb)[16][kSzRow],
                                               const FmtInt4::K& kc,
-                                              uint32_t (&av)[VerifyShared<M, KW>::kSets][4][4],
-                                              float (&y)[RT][VerifyShared<M, KW>::kSets][4],
+                                              uint32_t (&av)[VerifyShared<M, KW>::kA1][VerifyShared<M, KW>::kA2][4],
+                                              float (&y)[RT][VerifyShared<M, KW>::kYS][4],
                                               VerifyPart<M, RT, SR>& part, uint8_t* tile) {
-  constexpr int SETS = VerifyShared<M, KW>::kSets;
+  constexpr int YS = VerifyShared<M, KW>::kYS;
   constexpr int GI = 4 * OCT;          // groups per item
   constexpr int IW = kSzWin / GI;      // items per (scale, zero) window
   const int64_t nb = b1 - b0;
@@ -406,7 +603,7 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
     verify_load<RT, OCT, LT>(a, b0 + b2, g0, i2, lane, nx, more);
     if (more && i2 == 0) nxt = claim_batch(ctr, lane);
     verify_item<M, KW, RT, OCT, LT>(cur, it * GI, (it % IW) * GI, a.gshift, rq, col, sh, szb, kc, av, y, tile);
-    if (it + 1 == items) verify_fold<M, RT, SETS, SR>(a, b0 + bi, (int)bi, first, last, rq, col, y, part);
+    if (it + 1 == items) verify_fold<M, RT, YS, SR>(a, b0 + bi, (int)bi, first, last, rq, col, y, part);
     bi = b2;
     it = i2;
   };
@@ -463,7 +660,6 @@ struct VerifyCuts {
 template <int M, int KW, int WAVES, int RT, int OCT, bool LT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const GemvArgs* __restrict__ mats,
                                                                       VerifyCuts cuts) {
-  constexpr int SETS = VerifyShared<M, KW>::kSets;
   constexpr int GI = 4 * OCT;          // groups per item
   constexpr int SR = verify_round_blocks<WAVES>();
   static_assert(kSzWin % GI == 0 && KW % kSzWin == 0, "windows must nest");
@@ -518,18 +714,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   }
   __syncthreads();
 
-  uint32_t av[SETS][4][4];
+  constexpr int A1 = VerifyShared<M, KW>::kA1, A2 = VerifyShared<M, KW>::kA2, YS = VerifyShared<M, KW>::kYS;
+  uint32_t av[A1][A2][4];
 #pragma unroll
-  for (int st = 0; st < SETS; ++st)
+  for (int st = 0; st < A1; ++st)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < A2; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) av[st][j][e] = 0u;
-  float y[RT][SETS][4];
+  float y[RT][YS][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int st = 0; st < SETS; ++st)
+    for (int st = 0; st < YS; ++st)
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[rt][st][r] = 0.0f;
   int64_t gb = uniform_i64(range[0]);

@@ -129,13 +129,15 @@ def test_gemv_int4g32(wq, n, k):
 
 # m >= 2 runs on the matrix cores with K windows of 256 groups: the cases
 # cover one window, several, a ragged last window (k = 8288, 12352, 8224),
-# matrices with more row blocks than resident workgroups (3 to 7 blocks per
-# workgroup with 1 to 16 items each, ragged last blocks), and k = 0
+# matrices with more row blocks than resident workgroups (3 to 8 blocks per
+# workgroup with 1 to 32 items each, every token count, ragged last blocks),
+# and k = 0
 SMALLM_CASES = [(m, n, k) for m in range(1, 9) for (n, k) in [(45, 4096), (3, 32), (70, 8192)]] + \
     [(m, 21, 16384) for m in (2, 5, 6, 8)] + [(m, 19, 28672) for m in (2, 3, 4, 5, 7, 8)] + \
     [(5, 8, 32768), (1, 10, 131072), (5, 6, 131072), (5, 50, 8288), (7, 37, 12352), (3, 100, 8224),
     (2, 9, 0), (6, 9, 0), (5, 16411, 512), (3, 18000, 8224), (8, 17000, 4128), (2, 20000, 16416),
-    (5, 31990, 1024), (6, 55999, 1024), (2, 23999, 4096), (4, 39995, 256), (3, 40000, 2048)]
+    (5, 31990, 1024), (6, 55999, 1024), (2, 23999, 4096), (4, 39995, 256), (3, 40000, 2048)] + \
+    [(m, 49999, 256) for m in (2, 3, 4, 5, 7, 8)] + [(5, 50011, 1024), (8, 49300, 5376)]
 
 
 @pytest.mark.parametrize("m,n,k", SMALLM_CASES)
@@ -266,7 +268,8 @@ def test_gemm_small_m_int8(wq, m, n, k):
 
 
 GROUP_SMALLM_CASES = [(2, 64, 45, 4096), (3, 128, 70, 8192), (5, 128, 19, 28672), (5, 256, 33, 1024),
-                      (8, 64, 21, 16384), (5, 0, 40, 8288), (4, 0, 7, 96), (6, 256, 9, 131072 // 2)]
+                      (8, 64, 21, 16384), (5, 0, 40, 8288), (4, 0, 7, 96), (6, 256, 9, 131072 // 2),
+                      (5, 128, 49999, 1024), (3, 0, 50000, 512), (7, 64, 49153, 2048)]
 
 
 @pytest.mark.parametrize("m,group,n,k", GROUP_SMALLM_CASES)

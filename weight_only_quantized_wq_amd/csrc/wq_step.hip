@@ -74,7 +74,6 @@ static StepVariant i8mt_variant() {
 constexpr int64_t kTiledMaxK = (int64_t)1 << 24;
 constexpr int64_t kTiledMaxBytes = (int64_t)0xFFFFFF00u;
 
-constexpr int kVerifyKW = 256, kVerifyRT = 2, kVerifyOct = 2;
 // starting value of the verify kernel's long-row cost factor (measured on
 // the Llama-3.1-70B set: rows of 28672 inputs cost ~1.2x per byte); each
 // launch refines it
@@ -87,13 +86,19 @@ static void verify_launch(int grid, const StepLaunch& l, hipStream_t stream) {
 }
 
 // LT: codes loaded line-wide and moved to the MFMA layout through a per-wave
-// LDS tile (2 KiB per wave on top of the activation window; fits up to 5
-// tokens), else quad-row loads and cross-lane permutes.
-template <int M, int WAVES, int RT = kVerifyRT, int OCT = kVerifyOct, int KW = kVerifyKW, bool LT = false>
+// LDS tile (2 KiB per wave on top of the activation window), else quad-row
+// loads and cross-lane permutes.
+template <int M, int WAVES, int RT, int OCT, int KW, bool LT>
 static StepVariant verify_variant() {
   return StepVariant{1, WAVES, 16 * RT,
                      reinterpret_cast<const void*>(gemm_verify_step_kernel<M, KW, WAVES, RT, OCT, LT>),
                      &verify_launch<M, WAVES, RT, OCT, KW, LT>, 0, true, KW};
+}
+
+template <int M>
+static StepVariant verify_config_variant() {
+  using C = VerifyConfig<M>;
+  return verify_variant<M, C::kWaves, C::kRT, C::kOct, C::kKW, C::kLT>();
 }
 
 static bool is_int4(int format) {
@@ -122,13 +127,13 @@ static bool pick_variant(int format, int m, StepVariant& v) {
     // 32-input chunk reading its group's (scale, zero) word
     switch (m) {
       case 1: v = shared_variant<FmtInt4, 2, 2, 16, true>(); break;
-      case 2: v = verify_variant<2, 8, 2, 4, 512, true>(); break;
-      case 3: v = verify_variant<3, 8, 2, 4, kVerifyKW, true>(); break;
-      case 4: v = verify_variant<4, 12, kVerifyRT, kVerifyOct, kVerifyKW, true>(); break;
-      case 5: v = verify_variant<5, 8, 2, 4, kVerifyKW, true>(); break;
-      case 6: v = verify_variant<6, 8, 2, 4, 224, true>(); break;   // windows of 224 / 192 groups leave room
-      case 7: v = verify_variant<7, 8, 2, 4, 192, true>(); break;   // for the code tiles
-      case 8: v = verify_variant<8, 8, 2, 4, 160, true>(); break;   // window of 160 groups leaves room for the tile
+      case 2: v = verify_config_variant<2>(); break;
+      case 3: v = verify_config_variant<3>(); break;
+      case 4: v = verify_config_variant<4>(); break;
+      case 5: v = verify_config_variant<5>(); break;
+      case 6: v = verify_config_variant<6>(); break;
+      case 7: v = verify_config_variant<7>(); break;
+      case 8: v = verify_config_variant<8>(); break;
       default: return false;
     }
   } else {

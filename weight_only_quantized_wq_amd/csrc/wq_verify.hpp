@@ -47,6 +47,19 @@ namespace wq {
 // Longest row (inputs) the verify kernel accepts (offsets stay in 32 bits).
 constexpr int kVerifyMaxK = 131072;
 
+// Per token count: waves per workgroup, 16-row tiles per block, quads per
+// item, groups per staged activation window, code tiles in LDS (chosen by
+// timing the Llama-3.1-70B verify sets; the windows of 6..8 tokens leave room
+// for the tiles).
+template <int M>
+struct VerifyConfig {
+  static constexpr int kWaves = M == 4 ? 12 : 8;
+  static constexpr int kRT = 2;
+  static constexpr int kOct = M == 4 ? 2 : 4;
+  static constexpr int kKW = M == 2 ? 512 : (M == 6 ? 224 : (M == 7 ? 192 : (M == 8 ? 160 : 256)));
+  static constexpr bool kLT = true;
+};
+
 typedef __bf16 vbf16x8 __attribute__((ext_vector_type(8)));
 typedef float vf32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -64,13 +77,13 @@ struct alignas(16) VerifyShared {
   static constexpr int kA2 = kWide ? 2 : 4;
   static constexpr int kYS = kWide ? 1 : kSets;
   static constexpr int kRow = KW * 16 + 4;
-  static constexpr int kZRows = kWide ? 16 : 8;   // A rows of the zero-point product: lo * kZLo + token
-  static constexpr int kZLo = kWide ? 8 : 4;
+  static constexpr int kZLo = kWide ? 8 : 4;      // A rows of the zero-point products: part * kZLo + token
+  static constexpr int kZRows = 3 * kZLo;
   static constexpr int kSumRow = KW + 8;          // bf16 per row of xz (rows 16 bytes apart in bank)
   uint32_t xs[M][kRow];          // pre-permuted bf16 pairs, 16 words per group
   float gs[KW][kSets][4];        // -128 x the per-group activation sums, [group][set][token in set]
-  // the per-group activation sums X as an exact bf16 pair hi + lo
-  // (|X - hi - lo| <= 2^-18 |X|); rows of tokens past M are zero
+  // the per-group activation sums X as three bf16 parts hi + mid + lo
+  // (|X - hi - mid - lo| <= 2^-27 |X|); rows of tokens past M are zero
   alignas(16) uint16_t xz[kZRows][kSumRow];
 };
 
@@ -117,7 +130,7 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
     const int t = it / kz;
     const int g = it - t * kz;
     const int gg = g0 + g;
-    uint16_t hi = 0, lo = 0;
+    uint16_t hi = 0, mid = 0, lo = 0;
     float gsum = 0.0f;
     if (t < M) {
       const FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, gg, gg < a.chunks && g < kpad);
@@ -128,26 +141,31 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
               u32x4{xv.p[4 * h], xv.p[4 * h + 1], xv.p[4 * h + 2], xv.p[4 * h + 3]};
       }
       gsum = xv.gsum;
+      // each difference is exact in fp32
       hi = f32_to_bf16(gsum);
-      lo = f32_to_bf16(gsum - __uint_as_float((uint32_t)hi << 16));
+      const float r1 = gsum - __uint_as_float((uint32_t)hi << 16);
+      mid = f32_to_bf16(r1);
+      lo = f32_to_bf16(r1 - __uint_as_float((uint32_t)mid << 16));
     }
     if (t < 4 * SETS && g < kpad) sh.gs[g][t >> 2][t & 3] = -128.0f * gsum;
     sh.xz[t][g] = hi;
-    sh.xz[ZLO + t][g] = lo;
+    sh.xz[ZLO + t][g] = mid;
+    sh.xz[2 * ZLO + t][g] = lo;
   }
 }
 
 // The zero points of a (scale, zero) window for the wave's block.  A group
 // contributes s * (D - 128 X) + z * X to each token (D = sum of (128 + q) x
 // from the MFMAs, whose accumulators start at -128 X, X the group's
-// activation sum); the z * X terms of the window's 32 groups are one more
-// MFMA: A = X (rows kZLo lo + t: its hi and lo bf16 parts, exact), B = the
-// groups' zero points (bf16, exact).  Lane (rq, col) receives rows 4 rq + r:
-// in the wide layout tokens 4 (rq % 2) + r, hi for rq < 2 and lo otherwise;
-// with up to four tokens token r, hi for rq = 0 and lo for rq = 1 (rows 8..15
-// zero) -- in both the tokens of its own accumulators, so the slot sums of
-// the fold add hi and lo.  il: the window's first group in the activation
-// window; chunk i of the window uses (scale, zero) word i >> gshift.
+// activation sum); the z * X terms of the window's 32 groups are MFMAs with
+// A = X (rows kZLo part + t: its hi, mid and lo bf16 parts), B = the groups'
+// zero points (bf16, exact), one MFMA per 16 A rows.  Lane (rq, col)
+// receives rows 4 rq + r of each: in the wide layout tokens 4 (rq % 2) + r
+// (hi or mid in the first MFMA, lo or nothing in the second); with up to four
+// tokens token r (hi, mid, lo or nothing by rq) -- in both the tokens of its
+// own accumulators, so the slot sums of the fold add the parts.  il: the
+// window's first group in the activation window; chunk i of the window uses
+// (scale, zero) word i >> gshift.
 template <int M, int KW, int RT, int YS>
 __device__ __forceinline__ void verify_zero_term(const VerifyShared<M, KW>& sh, const uint32_t (*szb)[16][kSzRow],
                                                  int il, int gshift, int rq, int col, float (&y)[RT][YS][4]) {
@@ -155,13 +173,19 @@ __device__ __forceinline__ void verify_zero_term(const VerifyShared<M, KW>& sh, 
   // the window's words were stored by other lanes of the wave (sz_put)
   __builtin_amdgcn_wave_barrier();
   constexpr int ZR = VerifyShared<M, KW>::kZRows;
-  uint32_t av[4] = {0u, 0u, 0u, 0u};
-  if (col < ZR) {
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(&sh.xz[col < ZR ? col : 0][il + 8 * rq]);
-    av[0] = xa[0];
-    av[1] = xa[1];
-    av[2] = xa[2];
-    av[3] = xa[3];
+  constexpr int ZM = (ZR + 15) / 16;   // MFMAs per tile
+  uint32_t av[ZM][4];
+#pragma unroll
+  for (int h = 0; h < ZM; ++h) {
+    const int row = 16 * h + col;
+    av[h][0] = av[h][1] = av[h][2] = av[h][3] = 0u;
+    if (row < ZR) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(&sh.xz[row < ZR ? row : 0][il + 8 * rq]);
+      av[h][0] = xa[0];
+      av[h][1] = xa[1];
+      av[h][2] = xa[2];
+      av[h][3] = xa[3];
+    }
   }
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -178,8 +202,9 @@ __device__ __forceinline__ void verify_zero_term(const VerifyShared<M, KW>& sh, 
     uint32_t bz[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bz[j] = __builtin_amdgcn_perm(w[2 * j + 1], w[2 * j], 0x07060302u);   // (z_2j, z_2j+1)
-    const vf32x4 zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-    const vf32x4 dz = mfma16x16x32(av, bz, zero4);
+    vf32x4 dz = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < ZM; ++h) dz = mfma16x16x32(av[h], bz, dz);
 #pragma unroll
     for (int r = 0; r < 4; ++r) y[rt][0][r] += dz[r];
   }

@@ -262,9 +262,19 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     // the shared-activation and int8 matrix-core kernels stream a row in
     // `passes` passes
     a.cpl = (v.cmax || v.tiled) ? (int32_t)passes : 1;
+    // one-token kernels: rows of one pass that would leave half the lanes
+    // idle share a wave pass, L = 64 / rpp lanes each (L >= 8 and L * CPL
+    // chunks cover the row)
+    a.rpp = 1;
+    if (!v.tiled && !v.verify && passes == 1) {
+      const int64_t lanes = (chunks + v.cpl_max - 1) / v.cpl_max;
+      int L = kWave;
+      while (L > 8 && L / 2 >= lanes) L /= 2;
+      a.rpp = kWave / L;
+    }
     // the verify kernel's batch is a block of 16-row tiles, the
-    // shared-activation kernel's u rows of one wave
-    const int64_t rows_per_batch = (int64_t)v.u;
+    // shared-activation kernel's u rows of one wave (u x rpp with short rows)
+    const int64_t rows_per_batch = (int64_t)v.u * a.rpp;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -275,7 +285,10 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     // including the lanes past a row's end in its last pass: weigh a batch by
     // its padded length so that rows whose length is not a multiple of a
     // pass (e.g. k = 11008) get proportionally shorter ranges
-    if (v.cmax || v.tiled) batch_bytes[(size_t)i] *= (double)(passes * per_wave_max) / (double)chunks;
+    if (v.cmax || v.tiled) {
+      const int64_t padded = a.rpp > 1 ? (int64_t)(kWave / a.rpp) * v.cpl_max : passes * per_wave_max;
+      batch_bytes[(size_t)i] *= (double)padded / (double)chunks;
+    }
   }
   int rc = check_device();
   if (rc) return rc;

@@ -46,11 +46,13 @@ constexpr int shared_x_cmax() {
   return (kSharedXWords / F::kLdsWordsPerChunk) / (kWave * CPL) * (kWave * CPL);
 }
 
-// One batch-pass of weights in registers: U rows x CPL chunks (+ group words).
+// One batch-pass of weights in registers: U rows x CPL chunks (+ group words;
+// packed short rows: + the row scale bits of the row the lane stores for u).
 template <int U, int CPL>
 struct PassBuf {
   u32x4 w[U][CPL];
   uint32_t aux[U][CPL];
+  uint32_t sc[U];
 };
 
 // Claims the next batch index of the segment for the calling wave.
@@ -88,6 +90,52 @@ __device__ __forceinline__ void load_pass(const GemvArgs& a, int64_t batch, int 
     } else {
 #pragma unroll
       for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;
+    }
+  }
+}
+
+// Short rows (one pass of fewer than 64 * CPL / 2 chunks): R = a.rpp rows
+// share a wave pass, L = 64 / R lanes each; lane (s, q) = (lane / L, lane % L)
+// takes chunks q + j L of row (batch U + u) R + s.  One buffer resource spans
+// the R rows (wave-uniform), and a chunk past its row reads an offset past
+// the resource, so it neither reads the next row nor faults.
+template <class F, int U, int CPL>
+__device__ __forceinline__ void load_pass_packed(const GemvArgs& a, int64_t batch, int lane, PassBuf<U, CPL>& bt,
+                                                 bool ok = true) {
+  const int R = a.rpp, L = kWave / R;
+  const int s = lane / L, q = lane - s * L;
+  const uint32_t rb = (uint32_t)a.row_bytes;
+  const int64_t words = int4_row_words(a.chunks, a.gshift);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t r0 = (batch * U + u) * R;
+    const int64_t left = a.n - r0;
+    const uint32_t rows_ok = !ok || left <= 0 ? 0u : (left >= R ? (uint32_t)R : (uint32_t)left);
+    const int64_t rr = rows_ok ? r0 : 0;
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rr * a.row_bytes, rows_ok * rb);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = q + j * L;
+      bt.w[u][j] = buffer_load16_nt(rw, c < a.chunks ? (uint32_t)s * rb + (uint32_t)c * 16u : 0x80000000u);
+    }
+    if constexpr (F::kGroupAux) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, rows_ok * (uint32_t)words * 4u);
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = q + j * L;
+        bt.aux[u][j] = buffer_load4_nt(
+            rs, c < a.chunks ? ((uint32_t)s * (uint32_t)words + (uint32_t)(c >> a.gshift)) * 4u : 0x80000000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) bt.aux[u][j] = 0u;
+    }
+    if constexpr (F::kRowScale) {
+      // requested with the pass, clamped to a valid row, so that nothing
+      // waits for it before the next pass is requested
+      int64_t r = r0 + s;
+      if (r >= a.n) r = a.n - 1;
+      bt.sc[u] = (uint32_t)*gmem(a.scale + r);
     }
   }
 }
@@ -143,11 +191,95 @@ __device__ __forceinline__ void finish_pass(const GemvArgs& a, int64_t batch, in
   }
 }
 
+// Sum over the L lanes of a group (L a power of two, at most 32), the same
+// tree in every group.
+__device__ __forceinline__ float group_sum(float v, int L) {
+  for (int o = L >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Accumulates a packed pass (load_pass_packed) and stores its U * R rows:
+// the L lanes of each row are summed and lane q = 0 stores the row.
+template <class F, int U, int CPL, int CMAX>
+__device__ __forceinline__ void finish_pass_packed(const GemvArgs& a, int64_t batch, int lane,
+                                                   const PassBuf<U, CPL>& bt, const uint32_t* xs,
+                                                   const typename F::K& kc, float (&acc)[U], float bias) {
+  const int R = a.rpp, L = kWave / R;
+  const int s = lane / L, q = lane - s * L;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const typename F::X xv = F::lds_x(xs, CMAX, q + j * L);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      typename F::D d;
+      F::decode(bt.w[u][j], d, kc);
+      acc[u] = F::dot(d, bt.aux[u][j], xv, acc[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float v = group_sum(acc[u], L);
+    acc[u] = bias;
+    const int64_t r = (batch * U + u) * R + s;
+    if (q == 0 && r < a.n) {
+      if constexpr (F::kRowScale) v *= __uint_as_float(bt.sc[u] << 16);
+      if (a.y32) *gmem(a.y32 + r) = v;
+      if (a.y16) *gmem(a.y16 + r) = f32_to_bf16(v);
+    }
+  }
+}
+
+// The packed segment loop: one pass per batch, the next batch's loads
+// requested before the current one is reduced (two alternating buffers, as
+// in stream_segment).
+template <class F, int U, int CPL, int CMAX>
+__device__ __forceinline__ void stream_segment_packed(const GemvArgs& a, int64_t lb, int64_t le, const uint32_t* xs,
+                                                      int* ctr, int lane) {
+  const typename F::K kc = F::consts();
+  float bias = 0.0f;
+  if constexpr (F::kLaneBias) {
+    const int L = kWave / a.rpp, q = lane % L;
+    for (int j = 0; j < CPL; ++j) bias += F::lds_bias(xs, CMAX, q + j * L);
+  }
+  int64_t cur = lb + claim_batch(ctr, lane);
+  if (cur >= le) return;
+  float acc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc[u] = bias;
+  PassBuf<U, CPL> A, B;
+  load_pass_packed<F, U, CPL>(a, cur, lane, A);
+  for (;;) {
+    int64_t nx = lb + claim_batch(ctr, lane);
+    bool more = nx < le;
+    load_pass_packed<F, U, CPL>(a, nx, lane, B, more);
+    finish_pass_packed<F, U, CPL, CMAX>(a, cur, lane, A, xs, kc, acc, bias);
+    if (!more) {
+      wait_vmem_all();   // no path reaches the loop head with the last request in flight
+      break;
+    }
+    cur = nx;
+    nx = lb + claim_batch(ctr, lane);
+    more = nx < le;
+    load_pass_packed<F, U, CPL>(a, nx, lane, A, more);
+    finish_pass_packed<F, U, CPL, CMAX>(a, cur, lane, B, xs, kc, acc, bias);
+    if (!more) {
+      wait_vmem_all();
+      break;
+    }
+    cur = nx;
+  }
+}
+
 // The waves' share of one matrix segment: batches [lb, le) of matrix `a`,
-// claimed one at a time from `ctr` (zeroed by the caller).
-template <class F, int U, int CPL, int CMAX, bool PF>
+// claimed one at a time from `ctr` (zeroed by the caller).  PACK: short rows,
+// a.rpp of them per wave pass (one pass per batch).
+template <class F, int U, int CPL, int CMAX, bool PF, bool PACK>
 __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, int64_t le, const uint32_t* xs,
                                                int* ctr, int lane) {
+  if constexpr (PACK) {
+    stream_segment_packed<F, U, CPL, CMAX>(a, lb, le, xs, ctr, lane);
+    return;
+  }
   const int passes = a.cpl;
   const typename F::K kc = F::consts();
   float bias = 0.0f;
@@ -414,7 +546,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
     for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
     if (threadIdx.x == 0) ctr = 0;
     __syncthreads();
-    stream_segment<F, U, CPL, CMAX, PF>(a, lb, le, xs, &ctr, lane);
+    if (a.rpp > 1)
+      stream_segment<F, U, CPL, CMAX, PF, true>(a, lb, le, xs, &ctr, lane);
+    else
+      stream_segment<F, U, CPL, CMAX, PF, false>(a, lb, le, xs, &ctr, lane);
   });
 }
 

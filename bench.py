@@ -37,12 +37,12 @@ METRIC_OTHER = "achieved HBM GB/s (% of peak) + equiv. batch-1 decode tok/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     # 20 warmup steps: the step kernels re-cut their workgroups' ranges from
-    # the balance state each launch measures, and the clocks ramp; both
-    # settle within about 20 launches
+    # the balance state each launch measures (settled within a few launches);
+    # an idle device's ramp is taken by --device-warmup-ms
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="llama2-7b-int4")
@@ -51,10 +51,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time for the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-calibration", action="store_true", help="skip the 1 GiB copy used to scale PMC counters")
+    p.add_argument("--device-warmup-ms", type=float, default=60.0,
+                   help="untimed HBM streaming through a scratch buffer before the warmup steps (0: none)")
     p.add_argument("--no-graph", action="store_true",
                    help="fused steps: skip the HIP-graph replay timed for comparison (kernel traces then hold "
                         "only the direct launches)")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 def source_sha():
@@ -116,6 +118,29 @@ def copy_calibration():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+
+
+def device_warmup(ms):
+    """Streams a 256 MiB scratch buffer (not the workload's) through HBM for
+    about `ms` milliseconds.  A device that was idle runs its first ~20
+    launches up to 5 % slower; fresh plans on a warm device do not (the
+    balance state plays no part), so this brings the device, not the plan,
+    to its sustained state before the warmup steps."""
+    import torch
+    if ms <= 0:
+        return 0
+    src = torch.empty(1 << 26, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(16):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        n += 16
+    del src, dst
+    return n
 
 
 def capture(fn):
@@ -394,6 +419,7 @@ def main():
           f"in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
     if not args.no_calibration:
         copy_calibration()
+    device_warmup(args.device_warmup_ms)
 
     fused = hasattr(ls, "plan")
     for _ in range(args.warmup):
@@ -451,6 +477,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "device_warmup_ms": args.device_warmup_ms,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

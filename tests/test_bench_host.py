@@ -26,6 +26,15 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.stdout == ""
 
 
+def test_device_warmup_is_explicit_and_can_be_switched_off():
+    """The untimed device warm-up before the warmup steps is a flag of its
+    own (recorded in the line), and 0 skips it without touching the GPU."""
+    import bench
+    assert bench.parse([]).device_warmup_ms == 60.0
+    assert bench.parse(["--device-warmup-ms", "0"]).device_warmup_ms == 0.0
+    assert bench.device_warmup(0) == 0
+
+
 def test_roofline_takes_the_class_with_the_most_time():
     import bench
     launches = [("a", 0, 1e9), ("a", 0, 1e9), ("b", 0, 6e9)]

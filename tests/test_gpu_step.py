@@ -177,8 +177,9 @@ def test_step_argument_errors():
                                   ("int8", 5), ("int4g128", 5)])
 def test_step_balance_never_changes_results(fmt, m):
     """Each launch re-cuts the workgroups' ranges from the balance state the
-    previous launches measured (XCD speed weights for one token row, the
-    long-row cost factor for 2..8); which workgroup streams a row must never
+    previous launches measured (per-workgroup speed weights for the one-token
+    and int8 kernels, XCD weights and the long-row cost factor for the int4
+    verify kernel); which workgroup streams a row must never
     change the row's bits.  30 launches of one plan, and a fresh plan whose
     state starts from the prior, all give the first launch's outputs."""
     import torch
@@ -209,21 +210,24 @@ def test_step_balance_never_changes_results(fmt, m):
         assert np.array_equal(host(mt[5]), f32), "a fresh plan differs"
 
 
-# The balance state sits at the end of a step workspace: the XCD state of
-# the one-token and int8 2..8-row kernels (128 bytes: float w[8], cost[8],
-# time[8], int32 done, xoff, pad[6]), then the verify kernel's (144 bytes:
-# double f, t[2], c[2], int32 done, xoff, float w[8], xcost[8], xtime[8]).
-_STEP_BAL, _VERIFY_BAL = 128, 144
+# The balance state sits at the end of a step workspace: the per-workgroup
+# state every step kernel uses (int32 done, launches, pad[2]; float w[8192],
+# cost[8192], time[8192]; double cum[8193]; pad to 16 bytes), then the verify
+# kernel's long-row state (48 bytes: double f, t[2], c[2], pad).
+_MAXG = 8192
+_STEP_BAL, _VERIFY_BAL = 16 + 12 * _MAXG + 8 * (_MAXG + 1) + 8, 48
 
 
 @pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 5), ("int4g32", 5)])
 def test_step_balance_feedback_runs(fmt, m):
     """The last workgroup of every launch turns the launch's reports into the
-    next launch's factors and clears the sums: after several launches the
-    counters and sums are zero again, the XCD weights keep mean 1 within
-    their clamp's range, and (verify kernel, short and long rows in one plan) the
-    long-row factor has left its prior of 1.2.  A report lost or counted
-    twice would leave `done` non-zero."""
+    next launch's factors: after several launches the `done` count is zero
+    again and the launches were counted, the workgroup weights have mean 1
+    and stay within their clamp's range, every workgroup reported a positive
+    cost and time, and the cumulative shares run from 0 to 1 in steps of
+    w / G; verify kernel (short and long rows in one plan): the long-row sums
+    are cleared and the long-row factor has left its prior of 1.2.  A report
+    lost or counted twice would leave `done` non-zero."""
     import torch
     import weight_only_quantized_wq_amd as wq
     say(f"balance feedback {fmt} m={m}")
@@ -236,18 +240,19 @@ def test_step_balance_feedback_runs(fmt, m):
     torch.cuda.synchronize()
     tail = ws[nbytes - _STEP_BAL - _VERIFY_BAL:].cpu().numpy()
     sb, vb = tail[:_STEP_BAL], tail[_STEP_BAL:]
-    verify = fmt.startswith("int4") and m > 1
-    if verify:
+    if fmt.startswith("int4") and m > 1:
         f, t0, t1, c0, c1 = np.frombuffer(vb[:40].tobytes(), dtype=np.float64)
-        done, xoff = np.frombuffer(vb[40:48].tobytes(), dtype=np.int32)
-        w, xcost, xtime = np.frombuffer(vb[48:144].tobytes(), dtype=np.float32).reshape(3, 8)
         assert (t0, t1, c0, c1) == (0.0, 0.0, 0.0, 0.0)
         assert 0.5 <= f <= 4.0 and f != 1.2, f"long-row factor {f}"
-    else:
-        w, xcost, xtime = np.frombuffer(sb[:96].tobytes(), dtype=np.float32).reshape(3, 8)
-        done, xoff = np.frombuffer(sb[96:104].tobytes(), dtype=np.int32)
+    G = plan.groups
+    done, launches = (int(v) for v in np.frombuffer(sb[:8].tobytes(), dtype=np.int32))
+    assert launches == 12, f"{launches} launches counted"
+    arr = np.frombuffer(sb[16:16 + 12 * _MAXG].tobytes(), dtype=np.float32).reshape(3, _MAXG)
+    w, cost, tm = arr[0, :G], arr[1, :G], arr[2, :G]
+    cum = np.frombuffer(sb[16 + 12 * _MAXG:16 + 12 * _MAXG + 8 * (G + 1)].tobytes(), dtype=np.float64)
     assert done == 0, f"{done} reports left over"
-    assert 0 <= xoff < 8
-    assert not xcost.any() and not xtime.any()
-    # clamped to [0.7, 1.3], then scaled to mean 1
-    assert np.all((w >= 0.57) & (w <= 1.68)) and abs(float(w.sum()) - 8.0) < 1e-3, w
+    # clamped to [0.5, 2], then scaled to mean 1
+    assert np.all((w >= 0.25) & (w <= 4.0)) and abs(float(w.mean()) - 1.0) < 1e-3, w
+    assert np.all(cost > 0) and np.all(tm > 0)
+    assert cum[0] == 0.0 and cum[G] == 1.0 and np.all(np.diff(cum) > 0)
+    assert np.allclose(np.diff(cum), w / G, rtol=1e-4, atol=1e-9)

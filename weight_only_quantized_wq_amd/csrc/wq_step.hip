@@ -18,7 +18,7 @@ namespace wq {
 // Device pointers of a prepared plan's workspace.
 struct StepLaunch {
   const GemvArgs* mats;
-  StepCuts cuts;          // cost prefix and XCD balance (shared-activation kernel)
+  StepCuts cuts;          // cost prefix and per-workgroup balance (every step kernel)
   VerifyCuts vcuts;       // cost prefixes and long-row balance (verify kernel)
 };
 
@@ -156,13 +156,13 @@ static int64_t row_bytes_of(int format, int64_t k) {
   return format == WQ_FORMAT_BF16 ? 2 * k : (format == WQ_FORMAT_INT8 ? k : k / 2);
 }
 
-constexpr int kMaxGroups = 8192;   // workgroups of one step launch (upper bound)
+constexpr int kMaxGroups = kStepMaxGroups;   // workgroups of one step launch (upper bound)
 
 // Workspace layout: per-matrix descriptors, the step's cost before each
 // matrix (count + 1; for the verify kernel: of the short-row matrices), the
 // long-row cost before each matrix (count + 1, verify kernel), the cost per
-// batch of each matrix (count), then the XCD balance state and the verify
-// kernel's long-row balance state.  Workgroups cut their ranges from these
+// batch of each matrix (count), then the per-workgroup balance state and the
+// verify kernel's long-row balance state.  Workgroups cut their ranges from these
 // on the device.
 struct StepLayout {
   size_t prefix, prefl, bcost, bal, vbal, end;
@@ -196,6 +196,7 @@ static StepLaunch launch_view(void* workspace, int32_t count, int64_t total) {
   v.vcuts.pre_long = reinterpret_cast<const double*>(ws + l.prefl);
   v.vcuts.bcost = v.cuts.bcost;
   v.vcuts.bal = reinterpret_cast<VerifyBalance*>(ws + l.vbal);
+  v.vcuts.wg = v.cuts.bal;
   v.vcuts.count = count;
   return v;
 }
@@ -318,12 +319,15 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   memcpy(host.data() + lay.prefix, prefix.data(), prefix.size() * 8);
   memcpy(host.data() + lay.prefl, prefl.data(), prefl.size() * 8);
   memcpy(host.data() + lay.bcost, batch_bytes.data(), (size_t)count * 8);
-  StepBalance bal{};
-  for (int x = 0; x < 8; ++x) bal.w[x] = 1.0f;
-  memcpy(host.data() + lay.bal, &bal, sizeof(bal));
+  // equal shares to begin with: every workgroup weighs 1
+  StepBalance* bal = reinterpret_cast<StepBalance*>(host.data() + lay.bal);
+  for (int g = 0; g < groups; ++g) {
+    bal->w[g] = 1.0f;
+    bal->cum[g] = (double)g / (double)groups;
+  }
+  bal->cum[groups] = 1.0;
   VerifyBalance vbal{};
   vbal.f = kVerifyLongRowPrior;
-  for (int x = 0; x < 8; ++x) vbal.w[x] = 1.0f;
   memcpy(host.data() + lay.vbal, &vbal, sizeof(vbal));
   hipError_t e = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
   if (e != hipSuccess) {

@@ -216,7 +216,7 @@ __device__ __forceinline__ void mt_stream_segment(const GemvArgs& a, int64_t lb,
 }
 
 // mats: per-matrix descriptors (batch = U tiles of 16 rows; `cpl` holds the
-// number of passes per row); ranges and XCD balance as in the one-token step.
+// number of passes per row); ranges and balance as in the one-token step.
 template <int M, int U, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void gemm_i8_step_kernel(const GemvArgs* __restrict__ mats, StepCuts cuts) {
   __shared__ __attribute__((aligned(16))) uint8_t tiles[WAVES][kMtTileLds];

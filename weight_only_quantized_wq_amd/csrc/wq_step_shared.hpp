@@ -3,14 +3,14 @@
 // A batch-1 decode step streams every linear layer once.  This persistent
 // kernel covers a whole step in one launch:
 //   * each workgroup owns a contiguous range of the step's row batches, of
-//     equal cost on the first launch and then proportional to the measured
-//     speed of its XCD (see StepBalance); one workgroup per CU, so waves of
-//     one CU never compete across workgroups, whose issue priority follows
-//     dispatch order;
+//     equal cost on the first launch and then proportional to its measured
+//     speed (see StepBalance); one workgroup per CU, so waves of one CU never
+//     compete across workgroups, whose issue priority follows dispatch order;
 //   * per matrix segment of its range the workgroup stages that matrix's
 //     activations ONCE into LDS in the format's pre-decoded form, so a single
 //     wave can cover a row of any length -- no split-K, no cross-wave
-//     reduction, no barrier inside a matrix;
+//     reduction, no barrier inside a matrix; each wave claims its first
+//     batches and requests their weights before the staging;
 //   * the waves claim batches of U rows from an LDS counter, so a wave that
 //     gets less issue time simply takes fewer batches;
 //   * a row batch is streamed in passes of CPL 16-byte chunks per lane (64 *
@@ -232,22 +232,26 @@ __device__ __forceinline__ void finish_pass_packed(const GemvArgs& a, int64_t ba
 // The packed segment loop: one pass per batch, the next batch's loads
 // requested before the current one is reduced (two alternating buffers, as
 // in stream_segment).
-template <class F, int U, int CPL, int CMAX>
+template <class F, int U, int CPL, int CMAX, class Stage>
 __device__ __forceinline__ void stream_segment_packed(const GemvArgs& a, int64_t lb, int64_t le, const uint32_t* xs,
-                                                      int* ctr, int lane) {
+                                                      int* ctr, int lane, Stage&& stage) {
   const typename F::K kc = F::consts();
+  int64_t cur = lb + claim_batch(ctr, lane);
+  if (cur >= le) {
+    stage();
+    return;
+  }
+  PassBuf<U, CPL> A, B;
+  load_pass_packed<F, U, CPL>(a, cur, lane, A);
+  stage();
   float bias = 0.0f;
   if constexpr (F::kLaneBias) {
     const int L = kWave / a.rpp, q = lane % L;
     for (int j = 0; j < CPL; ++j) bias += F::lds_bias(xs, CMAX, q + j * L);
   }
-  int64_t cur = lb + claim_batch(ctr, lane);
-  if (cur >= le) return;
   float acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = bias;
-  PassBuf<U, CPL> A, B;
-  load_pass_packed<F, U, CPL>(a, cur, lane, A);
   for (;;) {
     int64_t nx = lb + claim_batch(ctr, lane);
     bool more = nx < le;
@@ -271,30 +275,39 @@ __device__ __forceinline__ void stream_segment_packed(const GemvArgs& a, int64_t
 }
 
 // The waves' share of one matrix segment: batches [lb, le) of matrix `a`,
-// claimed one at a time from `ctr` (zeroed by the caller).  PACK: short rows,
-// a.rpp of them per wave pass (one pass per batch).
-template <class F, int U, int CPL, int CMAX, bool PF, bool PACK>
+// claimed one at a time from `ctr` (zeroed before the segment starts).  A
+// wave claims its first batches and requests their weights first, then
+// calls `stage`, which stages the segment's activations in LDS `xs` and
+// waits for the whole workgroup: the weights do not depend on the
+// activations, so their latency runs under the staging.  Every wave calls
+// `stage` exactly once, with or without a batch.  PACK: short rows, a.rpp of
+// them per wave pass (one pass per batch).
+template <class F, int U, int CPL, int CMAX, bool PF, bool PACK, class Stage>
 __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, int64_t le, const uint32_t* xs,
-                                               int* ctr, int lane) {
+                                               int* ctr, int lane, Stage&& stage) {
   if constexpr (PACK) {
-    stream_segment_packed<F, U, CPL, CMAX>(a, lb, le, xs, ctr, lane);
+    stream_segment_packed<F, U, CPL, CMAX>(a, lb, le, xs, ctr, lane, stage);
     return;
   }
   const int passes = a.cpl;
   const typename F::K kc = F::consts();
+  int64_t cur = lb + claim_batch(ctr, lane);
+  if (cur >= le) {
+    stage();
+    return;
+  }
+  int64_t nxt = lb + claim_batch(ctr, lane);
+  PassBuf<U, CPL> A;
+  load_pass<F, U, CPL>(a, cur, 0, lane, A);
+  stage();
   float bias = 0.0f;
   if constexpr (F::kLaneBias) {
     for (int c = lane; c < passes * CPL * kWave; c += kWave) bias += F::lds_bias(xs, CMAX, c);
   }
-  int64_t cur = lb + claim_batch(ctr, lane);
-  if (cur >= le) return;
-  int64_t nxt = lb + claim_batch(ctr, lane);
   int pass = 0;
   float acc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) acc[u] = bias;
-  PassBuf<U, CPL> A;
-  load_pass<F, U, CPL>(a, cur, 0, lane, A);
   if constexpr (PF) {
     PassBuf<U, CPL> B;
     for (;;) {
@@ -351,36 +364,32 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
   }
 }
 
-// Load balance across XCDs.  The workgroups of a launch are dispatched to
-// the 8 XCDs round robin, but the XCD the first one lands on depends on what
-// was dispatched before (back-to-back launches from a HIP graph start one
-// XCD further than the same launches issued directly), so workgroup g runs
-// on XCD (g + off) mod 8 with a per-launch offset `off`.  Each workgroup
-// reads the XCD it actually runs on from the hardware (XCC_ID).  Under this
-// kernel's mix of streaming and arithmetic the XCDs of one device finish
-// equal shares up to ~8 % apart, so each launch measures, per actual XCD,
-// the cost its workgroups streamed and the time they took; the last
-// workgroup to finish turns that into relative speeds (a quarter of the new
-// measurement per launch, clamped to [0.7, 1.3]) and records the offset it
-// observed.  The next launch cuts the step into ranges proportional to the
-// speeds of the XCDs its workgroups are expected on (that offset): every
-// workgroup reads the same state, so the ranges always partition the step,
-// and an offset that changed in between only costs balance for one launch.
-// Which workgroup computes a row never changes the row's result.
+// Load balance across workgroups (one-token and int8 2..8-row steps).  A
+// workgroup's time per unit of cost depends on what its range holds (rows
+// of different lengths stream at different rates per byte; every matrix
+// boundary inside a range costs a staging and a drain) and on the CU it runs
+// on, and for a given plan it repeats from launch to launch: the workgroup
+// -> CU assignment is stable and the ranges move little.  So each workgroup
+// reports the cost of its range and the time it took; the last workgroup of
+// the launch turns these into relative speeds and writes the share of the
+// step before each workgroup, which the next launch cuts with.  The first
+// launch of a plan sets the speeds to its measured rates, the second and
+// third move them half and a third of the way to theirs, every later launch
+// a quarter; clamped to [0.5, 2], mean 1.
+// Every workgroup reads the same table, so the ranges always partition the
+// step; which workgroup computes a row never changes the row's result.
+constexpr int kStepMaxGroups = 8192;
 struct StepBalance {
-  float w[8];      // relative speed of each XCD's workgroups (mean 1), by hardware XCD id
-  float cost[8];   // this launch: cost streamed by each XCD's workgroups
-  float time[8];   // this launch: their summed durations (wall-clock ticks)
-  int32_t done;    // workgroups finished in this launch
-  int32_t xoff;    // dispatch offset the last launch observed: workgroup g ran on XCD (g + xoff) mod 8
-  int32_t pad[6];
+  int32_t done;                     // workgroups finished in this launch
+  int32_t launches;                 // launches of the plan so far (saturates)
+  int32_t pad[2];
+  float w[kStepMaxGroups];          // relative speed of workgroup g (mean 1 over the launch's workgroups)
+  float cost[kStepMaxGroups];       // last launch: cost of workgroup g's range (units of the cut)
+  float time[kStepMaxGroups];       // last launch: its duration (wall-clock ticks)
+  double cum[kStepMaxGroups + 1];   // share of the step before workgroup g (cum[0] = 0, cum[G] = 1)
+  int32_t pad2[2];
 };
-
-// Hardware id of the XCD (accelerator complex die) the calling wave runs on.
-__device__ __forceinline__ int hw_xcd_id() {
-  // s_getreg_b32 of HW_REG_XCC_ID (register 20), bits [3:0]
-  return (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u);
-}
+static_assert(sizeof(StepBalance) % 16 == 0, "the verify state follows at a 16-byte boundary");
 
 struct StepCuts {
   const double* prefix;   // [count + 1] cost of the step before matrix i
@@ -390,92 +399,129 @@ struct StepCuts {
   int32_t count;          // matrices
 };
 
-// Share of a launch's work before workgroup g when workgroup j weighs the
-// speed of XCD (j + off) mod 8 (`groups` workgroups in all).
-__device__ __forceinline__ double xcd_share(const float (&w)[8], int off, int g, int groups) {
-  double sw = 0.0, part = 0.0, full = 0.0;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const double v = (double)w[(r + off) & 7];
-    sw += v;
-    if (r < g % 8) part += v;
-    if (r < groups % 8) full += v;
-  }
-  const double before = (double)(g / 8) * sw + part;
-  const double all = (double)(groups / 8) * sw + full;
-  return before / all;
-}
-
-// Cost at which workgroup g's range starts: the step's cost times the share
-// of the speed weights of workgroups 0 .. g-1.
-__device__ __forceinline__ double cut_cost(const StepCuts& c, const float (&w)[8], int off, int g, int groups) {
-  return c.prefix[c.count] * xcd_share(w, off, g, groups);
-}
-
-// A workgroup's balance report: its sums are atomics, counted in by the
-// `done` atomic after them, and the last workgroup reads them back with
-// agent-scope atomic loads.  The only order needed is "sums performed before
-// the count", which a wait for this wave's outstanding memory operations
-// gives; an agent-scope fence would add an L2 write-back and invalidate per
-// workgroup (several microseconds at the end of every launch).  A report
-// that came late would only blur one launch's weights: the cuts are valid
-// for any weights.
+// A workgroup's balance report: agent-scope atomic stores or adds, counted
+// in by the `done` atomic after them, and the last workgroup reads them back
+// with agent-scope atomic loads.  The only order needed is "report performed
+// before the count", which a wait for this wave's outstanding memory
+// operations gives; an agent-scope fence would add an L2 write-back and
+// invalidate per workgroup (several microseconds at the end of every
+// launch).  A report that came late would only blur one launch's weights:
+// the cuts are valid for any weights.
 __device__ __forceinline__ void report_in_order() { wait_vmem_all(); }
 
-// The last workgroup of a launch: new XCD speed weights from the cost each
-// XCD streamed and the time its workgroups took (a quarter of the way to the
-// measured rates, clamped to [0.7, 1.3], mean 1), the dispatch offset this
-// launch saw, and the sums cleared for the next launch.
-__device__ __forceinline__ void xcd_update(float* wv, float* cost, float* time, int32_t* xoff, const float (&w)[8],
-                                           int observed_off) {
-  float r[8], wn[8];
-  float mean = 0.0f;
-  int n = 0;
-  for (int y = 0; y < 8; ++y) {
-    const float cy = __hip_atomic_load(&cost[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const float ty = __hip_atomic_load(&time[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    r[y] = (ty > 0.0f && cy > 0.0f) ? cy / ty : 0.0f;
-    if (r[y] > 0.0f) {
-      mean += r[y];
-      ++n;
+// Sum over the workgroup of one value per thread (NT threads).
+template <int NT>
+__device__ __forceinline__ double block_sum(double v, double* lds) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  __syncthreads();
+  if (lane_id() == 0) lds[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += lds[i];
+  return t;
+}
+
+// Sum of the values of the threads before this one (NT threads), and of all.
+template <int NT>
+__device__ __forceinline__ double block_exclusive_scan(double v, double* lds, double& all) {
+  const int lane = lane_id();
+  double inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += o;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) lds[threadIdx.x >> 6] = inc;
+  __syncthreads();
+  double before = 0.0;
+  all = 0.0;
+  const int wv = (int)(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    if (i < wv) before += lds[i];
+    all += lds[i];
+  }
+  return before + inc - v;
+}
+
+// The last workgroup of a launch (all NT threads): new speed weights from
+// the launch's reports and the cumulative shares the next launch cuts with.
+// Thread i handles workgroups [i * per, (i + 1) * per).  `lds`: NT / 64
+// doubles of LDS the workgroup no longer needs.
+template <int NT>
+__device__ __forceinline__ void step_balance_update(StepBalance* b, int G, double* lds) {
+  constexpr int P = kStepMaxGroups / NT;
+  const int per = (G + NT - 1) / NT;
+  const int j0 = (int)threadIdx.x * per;
+  float r[P], wv[P];
+  double rs = 0.0, rn = 0.0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    r[i] = 0.0f;
+    wv[i] = 1.0f;
+    const int j = j0 + i;
+    if (i < per && j < G) {
+      const float c = __hip_atomic_load(&b->cost[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float t = __hip_atomic_load(&b->time[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wv[i] = __hip_atomic_load(&b->w[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      r[i] = (c > 0.0f && t > 0.0f) ? c / t : 0.0f;
+      if (r[i] > 0.0f) {
+        rs += r[i];
+        rn += 1.0;
+      }
     }
   }
-  mean = n ? mean / (float)n : 0.0f;
-  float sw = 0.0f;
-  for (int y = 0; y < 8; ++y) {
-    float v = w[y];
-    if (mean > 0.0f && r[y] > 0.0f) v = 0.75f * w[y] + 0.25f * (r[y] / mean);
-    v = fminf(fmaxf(v, 0.7f), 1.3f);
-    wn[y] = v;
-    sw += v;
+  rs = block_sum<NT>(rs, lds);
+  rn = block_sum<NT>(rn, lds);
+  const float mean = rn > 0.0 ? (float)(rs / rn) : 0.0f;
+  const int n = __hip_atomic_load(&b->launches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float gain = n < 3 ? 1.0f / (float)(n + 1) : 0.25f;
+  double local = 0.0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    float v = wv[i];
+    if (mean > 0.0f && r[i] > 0.0f) v = (1.0f - gain) * v + gain * (r[i] / mean);
+    wv[i] = fminf(fmaxf(v, 0.5f), 2.0f);
+    if (i < per && j0 + i < G) local += wv[i];
   }
-  for (int y = 0; y < 8; ++y) {
-    atomicExch(&wv[y], wn[y] * 8.0f / sw);
-    atomicExch(&cost[y], 0.0f);
-    atomicExch(&time[y], 0.0f);
+  double all;
+  double run = block_exclusive_scan<NT>(local, lds, all);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int j = j0 + i;
+    if (i < per && j < G) {
+      run += wv[i];
+      __hip_atomic_store(&b->w[j], (float)(wv[i] * (double)G / all), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&b->cum[j + 1], j + 1 == G ? 1.0 : run / all, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  atomicExch(xoff, observed_off);
+  if (threadIdx.x == 0) {
+    if (n < (1 << 30)) atomicExch(&b->launches, n + 1);
+    atomicExch(&b->done, 0);
+  }
 }
 
 // The persistent step's frame.  Each workgroup cuts its own contiguous range
-// of the step's batches from the cost prefix and the XCD speed weights,
-// hands each matrix's part of it, batches [lb, le) of `a`, to
+// of the step's batches from the cost prefix and its share of the step
+// (StepBalance), hands each matrix's part of it, batches [lb, le) of `a`, to
 // `segment(a, lb, le)` (called by every thread of the workgroup), and then
-// reports the cost it streamed and the time it took to the XCD balance.
+// reports the cost it streamed and the time it took.
 template <int WAVES, class Segment>
 __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, const StepCuts& cuts,
                                            Segment&& segment) {
   __shared__ int64_t range[2];
   __shared__ int first_mat;
+  __shared__ int last;
+  __shared__ double bal_lds[WAVES];
   const long long t_start = wall_clock64();
-  float w[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) w[x] = cuts.bal->w[x];
-  const int off = cuts.bal->xoff & 7;
   const int G = (int)gridDim.x;
-  const double c0 = cut_cost(cuts, w, off, (int)blockIdx.x, G);
-  const double c1 =
-      (int)blockIdx.x + 1 == G ? cuts.prefix[cuts.count] : cut_cost(cuts, w, off, (int)blockIdx.x + 1, G);
+  const double total = cuts.prefix[cuts.count];
+  const double c0 = total * cuts.bal->cum[blockIdx.x];
+  const double c1 = (int)blockIdx.x + 1 == G ? total : total * cuts.bal->cum[blockIdx.x + 1];
   // the batch at cost c: first batch of matrix i (prefix[i] <= c < prefix[i + 1])
   // whose start is at or past c; every matrix is checked by one thread
   if (threadIdx.x == 0) {
@@ -518,16 +564,15 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
   __syncthreads();
   if (threadIdx.x == 0) {
     StepBalance* b = cuts.bal;
-    const int x = hw_xcd_id();
-    atomicAdd(&b->cost[x], (float)(c1 - c0));
-    atomicAdd(&b->time[x], (float)(wall_clock64() - t_start));
+    __hip_atomic_store(&b->cost[blockIdx.x], (float)(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&b->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
     report_in_order();
-    if (atomicAdd(&b->done, 1) == G - 1) {
-      // every workgroup has reported: new speed weights for the next launch
-      xcd_update(b->w, b->cost, b->time, &b->xoff, w, (x - (int)(blockIdx.x % 8) + 8) & 7);
-      atomicExch(&b->done, 0);
-    }
+    last = atomicAdd(&b->done, 1) == G - 1;
   }
+  __syncthreads();
+  // every workgroup has reported: the shares of the next launch
+  if (last) step_balance_update<WAVES * kWave>(cuts.bal, G, bal_lds);
 }
 
 // mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of
@@ -538,18 +583,25 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
                                                                       StepCuts cuts) {
   constexpr int CMAX = shared_x_cmax<F, CPL>();
   __shared__ __attribute__((aligned(16))) uint32_t xs[kSharedXWords];
-  __shared__ int ctr;
+  // batch counters of alternate segments: a segment's claims start before
+  // its staging barrier, so its counter is cleared one segment ahead
+  __shared__ int ctr[2];
   const int lane = lane_id();
+  if (threadIdx.x < 2) ctr[threadIdx.x] = 0;
+  int par = 0;
   step_frame<WAVES>(mats, cuts, [&](const GemvArgs& a, int64_t lb, int64_t le) {
-    const int cpad = a.cpl * CPL * kWave;
-    __syncthreads();   // every wave is done with the previous segment's LDS
-    for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
-    if (threadIdx.x == 0) ctr = 0;
-    __syncthreads();
+    __syncthreads();   // every wave is done with the previous segment's LDS and counter
+    if (threadIdx.x == 0) ctr[par ^ 1] = 0;
+    auto stage = [&]() {
+      const int cpad = a.cpl * CPL * kWave;
+      for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
+      __syncthreads();
+    };
     if (a.rpp > 1)
-      stream_segment<F, U, CPL, CMAX, PF, true>(a, lb, le, xs, &ctr, lane);
+      stream_segment<F, U, CPL, CMAX, PF, true>(a, lb, le, xs, &ctr[par], lane, stage);
     else
-      stream_segment<F, U, CPL, CMAX, PF, false>(a, lb, le, xs, &ctr, lane);
+      stream_segment<F, U, CPL, CMAX, PF, false>(a, lb, le, xs, &ctr[par], lane, stage);
+    par ^= 1;
   });
 }
 

@@ -658,17 +658,13 @@ __device__ __forceinline__ void verify_window(const GemvArgs& a, int64_t b0, int
 // the next launch cuts with it.  Which workgroup computes a row never changes
 // the row's result.
 //
-// On top of that, ranges follow the speeds of the XCDs the workgroups run on,
-// measured per launch as in the one-token step (xcd_share / xcd_update).
+// On top of that, ranges follow the measured speeds of the workgroups, as in
+// the one-token step (StepBalance, step_balance_update).
 struct VerifyBalance {
   double f;
   double t[2];      // this launch: wall-clock ticks spent on short / long rows
   double c[2];      // this launch: bytes of short / long rows streamed
-  int32_t done;     // workgroups finished in this launch
-  int32_t xoff;     // dispatch offset the last launch observed (workgroup g on XCD (g + xoff) mod 8)
-  float w[8];       // relative speed of each XCD's workgroups (mean 1), by hardware XCD id
-  float xcost[8];   // this launch: cost (units of the cut) streamed by each XCD's workgroups
-  float xtime[8];   // this launch: their summed durations (wall-clock ticks)
+  double pad;
 };
 
 struct VerifyCuts {
@@ -676,6 +672,7 @@ struct VerifyCuts {
   const double* pre_long;    // [count + 1] bytes of long-row matrices before matrix i
   const double* bcost;       // [count] bytes of one block of matrix i
   VerifyBalance* bal;
+  StepBalance* wg;           // per-workgroup speeds and shares
   int32_t count;
 };
 
@@ -695,6 +692,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   __shared__ int ctr;
   __shared__ int64_t range[2];
   __shared__ int first_mat;
+  __shared__ int last;
   const int lane = lane_id();
   const int wave = wave_id();
   const int rq = lane >> 4;
@@ -702,17 +700,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   uint32_t (*szb)[16][kSzRow] = szs[wave];
   const FmtInt4::K kc = FmtInt4::consts();
 
-  // this workgroup's range: its XCD-speed-weighted share of the step's cost
+  // this workgroup's range: its speed-weighted share of the step's cost
   const long long t_start = wall_clock64();
   const double f = cuts.bal->f;
-  float xw[8];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) xw[x] = cuts.bal->w[x];
-  const int xoff = cuts.bal->xoff & 7;
   const int G = (int)gridDim.x;
   const double total = cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count];
-  const double c0 = total * xcd_share(xw, xoff, (int)blockIdx.x, G);
-  const double c1 = (int)blockIdx.x + 1 == G ? total : total * xcd_share(xw, xoff, (int)blockIdx.x + 1, G);
+  const double c0 = total * cuts.wg->cum[blockIdx.x];
+  const double c1 = (int)blockIdx.x + 1 == G ? total : total * cuts.wg->cum[blockIdx.x + 1];
   if (threadIdx.x == 0) {
     range[0] = mats[cuts.count - 1].batch_begin + mats[cuts.count - 1].batches;
     range[1] = range[0];
@@ -808,13 +802,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
       atomicAdd(&b->t[e], tk[e]);
       atomicAdd(&b->c[e], ck[e]);
     }
-    const int x = hw_xcd_id();
-    atomicAdd(&b->xcost[x], (float)(c1 - c0));
-    atomicAdd(&b->xtime[x], (float)(wall_clock64() - t_start));
+    StepBalance* sb = cuts.wg;
+    __hip_atomic_store(&sb->cost[blockIdx.x], (float)(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&sb->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
     report_in_order();
-    if (atomicAdd(&b->done, 1) == G - 1) {
-      // every workgroup has reported: the factors for the next launch
-      xcd_update(b->w, b->xcost, b->xtime, &b->xoff, xw, (x - (int)(blockIdx.x % 8) + 8) & 7);
+    last = atomicAdd(&sb->done, 1) == G - 1;
+    if (last) {
+      // every workgroup has reported: the long-row factor for the next launch
       double t[2], c[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -831,9 +826,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
         __hip_atomic_store(&b->t[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&b->c[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __hip_atomic_store(&b->done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  __syncthreads();
+  // and the workgroups' shares (clears the `done` count)
+  static_assert(sizeof(part) >= WAVES * sizeof(double), "the partial sums' LDS holds the update's sums");
+  if (last) step_balance_update<WAVES * kWave>(cuts.wg, G, reinterpret_cast<double*>(&part));
 }
 
 }  // namespace wq

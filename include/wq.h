@@ -302,9 +302,9 @@ int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix* mats, int
 /* Launches a prepared step on `stream` (asynchronous; may be captured into a
  * HIP graph).  Runs of one plan must not overlap (they share its workspace,
  * which carries balance state that each run measures and the next run uses
- * to cut the step into per-CU ranges: the XCD speed weights of one-token
- * steps, the relative cost of rows longer than one activation window for
- * 2..8 token rows); runs of plans that share output buffers race. */
+ * to cut the step into per-CU ranges: the measured speed of each workgroup,
+ * and for int4 with 2..8 token rows the relative cost of rows longer than
+ * one activation window); runs of plans that share output buffers race. */
 int wq_decode_step_run(const wq_step_plan* plan, void* stream);
 
 /* ------------------------------------------------------------------------ */

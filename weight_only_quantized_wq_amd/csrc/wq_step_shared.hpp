@@ -505,6 +505,33 @@ __device__ __forceinline__ void step_balance_update(StepBalance* b, int G, doubl
   }
 }
 
+// End of a balanced launch (every thread of the workgroup): the workgroup
+// reports the cost of its range (units of the cut) and the time since
+// `t_start`; the last workgroup to report computes the next launch's shares.
+// `lds`: WAVES doubles of LDS the workgroup no longer needs.
+template <int WAVES>
+__device__ __forceinline__ void step_balance_report(StepBalance* b, double cost, long long t_start, double* lds) {
+  __shared__ int last;
+  const int G = (int)gridDim.x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(&b->cost[blockIdx.x], (float)cost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&b->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    report_in_order();
+    last = atomicAdd(&b->done, 1) == G - 1;
+  }
+  __syncthreads();
+  // every workgroup has reported: the shares of the next launch
+  if (last) step_balance_update<WAVES * kWave>(b, G, lds);
+}
+
+// Workgroup g's share [c0, c1) of a launch of cost `total`.
+__device__ __forceinline__ void step_share(const StepBalance* b, double total, double& c0, double& c1) {
+  c0 = total * b->cum[blockIdx.x];
+  c1 = (int)blockIdx.x + 1 == (int)gridDim.x ? total : total * b->cum[blockIdx.x + 1];
+}
+
 // The persistent step's frame.  Each workgroup cuts its own contiguous range
 // of the step's batches from the cost prefix and its share of the step
 // (StepBalance), hands each matrix's part of it, batches [lb, le) of `a`, to
@@ -515,13 +542,10 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
                                            Segment&& segment) {
   __shared__ int64_t range[2];
   __shared__ int first_mat;
-  __shared__ int last;
   __shared__ double bal_lds[WAVES];
   const long long t_start = wall_clock64();
-  const int G = (int)gridDim.x;
-  const double total = cuts.prefix[cuts.count];
-  const double c0 = total * cuts.bal->cum[blockIdx.x];
-  const double c1 = (int)blockIdx.x + 1 == G ? total : total * cuts.bal->cum[blockIdx.x + 1];
+  double c0, c1;
+  step_share(cuts.bal, cuts.prefix[cuts.count], c0, c1);
   // the batch at cost c: first batch of matrix i (prefix[i] <= c < prefix[i + 1])
   // whose start is at or past c; every matrix is checked by one thread
   if (threadIdx.x == 0) {
@@ -561,18 +585,7 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
     gb = a.batch_begin + le;
     ++mi;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    StepBalance* b = cuts.bal;
-    __hip_atomic_store(&b->cost[blockIdx.x], (float)(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&b->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    report_in_order();
-    last = atomicAdd(&b->done, 1) == G - 1;
-  }
-  __syncthreads();
-  // every workgroup has reported: the shares of the next launch
-  if (last) step_balance_update<WAVES * kWave>(cuts.bal, G, bal_lds);
+  step_balance_report<WAVES>(cuts.bal, c1 - c0, t_start, bal_lds);
 }
 
 // mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of

@@ -704,9 +704,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   const long long t_start = wall_clock64();
   const double f = cuts.bal->f;
   const int G = (int)gridDim.x;
-  const double total = cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count];
-  const double c0 = total * cuts.wg->cum[blockIdx.x];
-  const double c1 = (int)blockIdx.x + 1 == G ? total : total * cuts.wg->cum[blockIdx.x + 1];
+  double c0, c1;
+  step_share(cuts.wg, cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count], c0, c1);
   if (threadIdx.x == 0) {
     range[0] = mats[cuts.count - 1].batch_begin + mats[cuts.count - 1].batches;
     range[1] = range[0];

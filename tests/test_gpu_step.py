@@ -19,11 +19,15 @@ from synth.gen import host_normal, host_bf16_normal
 pytestmark = pytest.mark.gpu
 
 SHAPES = {
-    ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8), (2, 65536)],
+    # one-token rows of one pass that share it: L lanes per row with 2 chunks
+    # of each of 2 rows per lane (k = 1024, 512, 32, ...), or "wide" with up
+    # to 4 (bf16: 8) chunks of one row per lane where that leaves fewer slots
+    # idle (int4 k = 1376, 1536, 2752, 3072; bf16 k = 688); ragged row counts
+    ("bf16", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 8), (2, 65536), (35, 688)],
     ("int8", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 16), (3, 28672),
-                  (2, 36864)],
+                  (2, 36864), (67, 1376)],
     ("int4g32", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 4096), (129, 1024), (64, 32), (3, 28672),
-                     (70, 4160), (2, 73728)],
+                     (70, 4160), (2, 73728), (67, 1376), (33, 2752), (21, 1536), (9, 3072)],
     ("int4g32", 5): [(70, 8192), (19, 28672), (1, 4096), (33, 1024), (8, 32)],
     ("int4g32", 2): [(45, 4096), (9, 16384)],
     ("int4g32", 8): [(45, 4096), (9, 16384), (3, 28672)],
@@ -32,9 +36,9 @@ SHAPES = {
     ("int4g32", 6): [(45, 4096), (9, 16384)],
     ("int4g32", 7): [(45, 4096), (31, 8192), (2, 32)],
     ("int4g64", 1): [(300, 4096), (37, 11008), (1, 64), (64, 28672)],
-    ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128)],
+    ("int4g128", 1): [(300, 4096), (5, 14336), (129, 1024), (3, 128), (21, 1536)],
     ("int4g256", 1): [(300, 4096), (37, 11008 // 256 * 256), (1, 256), (9, 28672)],
-    ("int4pc", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 32), (129, 1056), (3, 28672)],
+    ("int4pc", 1): [(300, 4096), (37, 11008), (5, 14336), (1, 32), (129, 1056), (3, 28672), (13, 1376)],
     # larger int4 groups with 2..8 token rows: words per 32-input chunk of the
     # (scale, zero) window, one- and multi-window rows (k > 8192), ragged n
     ("int4g64", 2): [(45, 4096), (9, 16384), (1, 64)],

@@ -48,6 +48,8 @@ struct GemvArgs {
   int32_t cpl;            // multi-matrix launches: chunks per lane used (<= CPL)
   int32_t gshift;         // int4: log2(group / 32): chunk c's (scale, zero) word is sz[row][c >> gshift]
   int32_t rpp;            // one-token step: rows sharing a wave pass (short rows; 0 or 1 = one row per wave)
+  int32_t wide;           // one-token step, rpp > 1: each lane takes up to U * CPL chunks of one row
+                          // (instead of CPL chunks of each of U rows)
 };
 
 // int4 with one group per row (per-channel): a shift past any row's chunk

@@ -265,17 +265,37 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     a.cpl = (v.cmax || v.tiled) ? (int32_t)passes : 1;
     // one-token kernels: rows of one pass that would leave half the lanes
     // idle share a wave pass, L = 64 / rpp lanes each (L >= 8 and L * CPL
-    // chunks cover the row)
+    // chunks cover the row).  A lane holds u x CPL chunk slots: CPL chunks of
+    // each of u rows, or ("wide") up to u * CPL chunks of one row, whichever
+    // leaves fewer slots past the row's end (a 43-chunk row: 32 lanes x 2
+    // fill 67 % of the slots, 16 lanes x 3 fill 90 %)
     a.rpp = 1;
+    a.wide = 0;
+    int64_t slots = passes * per_wave_max;   // chunk slots a row costs (arithmetic)
     if (!v.tiled && !v.verify && passes == 1) {
       const int64_t lanes = (chunks + v.cpl_max - 1) / v.cpl_max;
       int L = kWave;
       while (L > 8 && L / 2 >= lanes) L /= 2;
-      a.rpp = kWave / L;
+      const int64_t s_pair = (int64_t)L * v.cpl_max;
+      const int64_t per_lane = (int64_t)v.u * v.cpl_max;
+      int Lw = kWave;
+      while (Lw > 8 && (int64_t)(Lw / 2) * per_lane >= chunks) Lw /= 2;
+      const int64_t s_wide = (int64_t)Lw * ((chunks + Lw - 1) / Lw);
+      if (format != WQ_FORMAT_INT8 && Lw < kWave && 10 * s_pair >= 11 * s_wide) {
+        // wide pays off when it uses at least ~10 % more of its slots (not
+        // for int8, whose kernel has no wide passes)
+        a.rpp = kWave / Lw;
+        a.wide = 1;
+        slots = s_wide;
+      } else {
+        a.rpp = kWave / L;
+        if (a.rpp > 1) slots = s_pair;
+      }
     }
     // the verify kernel's batch is a block of 16-row tiles, the
-    // shared-activation kernel's u rows of one wave (u x rpp with short rows)
-    const int64_t rows_per_batch = (int64_t)v.u * a.rpp;
+    // shared-activation kernel's u rows of one wave (u x rpp with short rows;
+    // rpp rows when wide)
+    const int64_t rows_per_batch = a.wide ? (int64_t)a.rpp : (int64_t)v.u * a.rpp;
     a.batches = (a.n + rows_per_batch - 1) / rows_per_batch;
     a.batch_begin = total_batches;
     total_batches += a.batches;
@@ -286,10 +306,7 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
     // including the lanes past a row's end in its last pass: weigh a batch by
     // its padded length so that rows whose length is not a multiple of a
     // pass (e.g. k = 11008) get proportionally shorter ranges
-    if (v.cmax || v.tiled) {
-      const int64_t padded = a.rpp > 1 ? (int64_t)(kWave / a.rpp) * v.cpl_max : passes * per_wave_max;
-      batch_bytes[(size_t)i] *= (double)padded / (double)chunks;
-    }
+    if (v.cmax || v.tiled) batch_bytes[(size_t)i] *= (double)(v.tiled ? passes * per_wave_max : slots) / (double)chunks;
   }
   int rc = check_device();
   if (rc) return rc;

@@ -116,15 +116,19 @@ __device__ __forceinline__ void load_pass_packed(const GemvArgs& a, int64_t batc
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = q + j * L;
-      bt.w[u][j] = buffer_load16_nt(rw, c < a.chunks ? (uint32_t)s * rb + (uint32_t)c * 16u : 0x80000000u);
+      // wide passes (one row per lane): skip the slots past every lane's
+      // chunks (wave-uniform); with U rows per lane every slot is in use
+      if (U > 1 || j * L < a.chunks)
+        bt.w[u][j] = buffer_load16_nt(rw, c < a.chunks ? (uint32_t)s * rb + (uint32_t)c * 16u : 0x80000000u);
     }
     if constexpr (F::kGroupAux) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.sz + rr * words, rows_ok * (uint32_t)words * 4u);
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         const int c = q + j * L;
-        bt.aux[u][j] = buffer_load4_nt(
-            rs, c < a.chunks ? ((uint32_t)s * (uint32_t)words + (uint32_t)(c >> a.gshift)) * 4u : 0x80000000u);
+        if (U > 1 || j * L < a.chunks)
+          bt.aux[u][j] = buffer_load4_nt(
+              rs, c < a.chunks ? ((uint32_t)s * (uint32_t)words + (uint32_t)(c >> a.gshift)) * 4u : 0x80000000u);
       }
     } else {
 #pragma unroll
@@ -208,6 +212,7 @@ __device__ __forceinline__ void finish_pass_packed(const GemvArgs& a, int64_t ba
   const int s = lane / L, q = lane - s * L;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
+    if (U == 1 && j * L >= a.chunks) break;   // as loaded (load_pass_packed)
     const typename F::X xv = F::lds_x(xs, CMAX, q + j * L);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -610,6 +615,16 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_step_shared_kernel(const Gemv
       for (int c = threadIdx.x; c < cpad; c += WAVES * kWave) F::stage(a.x, a.chunks, c, xs, CMAX);
       __syncthreads();
     };
+    // wide passes for the formats whose activations are pre-decoded pairs
+    // (int8's fp32 activations for four chunk slots of one row would not fit
+    // the 16-wave register budget)
+    if constexpr (!F::kRowScale) {
+      if (a.rpp > 1 && a.wide) {
+        stream_segment_packed<F, 1, U * CPL, CMAX>(a, lb, le, xs, &ctr[par], lane, stage);
+        par ^= 1;
+        return;
+      }
+    }
     if (a.rpp > 1)
       stream_segment<F, U, CPL, CMAX, PF, true>(a, lb, le, xs, &ctr[par], lane, stage);
     else

@@ -215,23 +215,25 @@ def test_step_balance_never_changes_results(fmt, m):
 
 
 # The balance state sits at the end of a step workspace: the per-workgroup
-# state every step kernel uses (int32 done, launches, pad[2]; float w[8192],
-# cost[8192], time[8192]; double cum[8193]; pad to 16 bytes), then the verify
-# kernel's long-row state (48 bytes: double f, t[2], c[2], pad).
+# state every step kernel uses (int32 done, epoch, pad[2]; float w[8192];
+# float cost[2][8192], time[2][8192] and double cum[2][8193] by launch
+# parity), then the verify kernel's long-row state (48 bytes: double f, t[2],
+# c[2], pad).
 _MAXG = 8192
-_STEP_BAL, _VERIFY_BAL = 16 + 12 * _MAXG + 8 * (_MAXG + 1) + 8, 48
+_STEP_BAL, _VERIFY_BAL = 16 + 4 * _MAXG + 16 * _MAXG + 16 * (_MAXG + 1), 48
 
 
 @pytest.mark.parametrize("fmt,m", [("int4g32", 1), ("int8", 5), ("int4g32", 5)])
 def test_step_balance_feedback_runs(fmt, m):
-    """The last workgroup of every launch turns the launch's reports into the
-    next launch's factors: after several launches the `done` count is zero
-    again and the launches were counted, the workgroup weights have mean 1
-    and stay within their clamp's range, every workgroup reported a positive
-    cost and time, and the cumulative shares run from 0 to 1 in steps of
-    w / G; verify kernel (short and long rows in one plan): the long-row sums
-    are cleared and the long-row factor has left its prior of 1.2.  A report
-    lost or counted twice would leave `done` non-zero."""
+    """Each launch reports into its parity's buffers, its first workgroup to
+    finish turns the previous launch's reports into the shares of the launch
+    after the next, and its last advances the launch count.  After a dozen
+    launches: `done` back at zero and every launch counted, workgroup weights
+    of mean 1 within their clamp's range, a positive report from every
+    workgroup in both buffers, and the next launch's shares running from 0 to
+    1 in steps of w / G; verify kernel (short and long rows in one plan): the
+    long-row sums cleared and the long-row factor moved off its prior of 1.2.
+    A report lost or counted twice would leave `done` non-zero."""
     import torch
     import weight_only_quantized_wq_amd as wq
     say(f"balance feedback {fmt} m={m}")
@@ -249,14 +251,18 @@ def test_step_balance_feedback_runs(fmt, m):
         assert (t0, t1, c0, c1) == (0.0, 0.0, 0.0, 0.0)
         assert 0.5 <= f <= 4.0 and f != 1.2, f"long-row factor {f}"
     G = plan.groups
-    done, launches = (int(v) for v in np.frombuffer(sb[:8].tobytes(), dtype=np.int32))
-    assert launches == 12, f"{launches} launches counted"
-    arr = np.frombuffer(sb[16:16 + 12 * _MAXG].tobytes(), dtype=np.float32).reshape(3, _MAXG)
-    w, cost, tm = arr[0, :G], arr[1, :G], arr[2, :G]
-    cum = np.frombuffer(sb[16 + 12 * _MAXG:16 + 12 * _MAXG + 8 * (G + 1)].tobytes(), dtype=np.float64)
+    done, epoch = (int(v) for v in np.frombuffer(sb[:8].tobytes(), dtype=np.int32))
     assert done == 0, f"{done} reports left over"
+    assert epoch == 12, f"{epoch} launches counted"
+    o = 16
+    w = np.frombuffer(sb[o:o + 4 * G].tobytes(), dtype=np.float32)
+    o += 4 * _MAXG
+    rep = np.frombuffer(sb[o:o + 16 * _MAXG].tobytes(), dtype=np.float32).reshape(2, 2, _MAXG)[:, :, :G]
+    o += 16 * _MAXG
+    cum = np.frombuffer(sb[o:o + 16 * (_MAXG + 1)].tobytes(), dtype=np.float64).reshape(2, _MAXG + 1)
+    nxt = cum[epoch & 1, :G + 1]
     # clamped to [0.5, 2], then scaled to mean 1
     assert np.all((w >= 0.25) & (w <= 4.0)) and abs(float(w.mean()) - 1.0) < 1e-3, w
-    assert np.all(cost > 0) and np.all(tm > 0)
-    assert cum[0] == 0.0 and cum[G] == 1.0 and np.all(np.diff(cum) > 0)
-    assert np.allclose(np.diff(cum), w / G, rtol=1e-4, atol=1e-9)
+    assert np.all(rep > 0), "a workgroup's report is missing"
+    assert nxt[0] == 0.0 and nxt[G] == 1.0 and np.all(np.diff(nxt) > 0)
+    assert np.allclose(np.diff(nxt), w / G, rtol=1e-4, atol=1e-9)

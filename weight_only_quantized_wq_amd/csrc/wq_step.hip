@@ -338,11 +338,11 @@ extern "C" int wq_decode_step_prepare(int32_t format, int32_t m, const wq_matrix
   memcpy(host.data() + lay.bcost, batch_bytes.data(), (size_t)count * 8);
   // equal shares to begin with: every workgroup weighs 1
   StepBalance* bal = reinterpret_cast<StepBalance*>(host.data() + lay.bal);
-  for (int g = 0; g < groups; ++g) {
-    bal->w[g] = 1.0f;
-    bal->cum[g] = (double)g / (double)groups;
+  for (int g = 0; g < groups; ++g) bal->w[g] = 1.0f;
+  for (int p = 0; p < 2; ++p) {
+    for (int g = 0; g < groups; ++g) bal->cum[p][g] = (double)g / (double)groups;
+    bal->cum[p][groups] = 1.0;
   }
-  bal->cum[groups] = 1.0;
   VerifyBalance vbal{};
   vbal.f = kVerifyLongRowPrior;
   memcpy(host.data() + lay.vbal, &vbal, sizeof(vbal));

@@ -375,24 +375,28 @@ __device__ __forceinline__ void stream_segment(const GemvArgs& a, int64_t lb, in
 // boundary inside a range costs a staging and a drain) and on the CU it runs
 // on, and for a given plan it repeats from launch to launch: the workgroup
 // -> CU assignment is stable and the ranges move little.  So each workgroup
-// reports the cost of its range and the time it took; the last workgroup of
-// the launch turns these into relative speeds and writes the share of the
-// step before each workgroup, which the next launch cuts with.  The first
-// launch of a plan sets the speeds to its measured rates, the second and
-// third move them half and a third of the way to theirs, every later launch
-// a quarter; clamped to [0.5, 2], mean 1.
-// Every workgroup reads the same table, so the ranges always partition the
-// step; which workgroup computes a row never changes the row's result.
+// reports the cost of its range and the time it took, and a launch cuts with
+// per-workgroup shares derived from the reports of the launch before the
+// previous one.  Launch n (parity p = n & 1) reads shares[p] and writes
+// reports[p]; the first of its workgroups to finish turns reports[p ^ 1]
+// (launch n - 1, complete) into relative speeds and writes shares[p ^ 1]
+// for launch n + 1, while the others are still streaming, so none of this
+// work lengthens the launch; the last to finish only advances the launch
+// count.  Nothing a launch reads is written during it.  The speeds move all
+// the way to the first measurement, half and a third of the way for the
+// second and third, a quarter for every later one; clamped to [0.5, 2],
+// mean 1.  Every workgroup reads the same table, so the ranges always
+// partition the step; which workgroup computes a row never changes the
+// row's result.
 constexpr int kStepMaxGroups = 8192;
 struct StepBalance {
-  int32_t done;                     // workgroups finished in this launch
-  int32_t launches;                 // launches of the plan so far (saturates)
+  int32_t done;                        // workgroups finished in this launch
+  int32_t epoch;                       // launches of the plan so far (advanced by each launch's last workgroup)
   int32_t pad[2];
-  float w[kStepMaxGroups];          // relative speed of workgroup g (mean 1 over the launch's workgroups)
-  float cost[kStepMaxGroups];       // last launch: cost of workgroup g's range (units of the cut)
-  float time[kStepMaxGroups];       // last launch: its duration (wall-clock ticks)
-  double cum[kStepMaxGroups + 1];   // share of the step before workgroup g (cum[0] = 0, cum[G] = 1)
-  int32_t pad2[2];
+  float w[kStepMaxGroups];             // relative speed of workgroup g (mean 1 over the launch's workgroups)
+  float cost[2][kStepMaxGroups];       // by launch parity: cost of workgroup g's range (units of the cut)
+  float time[2][kStepMaxGroups];       // by launch parity: its duration (wall-clock ticks)
+  double cum[2][kStepMaxGroups + 1];   // by launch parity: share of the step before workgroup g
 };
 static_assert(sizeof(StepBalance) % 16 == 0, "the verify state follows at a 16-byte boundary");
 
@@ -452,12 +456,14 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* lds, do
   return before + inc - v;
 }
 
-// The last workgroup of a launch (all NT threads): new speed weights from
-// the launch's reports and the cumulative shares the next launch cuts with.
-// Thread i handles workgroups [i * per, (i + 1) * per).  `lds`: NT / 64
-// doubles of LDS the workgroup no longer needs.
+// The first workgroup of a launch to finish (all NT threads): new speed
+// weights from the reports in buffer `q` (measurement number `m` of the
+// plan) and the cumulative shares written to buffer `q`, which the launch
+// after this one cuts with.  Thread i handles workgroups [i * per,
+// (i + 1) * per).  `lds`: NT / 64 doubles of LDS the workgroup no longer
+// needs.
 template <int NT>
-__device__ __forceinline__ void step_balance_update(StepBalance* b, int G, double* lds) {
+__device__ __forceinline__ void step_balance_update(StepBalance* b, int G, int q, int m, double* lds) {
   constexpr int P = kStepMaxGroups / NT;
   const int per = (G + NT - 1) / NT;
   const int j0 = (int)threadIdx.x * per;
@@ -469,8 +475,8 @@ __device__ __forceinline__ void step_balance_update(StepBalance* b, int G, doubl
     wv[i] = 1.0f;
     const int j = j0 + i;
     if (i < per && j < G) {
-      const float c = __hip_atomic_load(&b->cost[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float t = __hip_atomic_load(&b->time[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float c = __hip_atomic_load(&b->cost[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float t = __hip_atomic_load(&b->time[q][j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       wv[i] = __hip_atomic_load(&b->w[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       r[i] = (c > 0.0f && t > 0.0f) ? c / t : 0.0f;
       if (r[i] > 0.0f) {
@@ -482,8 +488,7 @@ __device__ __forceinline__ void step_balance_update(StepBalance* b, int G, doubl
   rs = block_sum<NT>(rs, lds);
   rn = block_sum<NT>(rn, lds);
   const float mean = rn > 0.0 ? (float)(rs / rn) : 0.0f;
-  const int n = __hip_atomic_load(&b->launches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const float gain = n < 3 ? 1.0f / (float)(n + 1) : 0.25f;
+  const float gain = m < 3 ? 1.0f / (float)(m + 1) : 0.25f;
   double local = 0.0;
 #pragma unroll
   for (int i = 0; i < P; ++i) {
@@ -500,41 +505,57 @@ __device__ __forceinline__ void step_balance_update(StepBalance* b, int G, doubl
     if (i < per && j < G) {
       run += wv[i];
       __hip_atomic_store(&b->w[j], (float)(wv[i] * (double)G / all), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&b->cum[j + 1], j + 1 == G ? 1.0 : run / all, __ATOMIC_RELAXED,
+      __hip_atomic_store(&b->cum[q][j + 1], j + 1 == G ? 1.0 : run / all, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (threadIdx.x == 0) {
-    if (n < (1 << 30)) atomicExch(&b->launches, n + 1);
-    atomicExch(&b->done, 0);
-  }
 }
 
-// End of a balanced launch (every thread of the workgroup): the workgroup
-// reports the cost of its range (units of the cut) and the time since
-// `t_start`; the last workgroup to report computes the next launch's shares.
-// `lds`: WAVES doubles of LDS the workgroup no longer needs.
-template <int WAVES>
-__device__ __forceinline__ void step_balance_report(StepBalance* b, double cost, long long t_start, double* lds) {
-  __shared__ int last;
+// This launch's number (read once at the start by every workgroup; only the
+// launch's last workgroup changes it, after every workgroup has finished).
+__device__ __forceinline__ int step_epoch(const StepBalance* b) { return __builtin_amdgcn_readfirstlane(b->epoch); }
+
+// End of a balanced launch (every thread of the workgroup; `epoch` as read
+// at its start): the workgroup reports the cost of its range (units of the
+// cut) and the time since `t_start`.  The first workgroup to finish computes
+// the shares of the launch after the next from the previous launch's
+// reports; the last runs `on_last` (thread 0) and advances the launch
+// count.  `lds`: WAVES doubles of LDS the workgroup no longer needs.
+template <int WAVES, class OnLast>
+__device__ __forceinline__ void step_balance_report(StepBalance* b, int epoch, double cost, long long t_start,
+                                                    double* lds, OnLast&& on_last) {
+  __shared__ int role;   // bit 0: first to finish, bit 1: last
   const int G = (int)gridDim.x;
+  const int p = epoch & 1;
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_store(&b->cost[blockIdx.x], (float)cost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&b->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
+    __hip_atomic_store(&b->cost[p][blockIdx.x], (float)cost, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&b->time[p][blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     report_in_order();
-    last = atomicAdd(&b->done, 1) == G - 1;
+    const int r = atomicAdd(&b->done, 1);
+    role = (r == 0 ? 1 : 0) | (r == G - 1 ? 2 : 0);
+    if (r == G - 1) {
+      // every workgroup has reported (and read this launch's epoch)
+      on_last();
+      atomicExch(&b->done, 0);
+      if (epoch < (1 << 30)) atomicExch(&b->epoch, epoch + 1);
+    }
   }
   __syncthreads();
-  // every workgroup has reported: the shares of the next launch
-  if (last) step_balance_update<WAVES * kWave>(b, G, lds);
+  if ((role & 1) && epoch >= 1) step_balance_update<WAVES * kWave>(b, G, p ^ 1, epoch - 1, lds);
+}
+template <int WAVES>
+__device__ __forceinline__ void step_balance_report(StepBalance* b, int epoch, double cost, long long t_start,
+                                                    double* lds) {
+  step_balance_report<WAVES>(b, epoch, cost, t_start, lds, [] {});
 }
 
-// Workgroup g's share [c0, c1) of a launch of cost `total`.
-__device__ __forceinline__ void step_share(const StepBalance* b, double total, double& c0, double& c1) {
-  c0 = total * b->cum[blockIdx.x];
-  c1 = (int)blockIdx.x + 1 == (int)gridDim.x ? total : total * b->cum[blockIdx.x + 1];
+// Workgroup g's share [c0, c1) of a launch of cost `total` (launch `epoch`).
+__device__ __forceinline__ void step_share(const StepBalance* b, int epoch, double total, double& c0, double& c1) {
+  const double* cum = b->cum[epoch & 1];
+  c0 = total * cum[blockIdx.x];
+  c1 = (int)blockIdx.x + 1 == (int)gridDim.x ? total : total * cum[blockIdx.x + 1];
 }
 
 // The persistent step's frame.  Each workgroup cuts its own contiguous range
@@ -549,8 +570,9 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
   __shared__ int first_mat;
   __shared__ double bal_lds[WAVES];
   const long long t_start = wall_clock64();
+  const int epoch = step_epoch(cuts.bal);
   double c0, c1;
-  step_share(cuts.bal, cuts.prefix[cuts.count], c0, c1);
+  step_share(cuts.bal, epoch, cuts.prefix[cuts.count], c0, c1);
   // the batch at cost c: first batch of matrix i (prefix[i] <= c < prefix[i + 1])
   // whose start is at or past c; every matrix is checked by one thread
   if (threadIdx.x == 0) {
@@ -590,7 +612,7 @@ __device__ __forceinline__ void step_frame(const GemvArgs* __restrict__ mats, co
     gb = a.batch_begin + le;
     ++mi;
   }
-  step_balance_report<WAVES>(cuts.bal, c1 - c0, t_start, bal_lds);
+  step_balance_report<WAVES>(cuts.bal, epoch, c1 - c0, t_start, bal_lds);
 }
 
 // mats: per-matrix descriptors (batch = U rows; `cpl` holds the number of

@@ -692,7 +692,6 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   __shared__ int ctr;
   __shared__ int64_t range[2];
   __shared__ int first_mat;
-  __shared__ int last;
   const int lane = lane_id();
   const int wave = wave_id();
   const int rq = lane >> 4;
@@ -703,9 +702,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   // this workgroup's range: its speed-weighted share of the step's cost
   const long long t_start = wall_clock64();
   const double f = cuts.bal->f;
-  const int G = (int)gridDim.x;
+  const int epoch = step_epoch(cuts.wg);
   double c0, c1;
-  step_share(cuts.wg, cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count], c0, c1);
+  step_share(cuts.wg, epoch, cuts.pre_short[cuts.count] + f * cuts.pre_long[cuts.count], c0, c1);
   if (threadIdx.x == 0) {
     range[0] = mats[cuts.count - 1].batch_begin + mats[cuts.count - 1].batches;
     range[1] = range[0];
@@ -793,44 +792,37 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
     ++mi;
   }
   __syncthreads();
+  VerifyBalance* b = cuts.bal;
   if (threadIdx.x == 0) {
     if (kprev >= 0) tk[kprev] += (double)(wall_clock64() - tprev);
-    VerifyBalance* b = cuts.bal;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       atomicAdd(&b->t[e], tk[e]);
       atomicAdd(&b->c[e], ck[e]);
     }
-    StepBalance* sb = cuts.wg;
-    __hip_atomic_store(&sb->cost[blockIdx.x], (float)(c1 - c0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&sb->time[blockIdx.x], (float)(wall_clock64() - t_start), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    report_in_order();
-    last = atomicAdd(&sb->done, 1) == G - 1;
-    if (last) {
-      // every workgroup has reported: the long-row factor for the next launch
-      double t[2], c[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        t[e] = __hip_atomic_load(&b->t[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        c[e] = __hip_atomic_load(&b->c[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (t[0] > 0.0 && t[1] > 0.0 && c[0] > 0.0 && c[1] > 0.0) {
-        double nf = 0.75 * f + 0.25 * ((t[1] / c[1]) / (t[0] / c[0]));
-        nf = fmin(fmax(nf, 0.5), 4.0);
-        __hip_atomic_store(&b->f, nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        __hip_atomic_store(&b->t[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&b->c[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
   }
-  __syncthreads();
-  // and the workgroups' shares (clears the `done` count)
+  // the sums above are performed before this workgroup's count (the report's
+  // wait), so the last workgroup reads all of them
   static_assert(sizeof(part) >= WAVES * sizeof(double), "the partial sums' LDS holds the update's sums");
-  if (last) step_balance_update<WAVES * kWave>(cuts.wg, G, reinterpret_cast<double*>(&part));
+  step_balance_report<WAVES>(cuts.wg, epoch, c1 - c0, t_start, reinterpret_cast<double*>(&part), [&] {
+    // the long-row factor for the next launch
+    double t[2], c[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      t[e] = __hip_atomic_load(&b->t[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      c[e] = __hip_atomic_load(&b->c[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (t[0] > 0.0 && t[1] > 0.0 && c[0] > 0.0 && c[1] > 0.0) {
+      double nf = 0.75 * f + 0.25 * ((t[1] / c[1]) / (t[0] / c[0]));
+      nf = fmin(fmax(nf, 0.5), 4.0);
+      __hip_atomic_store(&b->f, nf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      __hip_atomic_store(&b->t[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&b->c[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  });
 }
 
 }  // namespace wq

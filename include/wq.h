@@ -349,15 +349,19 @@ int64_t wq_moe_step_workspace_bytes(int32_t count);
  * e == 8, dim and f, with dim % 16 == 0, f % 16 == 0, 16 <= dim <= 14336 and
  * 16 <= f <= 16384 (a layer's activations are staged whole in LDS).
  * Validates every layer on the host (null -> sizes -> alignment), then copies
- * the layer descriptors into `workspace` (device memory, 16-byte aligned,
- * caller-owned, unmodified while the plan is used).  The copy is
- * synchronous: prepare once, outside any graph capture.
+ * the layer descriptors and the two launches' initial balance state into
+ * `workspace` (device memory, 16-byte aligned, caller-owned, unmodified
+ * while the plan is used).  The copy is synchronous: prepare once, outside
+ * any graph capture.
  */
 int wq_moe_step_prepare(int64_t e, int64_t dim, int64_t f, const wq_moe_layer* layers, int32_t count,
                         void* workspace, int64_t workspace_bytes, wq_moe_plan* plan);
 
 /* Launches a prepared MoE step on `stream` (asynchronous; may be captured
- * into a HIP graph).  Runs of plans that share buffers must not overlap. */
+ * into a HIP graph).  Runs of one plan must not overlap (each run measures
+ * its workgroups' speeds into the workspace and later runs cut their per-CU
+ * ranges from them); runs of plans that share buffers must not overlap
+ * either. */
 int wq_moe_step_run(const wq_moe_plan* plan, void* stream);
 
 /* Static text for a wq_status value ("unknown status" otherwise). */

@@ -209,6 +209,51 @@ def test_moe_step_matches_oracle_and_single_layer_calls(wq, dim, f, seeds):
             assert np.array_equal(host(b["y32"]), f0), f"run {rep} differs"
 
 
+# The two launches' balance states sit at the end of a MoE step workspace,
+# W13 then W2, each: int32 done, epoch, pad[2]; float w[8192]; float
+# cost[2][8192], time[2][8192] and double cum[2][8193] by launch parity.
+_MAXG = 8192
+_BAL = 16 + 4 * _MAXG + 16 * _MAXG + 16 * (_MAXG + 1)
+
+
+def test_moe_step_balance_feedback_runs(wq):
+    """After several runs of a three-layer plan each launch's balance state
+    is consistent: `done` back at zero and every launch counted, workgroup
+    weights of mean 1 within their clamp's range, a positive report from
+    every workgroup in both buffers, and the next launch's shares running
+    from 0 to 1 in steps of w / G."""
+    import torch
+    dim, f = 1024, 2816
+    say("moe step balance feedback")
+    hl = _step_layers((21, 22, 23), dim, f)
+    layers = []
+    for (x, logits, q13, s13, q2, s2, _, _, _) in hl:
+        layers.append((dev(x), dev(logits), dev(q13), dev(s13), dev(q2), dev(s2),
+                       torch.empty(2 * f, dtype=torch.float32, device="cuda"),
+                       torch.empty(dim, dtype=torch.float32, device="cuda"), None, None, None))
+    nbytes = wq.wq_moe_step_workspace_bytes(len(layers))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    plan = wq.wq_moe_step_prepare(8, dim, f, layers, ws)
+    for _ in range(9):
+        wq.wq_moe_step_run(plan)
+    torch.cuda.synchronize()
+    tail = ws[nbytes - 2 * _BAL:].cpu().numpy()
+    for which, (sb, G) in enumerate(((tail[:_BAL], plan.grid13), (tail[_BAL:], plan.grid2))):
+        done, epoch = (int(v) for v in np.frombuffer(sb[:8].tobytes(), dtype=np.int32))
+        assert done == 0 and epoch == 9, (which, done, epoch)
+        o = 16
+        w = np.frombuffer(sb[o:o + 4 * G].tobytes(), dtype=np.float32)
+        o += 4 * _MAXG
+        rep = np.frombuffer(sb[o:o + 16 * _MAXG].tobytes(), dtype=np.float32).reshape(2, 2, _MAXG)[:, :, :G]
+        o += 16 * _MAXG
+        cum = np.frombuffer(sb[o:o + 16 * (_MAXG + 1)].tobytes(), dtype=np.float64).reshape(2, _MAXG + 1)
+        nxt = cum[epoch & 1, :G + 1]
+        assert np.all((w >= 0.25) & (w <= 4.0)) and abs(float(w.mean()) - 1.0) < 1e-3, (which, w)
+        assert np.all(rep > 0), which
+        assert nxt[0] == 0.0 and nxt[G] == 1.0 and np.all(np.diff(nxt) > 0), which
+        assert np.allclose(np.diff(nxt), w / G, rtol=1e-4, atol=1e-9), which
+
+
 def test_moe_step_full_mixtral_shape_unselected_not_read(wq):
     """Two Mixtral-8x7B-shaped layers through the two-launch step, the
     unselected experts holding codes that would change the result."""

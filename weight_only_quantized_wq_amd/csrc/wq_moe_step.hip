@@ -24,6 +24,10 @@ static const void* w2_kernel() {
   return reinterpret_cast<const void*>(moe_w2_step_kernel<kW2U, kW2Cpl, kW2Waves, kW2Pf>);
 }
 
+// Workspace: the layer descriptors, then the balance state of the W13
+// launch and that of the W2 launch.
+static int64_t desc_bytes(int32_t count) { return ((int64_t)count * (int64_t)sizeof(MoeLayerDesc) + 15) / 16 * 16; }
+
 static int64_t grid_for(int resident, int64_t batches) {
   int64_t g = resident < 1 ? 1 : resident;
   if (g > batches) g = batches;
@@ -36,7 +40,7 @@ using namespace wq;
 
 extern "C" int64_t wq_moe_step_workspace_bytes(int32_t count) {
   if (count < 0) return 0;
-  return ((int64_t)count * (int64_t)sizeof(MoeLayerDesc) + 15) / 16 * 16;
+  return desc_bytes(count) + 2 * (int64_t)sizeof(StepBalance);
 }
 
 extern "C" int wq_moe_step_prepare(int64_t e, int64_t dim, int64_t f, const wq_moe_layer* layers, int32_t count,
@@ -86,20 +90,34 @@ extern "C" int wq_moe_step_prepare(int64_t e, int64_t dim, int64_t f, const wq_m
     D.sel = L.sel;
     D.gates = L.gates;
   }
-  hipError_t err = hipMemcpy(workspace, desc.data(), desc.size() * sizeof(MoeLayerDesc), hipMemcpyHostToDevice);
-  if (err != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(WQ_ERR_LAUNCH, "%s: copying the layer descriptors failed: %s", name, hipGetErrorString(err));
-  }
   const int64_t b13 = (int64_t)count * 2 * ((f + kW13U - 1) / kW13U);
   const int64_t b2 = (int64_t)count * ((dim + kW2U - 1) / kW2U);
+  int64_t grids[2] = {grid_for(resident_groups(w13_kernel(), kW13Waves * kWave), b13),
+                      grid_for(resident_groups(w2_kernel(), kW2Waves * kWave), b2)};
+  // descriptors, then both launches' balance states at equal shares
+  std::vector<char> host((size_t)need, 0);
+  memcpy(host.data(), desc.data(), desc.size() * sizeof(MoeLayerDesc));
+  for (int l = 0; l < 2; ++l) {
+    if (grids[l] > kStepMaxGroups) grids[l] = kStepMaxGroups;
+    StepBalance* bal = reinterpret_cast<StepBalance*>(host.data() + desc_bytes(count) + l * sizeof(StepBalance));
+    for (int64_t g = 0; g < grids[l]; ++g) bal->w[g] = 1.0f;
+    for (int p = 0; p < 2; ++p) {
+      for (int64_t g = 0; g < grids[l]; ++g) bal->cum[p][g] = (double)g / (double)grids[l];
+      bal->cum[p][grids[l]] = 1.0;
+    }
+  }
+  hipError_t err = hipMemcpy(workspace, host.data(), host.size(), hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(WQ_ERR_LAUNCH, "%s: copying the plan to the workspace failed: %s", name, hipGetErrorString(err));
+  }
   memset(plan, 0, sizeof(*plan));
   plan->dim = dim;
   plan->f = f;
   plan->e = (int32_t)e;
   plan->count = count;
-  plan->grid13 = (int32_t)grid_for(resident_groups(w13_kernel(), kW13Waves * kWave), b13);
-  plan->grid2 = (int32_t)grid_for(resident_groups(w2_kernel(), kW2Waves * kWave), b2);
+  plan->grid13 = (int32_t)grids[0];
+  plan->grid2 = (int32_t)grids[1];
   plan->workspace = workspace;
   return WQ_OK;
 }
@@ -111,14 +129,19 @@ extern "C" int wq_moe_step_run(const wq_moe_plan* plan, void* stream) {
     return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_moe_step_prepare", name);
   int rc = check_device();
   if (rc) return rc;
+  if (plan->grid13 > kStepMaxGroups || plan->grid2 > kStepMaxGroups)
+    return fail(WQ_ERR_SHAPE, "%s: the plan was not produced by wq_moe_step_prepare", name);
   MoeStepDims d{plan->dim, plan->f, plan->e, plan->count};
-  const MoeLayerDesc* L = reinterpret_cast<const MoeLayerDesc*>(plan->workspace);
+  char* ws = reinterpret_cast<char*>(const_cast<void*>(plan->workspace));
+  const MoeLayerDesc* L = reinterpret_cast<const MoeLayerDesc*>(ws);
+  StepBalance* bal13 = reinterpret_cast<StepBalance*>(ws + desc_bytes(plan->count));
+  StepBalance* bal2 = bal13 + 1;
   hipStream_t s = (hipStream_t)stream;
   hipLaunchKernelGGL((moe_w13_step_kernel<kW13U, kW13Cpl, kW13Waves, kW13Pf>), dim3((unsigned)plan->grid13),
-                     dim3(kW13Waves * kWave), 0, s, L, d);
+                     dim3(kW13Waves * kWave), 0, s, L, d, bal13);
   rc = launch_status(name);
   if (rc) return rc;
   hipLaunchKernelGGL((moe_w2_step_kernel<kW2U, kW2Cpl, kW2Waves, kW2Pf>), dim3((unsigned)plan->grid2),
-                     dim3(kW2Waves * kWave), 0, s, L, d);
+                     dim3(kW2Waves * kWave), 0, s, L, d, bal2);
   return launch_status(name);
 }

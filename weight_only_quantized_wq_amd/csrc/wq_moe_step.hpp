@@ -8,8 +8,10 @@
 //
 // Both launches follow the shared-activation scheme of the decode step:
 //   * one workgroup per CU owns a contiguous range of the launch's batches
-//     (layer after layer; all layers have the same shape, so the ranges are
-//     computed from the grid, equal in size);
+//     (layer after layer; all layers have the same shape, so every batch
+//     costs the same), equal in size on a plan's first launches and then
+//     proportional to the workgroup's measured speed (StepBalance, one state
+//     per launch);
 //   * per layer segment the workgroup routes (softmax top-2 of the logits,
 //     equal logits -> lower index, gates renormalised over the pair; every
 //     workgroup derives the same choice) and stages the layer's activations
@@ -172,9 +174,18 @@ __device__ __forceinline__ void moe_stream(int64_t lo, int64_t hi, int passes, u
 }
 
 // Workgroup range [lo, hi) of a launch of `total` batches.
-__device__ __forceinline__ void moe_range(int64_t total, int64_t& lo, int64_t& hi) {
-  lo = total * (int64_t)blockIdx.x / (int64_t)gridDim.x;
-  hi = total * ((int64_t)blockIdx.x + 1) / (int64_t)gridDim.x;
+// This workgroup's batches [lo, hi) of `total` (launch `epoch`), from its
+// share of the launch: neighbours round their common boundary the same way.
+__device__ __forceinline__ void moe_range(const StepBalance* b, int epoch, int64_t total, int64_t& lo, int64_t& hi,
+                                          double& cost) {
+  double c0, c1;
+  step_share(b, epoch, (double)total, c0, c1);
+  lo = (int64_t)(c0 + 0.5);
+  hi = (int)blockIdx.x + 1 == (int)gridDim.x ? total : (int64_t)(c1 + 0.5);
+  if (lo > total) lo = total;
+  if (hi > total) hi = total;
+  if (hi < lo) hi = lo;
+  cost = c1 - c0;
 }
 
 // ---------------------------------------------------------------------------
@@ -182,18 +193,22 @@ __device__ __forceinline__ void moe_range(int64_t total, int64_t& lo, int64_t& h
 
 template <int U, int CPL, int WAVES, bool PF>
 __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayerDesc* __restrict__ layers,
-                                                                   MoeStepDims d) {
+                                                                   MoeStepDims d, StepBalance* bal) {
   constexpr int CMAX = moe_cmax<CPL, kMoeW13Words>();
   constexpr int NR = 2 * U;
   __shared__ __attribute__((aligned(16))) uint32_t xs[kMoeW13Words];
   __shared__ int ctr;
+  __shared__ double bal_lds[WAVES];
+  const long long t_start = wall_clock64();
+  const int epoch = step_epoch(bal);
   const int lane = lane_id();
   const int chunks = (int)(d.dim / 16);
   const int passes = (chunks + CPL * kWave - 1) / (CPL * kWave);
   const int64_t half = (d.f + U - 1) / U;   // batches per selected expert
   const int64_t per_layer = 2 * half;
   int64_t gb, gend;
-  moe_range(per_layer * d.count, gb, gend);
+  double cost;
+  moe_range(bal, epoch, per_layer * d.count, gb, gend, cost);
   while (gb < gend) {
     const int layer = (int)(gb / per_layer);
     const int64_t lo = gb - (int64_t)layer * per_layer;
@@ -275,6 +290,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
     moe_stream<NR, CPL, CMAX, 1>(lo, hi, passes, (uint32_t)d.dim, &ctr, lane, xs, acc, rows, scales, finish);
     gb = (int64_t)layer * per_layer + hi;
   }
+  step_balance_report<WAVES>(bal, epoch, cost, t_start, bal_lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -282,18 +298,22 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w13_step_kernel(const MoeLayer
 
 template <int U, int CPL, int WAVES, bool PF>
 __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerDesc* __restrict__ layers,
-                                                                  MoeStepDims d) {
+                                                                  MoeStepDims d, StepBalance* bal) {
   constexpr int CMAX = moe_cmax<CPL, kMoeW2Words / 2>();
   constexpr int PLANE = CMAX * FmtInt8::kLdsWordsPerChunk;
   constexpr int NR = 2 * U;
   __shared__ __attribute__((aligned(16))) uint32_t xs[kMoeW2Words];
   __shared__ int ctr;
+  __shared__ double bal_lds[WAVES];
+  const long long t_start = wall_clock64();
+  const int epoch = step_epoch(bal);
   const int lane = lane_id();
   const int chunks = (int)(d.f / 16);
   const int passes = (chunks + CPL * kWave - 1) / (CPL * kWave);
   const int64_t per_layer = (d.dim + U - 1) / U;
   int64_t gb, gend;
-  moe_range(per_layer * d.count, gb, gend);
+  double cost;
+  moe_range(bal, epoch, per_layer * d.count, gb, gend, cost);
   while (gb < gend) {
     const int layer = (int)(gb / per_layer);
     const int64_t lo = gb - (int64_t)layer * per_layer;
@@ -363,6 +383,7 @@ __global__ __launch_bounds__(WAVES * 64) void moe_w2_step_kernel(const MoeLayerD
     moe_stream<NR, CPL, CMAX, 2>(lo, hi, passes, (uint32_t)d.f, &ctr, lane, xs, acc, rows, scales, finish);
     gb = (int64_t)layer * per_layer + hi;
   }
+  step_balance_report<WAVES>(bal, epoch, cost, t_start, bal_lds);
 }
 
 }  // namespace wq

@@ -408,14 +408,15 @@ struct StepCuts {
   int32_t count;          // matrices
 };
 
-// A workgroup's balance report: agent-scope atomic stores or adds, counted
-// in by the `done` atomic after them, and the last workgroup reads them back
-// with agent-scope atomic loads.  The only order needed is "report performed
+// A workgroup's balance report: agent-scope atomic stores or adds, then the
+// `done` count; a later launch (per-workgroup speeds) or this launch's last
+// workgroup (the verify kernel's long-row sums) reads them back with
+// agent-scope atomic loads.  The only order needed is "report performed
 // before the count", which a wait for this wave's outstanding memory
 // operations gives; an agent-scope fence would add an L2 write-back and
 // invalidate per workgroup (several microseconds at the end of every
-// launch).  A report that came late would only blur one launch's weights:
-// the cuts are valid for any weights.
+// launch).  A report that came late would only blur one launch's factors:
+// the cuts are valid for any factors.
 __device__ __forceinline__ void report_in_order() { wait_vmem_all(); }
 
 // Sum over the workgroup of one value per thread (NT threads).

@@ -158,6 +158,15 @@ int wq_gemv_int4(const uint16_t* x, const uint8_t* qpacked, const uint16_t* sz, 
  * WQ_SMALLM_ENGINE=valu (read at each call) moves 2, 3 and 5 tokens to the
  * vector ALU where its plans reach (k <= 32768 for int4, 16384 for int8),
  * for comparison; =mfma or unset keeps the matrix cores (measured faster).
+ * On the matrix cores, 2..5 tokens over large matrices (k >= 8192 within
+ * one activation window, at least 1280 blocks of 32 rows) run a kernel
+ * whose workgroups claim row blocks from a per-call counter in a static
+ * device array of 1024 slots, each launch taking the next slot and leaving
+ * it zeroed: up to 1024 such launches may be in flight on one device at
+ * once.  WQ_SMALLM_KERNEL=split or =claim (read at each call) forces the
+ * fixed-stride or the claiming kernel wherever a row fits one activation
+ * window, for comparison; results agree to fp32 rounding and each kernel's
+ * are reproducible bit for bit.
  */
 int wq_gemm_smallM(const uint16_t* x, int64_t m, const uint8_t* qpacked, const uint16_t* sz,
                    int64_t n, int64_t k, float* y_f32, uint16_t* y_bf16, void* stream);

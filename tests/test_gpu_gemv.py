@@ -290,6 +290,44 @@ def test_gemm_small_m_int4_groups(wq, m, group, n, k):
     say(f"  err f32={e[0]:.2e} bf16={e[1]:.2e}")
 
 
+# The two matrix-core kernels for 2..5 token rows (WQ_SMALLM_KERNEL forces
+# one): 1..16 (scale, zero) windows per 32-row block, one block or many more
+# blocks than workgroups (blocks claimed at run time), ragged last blocks,
+# every group size the claiming kernel takes.
+KERNEL_CASES = [(5, 32, 45, 4096), (2, 32, 3, 32), (5, 32, 70, 8192), (3, 32, 16411, 512), (4, 32, 39995, 256),
+                (5, 32, 49999, 1024), (2, 32, 9000, 16384), (3, 32, 40000, 2048), (4, 32, 9001, 8192),
+                (5, 128, 20000, 4096), (2, 0, 30001, 1024), (3, 64, 12345, 8192)]
+
+
+@pytest.mark.parametrize("m,group,n,k", KERNEL_CASES)
+def test_gemm_small_m_kernels(wq, monkeypatch, m, group, n, k):
+    """The fixed-stride and the claiming matrix-core kernels each match the
+    oracle, each other to fp32 rounding, and themselves bit for bit on a
+    second call (the claiming kernel's blocks go to whichever workgroup
+    claims them first)."""
+    from oracle.quant import quantize_int4
+    g = group or k
+    say(f"kernels m={m} group={g} n={n} k={k}")
+    w = host_normal((n, k), 0.015, 954, m, n, k)
+    p, sz = quantize_int4(w, g)
+    x = host_bf16_normal((m, k), 954, m, n, k + 1)
+    ref = gemm_small_m(x, p, sz)
+    pd, szd, xd = _d(p), _d(sz), _d(x)
+    got = {}
+    for kind in ("split", "claim"):
+        monkeypatch.setenv("WQ_SMALLM_KERNEL", kind)
+        runs = []
+        for _ in range(2):
+            (b32, y32), (b16, y16) = _outputs(n, m)
+            wq.wq_gemm_smallM_int4(xd, m, pd, szd, n, k, g, y32, y16)
+            _compare(y32, y16, ref, (m, n))
+            _check_guards(b32, b16, m * n)
+            runs.append(host(y32).reshape(m, n))
+        assert_same(runs[1], runs[0])
+        got[kind] = runs[0]
+    assert rel_err(got["split"], got["claim"]) <= 1e-5
+
+
 ENGINE_CASES = [(fmt, m, n, k) for fmt in ("int4", "int8") for m in (2, 3, 5)
                 for (n, k) in [(45, 4096), (70, 8192), (3, 32), (130, 16384), (7, 0)]] + \
     [("int4", m, 19, 28672) for m in (2, 3, 5)] + [("int4", 5, 2, 32768), ("int8", 2, 9, 28672)]

@@ -185,15 +185,22 @@ struct FmtInt4 {
   };
 
   __device__ static X load_x(const uint16_t* x, int c, bool ok) {
+    u32x4 v[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) v[h] = ok ? load16(x + 32 * (int64_t)c + 8 * h) : u32x4{0, 0, 0, 0};
+    return from_words(v);
+  }
+  // The chunk's 32 activations as loaded (16 words, v[h][j] = word 4 h + j)
+  // in the layout above, with their sum.
+  __device__ static X from_words(const u32x4 (&v)[4]) {
     X r;
     uint32_t wd[16];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      u32x4 v = ok ? load16(x + 32 * (int64_t)c + 8 * h) : u32x4{0, 0, 0, 0};
-      wd[4 * h] = v[0];
-      wd[4 * h + 1] = v[1];
-      wd[4 * h + 2] = v[2];
-      wd[4 * h + 3] = v[3];
+      wd[4 * h] = v[h][0];
+      wd[4 * h + 1] = v[h][1];
+      wd[4 * h + 2] = v[h][2];
+      wd[4 * h + 3] = v[h][3];
     }
     // word t of x holds (x[2t], x[2t+1]); an 8-code weight word i spans x
     // words 4i .. 4i+3.

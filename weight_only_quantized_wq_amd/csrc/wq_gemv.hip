@@ -2,15 +2,19 @@
 // and int4 weights, streamed from HBM: launch planning and the C entry
 // points.  The kernels are in wq_gemv_kernel.hpp (one token row; 2, 3 and 5
 // rows on the vector ALU when WQ_SMALLM_ENGINE=valu asks for them),
-// wq_mfma.hpp (2..8 int4 rows) and wq_step_i8mt.hpp (2..8 int8 rows).
+// wq_mfma.hpp and wq_verify.hpp (2..8 int4 rows) and wq_step_i8mt.hpp (2..8
+// int8 rows).
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
 
 #include "wq_gemv_kernel.hpp"
 #include "wq_host.hpp"
 #include "wq_mfma.hpp"
 #include "wq_step_i8mt.hpp"
+#include "wq_verify.hpp"
 
 namespace wq {
 
@@ -297,6 +301,81 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   return launch_status("wq_gemm_smallM");
 }
 
+// Claim slots of the single-matrix verify kernel, one per launch in turn;
+// each launch leaves its slot zero.  Up to kMatrixClaimSlots launches may be
+// in flight on one device at once.
+constexpr int kMatrixClaimSlots = 1024;
+static __device__ MatrixClaim g_matrix_claims[kMatrixClaimSlots];
+
+static MatrixClaim* matrix_claim_slot() {
+  static std::atomic<MatrixClaim*> base[kMaxDevices];
+  static std::atomic<uint32_t> seq{0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  MatrixClaim* p = base[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(g_matrix_claims)) != hipSuccess || !q) return nullptr;
+    p = static_cast<MatrixClaim*>(q);
+    base[dev].store(p, std::memory_order_release);
+  }
+  return p + seq.fetch_add(1, std::memory_order_relaxed) % kMatrixClaimSlots;
+}
+
+// Verify product with the weights in the B operand (gemm_verify_matrix_kernel,
+// rows within one activation window): 8 waves over blocks of 32 rows, the
+// step kernel's per-token-count windows; blocks past each workgroup's first
+// are claimed as the workgroups go.
+template <int M>
+int launch_verify_matrix(const GemvArgs& g, hipStream_t stream) {
+  constexpr int RT = 2, WAVES = 8, OCT = M == 4 ? 2 : 4, KW = VerifyConfig<M>::kKW;
+  auto kern = gemm_verify_matrix_kernel<M, KW, WAVES, RT, OCT, true>;
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
+  GemvArgs a = g;
+  a.batches = (g.n + 16 * RT - 1) / (16 * RT);
+  const int64_t grid = a.batches < resident ? a.batches : resident;
+  if (grid <= 0) return WQ_OK;
+  // every workgroup may take up to `cap` blocks; grid * (cap - 1) blocks past
+  // the first ones must cover the matrix
+  const int64_t per = (a.batches + grid - 1) / grid;
+  if (per + 1 > kMatrixMaxLocal) return launch_mfma<M>(g, stream);
+  const int32_t cap = (int32_t)(2 * per + 2 < kMatrixMaxLocal ? 2 * per + 2 : kMatrixMaxLocal);
+  MatrixClaim* claim = matrix_claim_slot();
+  if (!claim) return fail(WQ_ERR_LAUNCH, "wq_gemm_smallM: no claim slot on the current device");
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * kWave), 0, stream, a, claim, cap);
+  return launch_status("wq_gemm_smallM");
+}
+
+// Which matrix-core kernel serves 2..5 int4 token rows of one matrix:
+// gemm_mfma_kernel ("split": a workgroup's blocks in a fixed stride, each
+// block's items dealt to its waves) or gemm_verify_matrix_kernel ("claim":
+// (block, window) units claimed by the waves, blocks past the first two
+// claimed by the workgroups).  "auto" takes claim where it was measured
+// faster: rows that fill all eight waves' windows (k >= 8192, within one
+// activation window) and at least 5 blocks per workgroup (57344 x 8192:
+// 67.8 -> 59.8 us, 128256 x 8192: 131.8 -> 108.8 us at 5 tokens); on
+// smaller or shorter matrices its staging and claims cost more than they
+// save (32768 x 8192 even, 16384 x 8192 and k = 4096 up to 20 % slower).
+// WQ_SMALLM_KERNEL=split or =claim forces one where it applies (read at each
+// call), which is how the two are timed and tested against each other.
+enum class VerifyKernel { kAuto, kSplit, kClaim };
+
+static VerifyKernel smallm_kernel() {
+  const char* v = getenv("WQ_SMALLM_KERNEL");
+  if (v && strcmp(v, "split") == 0) return VerifyKernel::kSplit;
+  if (v && strcmp(v, "claim") == 0) return VerifyKernel::kClaim;
+  return VerifyKernel::kAuto;
+}
+
+static bool use_claim_kernel(int64_t m, int64_t n, int64_t chunks) {
+  if (m < 2 || m > 5 || chunks <= 0) return false;
+  if (chunks > (m == 2 ? VerifyConfig<2>::kKW : VerifyConfig<3>::kKW)) return false;
+  const VerifyKernel kind = smallm_kernel();
+  if (kind != VerifyKernel::kAuto) return kind == VerifyKernel::kClaim;
+  const int64_t blocks = (n + 31) / 32;
+  return chunks >= 8 * kSzWin && blocks >= 5 * 256;
+}
+
 }  // namespace wq
 
 namespace wq {
@@ -365,6 +444,14 @@ static int gemm_small_m_int4(const char* name, const uint16_t* x, int64_t m, con
   if (m == 1) return run_gemv<FmtInt4, 1>(a, s, name);
   if (k > kMfmaMaxK) return fail(WQ_ERR_SHAPE, "%s: k = %lld is larger than %d", name, (long long)k, kMfmaMaxK);
   if (use_valu(false, m, a.chunks)) return run_gemv_m<FmtInt4>(a, m, s, name);
+  if (use_claim_kernel(m, n, a.chunks)) {
+    switch (m) {
+      case 2: return launch_verify_matrix<2>(a, s);
+      case 3: return launch_verify_matrix<3>(a, s);
+      case 4: return launch_verify_matrix<4>(a, s);
+      default: return launch_verify_matrix<5>(a, s);
+    }
+  }
   switch (m) {
     case 2: return launch_mfma<2>(a, s);
     case 3: return launch_mfma<3>(a, s);

@@ -46,6 +46,8 @@ namespace wq {
 
 // Longest row (inputs) the verify kernel accepts (offsets stay in 32 bits).
 constexpr int kVerifyMaxK = 131072;
+// Blocks one workgroup of the single-matrix verify kernel takes at most.
+constexpr int kMatrixMaxLocal = 64;
 
 // Per token count: waves per workgroup, 16-row tiles per block, quads per
 // item, groups per staged activation window, code tiles in LDS (chosen by
@@ -83,8 +85,9 @@ struct alignas(16) VerifyShared {
   uint32_t xs[M][kRow];          // pre-permuted bf16 pairs, 16 words per group
   float gs[KW][kSets][4];        // -128 x the per-group activation sums, [group][set][token in set]
   // the per-group activation sums X as three bf16 parts hi + mid + lo
-  // (|X - hi - mid - lo| <= 2^-27 |X|); rows of tokens past M are zero
-  alignas(16) uint16_t xz[kZRows][kSumRow];
+  // (|X - hi - mid - lo| <= 2^-27 |X|), row M part + token: only the M
+  // tokens' rows are kept (the A rows of absent tokens are zero registers)
+  alignas(16) uint16_t xz[3 * M][kSumRow];
 };
 
 template <int RT, int OCT>
@@ -117,6 +120,27 @@ __device__ __forceinline__ vf32x4 mfma16x16x32(const uint32_t (&a)[4], const uin
                                                  0, 0, 0);
 }
 
+// The LDS entries of token t (< M) for window group g: its pre-permuted
+// pairs and -128 x its sum (g < kpad), and the sum's three bf16 parts.
+template <int M, int KW>
+__device__ __forceinline__ void verify_put(VerifyShared<M, KW>& sh, int t, int g, int kpad, const FmtInt4::X& xv) {
+  if (g < kpad) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<u32x4*>(&sh.xs[t][16 * g + 4 * h]) =
+          u32x4{xv.p[4 * h], xv.p[4 * h + 1], xv.p[4 * h + 2], xv.p[4 * h + 3]};
+    sh.gs[g][t >> 2][t & 3] = -128.0f * xv.gsum;
+  }
+  // each difference is exact in fp32
+  const uint16_t hi = f32_to_bf16(xv.gsum);
+  const float r1 = xv.gsum - __uint_as_float((uint32_t)hi << 16);
+  const uint16_t mid = f32_to_bf16(r1);
+  const uint16_t lo = f32_to_bf16(r1 - __uint_as_float((uint32_t)mid << 16));
+  sh.xz[t][g] = hi;
+  sh.xz[M + t][g] = mid;
+  sh.xz[2 * M + t][g] = lo;
+}
+
 // Stages groups [g0, g0 + kpad) of every token and their sums over whole
 // (scale, zero) windows (kpad rounded up to kSzWin); groups at or past the
 // row's end are zero.
@@ -130,29 +154,52 @@ __device__ __forceinline__ void verify_stage(const GemvArgs& a, int g0, int kpad
     const int t = it / kz;
     const int g = it - t * kz;
     const int gg = g0 + g;
-    uint16_t hi = 0, mid = 0, lo = 0;
-    float gsum = 0.0f;
     if (t < M) {
-      const FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, gg, gg < a.chunks && g < kpad);
-      if (g < kpad) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          *reinterpret_cast<u32x4*>(&sh.xs[t][16 * g + 4 * h]) =
-              u32x4{xv.p[4 * h], xv.p[4 * h + 1], xv.p[4 * h + 2], xv.p[4 * h + 3]};
-      }
-      gsum = xv.gsum;
-      // each difference is exact in fp32
-      hi = f32_to_bf16(gsum);
-      const float r1 = gsum - __uint_as_float((uint32_t)hi << 16);
-      mid = f32_to_bf16(r1);
-      lo = f32_to_bf16(r1 - __uint_as_float((uint32_t)mid << 16));
+      verify_put<M, KW>(sh, t, g, kpad, FmtInt4::load_x(a.x + (int64_t)t * a.k, gg, gg < a.chunks && g < kpad));
+    } else if (t < 4 * SETS && g < kpad) {
+      sh.gs[g][t >> 2][t & 3] = 0.0f;
     }
-    if (t < 4 * SETS && g < kpad) sh.gs[g][t >> 2][t & 3] = -128.0f * gsum;
-    sh.xz[t][g] = hi;
-    sh.xz[ZLO + t][g] = mid;
-    sh.xz[2 * ZLO + t][g] = lo;
   }
 }
+
+// Two-phase staging of one whole window [0, kz) (kz a multiple of kSzWin):
+// stage_issue requests this thread's pieces (token, group) of the M token
+// rows -- through a buffer resource over them, so pieces past a row read as
+// zero without a branch -- and stage_finish permutes them into LDS.  Issued
+// before the weights, the activations arrive first, and their wait does not
+// hold for the weight loads behind them.
+template <int M, int KW, int THREADS>
+struct VerifyStage2 {
+  static constexpr int kPieces = (M * KW + THREADS - 1) / THREADS;
+  u32x4 v[kPieces][4];
+
+  __device__ __forceinline__ void issue(const GemvArgs& a, int kz) {
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, (uint32_t)(M * a.k * 2));
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int it = (int)threadIdx.x + q * THREADS;
+      const int t = it / kz, g = it - (it / kz) * kz;
+      const bool ok = t < M && g < a.chunks;
+      const uint32_t off = ok ? (uint32_t)t * (uint32_t)(a.k * 2) + (uint32_t)g * 64u : 0x80000000u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) v[q][h] = buffer_load16(rx, off + 16u * h);
+    }
+  }
+  __device__ __forceinline__ void finish(VerifyShared<M, KW>& sh, int kz) const {
+    constexpr int SETS = VerifyShared<M, KW>::kSets;
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int it = (int)threadIdx.x + q * THREADS;
+      const int t = it / kz, g = it - (it / kz) * kz;
+      if (t < M) verify_put<M, KW>(sh, t, g, kz, FmtInt4::from_words(v[q]));
+    }
+    // tokens past M in the last set: zero sums
+    for (int it = threadIdx.x; it < (4 * SETS - M) * kz; it += THREADS) {
+      const int t = M + it / kz, g = it - (it / kz) * kz;
+      sh.gs[g][t >> 2][t & 3] = 0.0f;
+    }
+  }
+};
 
 // The zero points of a (scale, zero) window for the wave's block.  A group
 // contributes s * (D - 128 X) + z * X to each token (D = sum of (128 + q) x
@@ -175,12 +222,14 @@ __device__ __forceinline__ void verify_zero_term(const VerifyShared<M, KW>& sh, 
   constexpr int ZR = VerifyShared<M, KW>::kZRows;
   constexpr int ZM = (ZR + 15) / 16;   // MFMAs per tile
   uint32_t av[ZM][4];
+  constexpr int ZLO = VerifyShared<M, KW>::kZLo;
 #pragma unroll
   for (int h = 0; h < ZM; ++h) {
-    const int row = 16 * h + col;
+    const int row = 16 * h + col;      // A row ZLO part + token
+    const int part = row / ZLO, t = row % ZLO;
     av[h][0] = av[h][1] = av[h][2] = av[h][3] = 0u;
-    if (row < ZR) {
-      const u32x4 xa = *reinterpret_cast<const u32x4*>(&sh.xz[row < ZR ? row : 0][il + 8 * rq]);
+    if (row < ZR && t < M) {
+      const u32x4 xa = *reinterpret_cast<const u32x4*>(&sh.xz[row < ZR && t < M ? M * part + t : 0][il + 8 * rq]);
       av[h][0] = xa[0];
       av[h][1] = xa[1];
       av[h][2] = xa[2];
@@ -257,7 +306,10 @@ __device__ __forceinline__ void verify_load(const GemvArgs& a, int64_t blk, int 
 // gw is a multiple of kSzWin, so the window's words start at word
 // gw >> gshift and chunk gw + i uses word i >> gshift of the window (the
 // window then holds more words than its chunks use).
-template <int RT>
+// OPAQUE hides each offset's select from the compiler, which otherwise may
+// issue two loads into the same registers under complementary lane masks;
+// the second then waits for every load in flight.
+template <int RT, bool OPAQUE = false>
 __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, int lane, SzWindow<RT>& z,
                                         bool any = true) {
   const uint32_t words = (uint32_t)int4_row_words(a.chunks, a.gshift);
@@ -273,9 +325,9 @@ __device__ __forceinline__ void sz_load(const GemvArgs& a, int64_t blk, int gw, 
 #pragma unroll
     for (int h = 0; h < kSzLoads; ++h) {
       const uint32_t row = (uint32_t)(kSzRowsPerLoad * h + lane / kSzLanesPerRow);
-      z.r[rt][h] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rs, (uint32_t)g < words ? (int)((row * words + (uint32_t)g) * 4u) : (int)0x80000000, 0, 2));
+      int off = (uint32_t)g < words ? (int)((row * words + (uint32_t)g) * 4u) : (int)0x80000000;
+      if constexpr (OPAQUE) asm volatile("" : "+v"(off));
+      z.r[rt][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2));
     }
   }
 }
@@ -823,6 +875,214 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
       __hip_atomic_store(&b->c[e], 0.0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   });
+}
+
+// Claim state of one single-matrix verify launch (gemm_verify_matrix_kernel):
+// blocks past each workgroup's first are claimed from `next`, and the
+// launch's last workgroup to finish (counted in `done`) returns both to
+// zero, so the slot is ready for its next launch.
+struct MatrixClaim {
+  int32_t next;
+  int32_t done;
+};
+
+// Waits for an LDS word written by another wave of the workgroup: until it
+// differs from `bad` (bad_is_value) or equals `want` (!bad_is_value).  The
+// waits of gemm_verify_matrix_kernel end once older work of the workgroup
+// has finished; the bound turns a broken invariant into wrong results
+// instead of a wave that never ends.
+__device__ __forceinline__ int lds_wait(const int* p, int v, bool until_equal) {
+  int x = 0;
+  for (int spin = 0; spin < (1 << 22); ++spin) {
+    x = __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if ((x == v) == until_equal) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return x;
+}
+
+// One matrix per launch (the single-matrix verify product), rows within one
+// activation window (k <= 32 KW).  The activations are staged once.  Work
+// units are (block of RT 16-row tiles, (scale, zero) window of kSzWin
+// groups = IW items): the waves of a workgroup claim them in order from an
+// LDS counter, so a slower wave simply takes fewer.  A workgroup's first
+// block is blockIdx.x; each further one is claimed from the launch's
+// MatrixClaim when the block before it is first entered (at most `cap`
+// blocks per workgroup), so faster workgroups take more blocks.  Each
+// unit's sums go to their own LDS slot; the wave that finishes a block's
+// last unit adds the slots in unit order and stores the rows, so results
+// do not depend on which wave or workgroup streamed what.  The next unit is
+// claimed, and its words and first item requested, before the current one
+// is reduced.
+template <int M, int KW, int WAVES, int RT, int OCT, bool LT>
+__global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs a, MatrixClaim* claim,
+                                                                        int32_t cap) {
+  constexpr int GI = 4 * OCT;          // groups per item
+  constexpr int IW = kSzWin / GI;      // items per unit
+  constexpr int UMAX = KW / kSzWin;    // units per block at most
+  constexpr int R = 2;                 // blocks whose unit sums may wait in LDS at once
+  static_assert(kSzWin % GI == 0 && KW % kSzWin == 0 && IW % 2 == 0, "windows must nest, items come in pairs");
+  constexpr int A1 = VerifyShared<M, KW>::kA1, A2 = VerifyShared<M, KW>::kA2, YS = VerifyShared<M, KW>::kYS;
+  __shared__ VerifyShared<M, KW> sh;
+  __shared__ __attribute__((aligned(16))) uint32_t szs[WAVES][RT][16][kSzRow];
+  __shared__ VerifyPart<M, RT, R * UMAX> part;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[LT ? WAVES : 1][LT ? kVerifyTile : 16];
+  __shared__ int gblk[kMatrixMaxLocal];   // global block of local block j; -1 until claimed
+  __shared__ int uctr;                    // units claimed
+  __shared__ int cnt[R];                  // units of the slot's block finished
+  __shared__ int freed[R];                // last local block summed out of the slot
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int rq = lane >> 4;
+  const int col = lane & 15;
+  uint32_t (*szb)[16][kSzRow] = szs[wave];
+  uint8_t* tile = tiles[LT ? wave : 0];
+  const FmtInt4::K kc = FmtInt4::consts();
+  const int nb = (int)a.batches;
+  const int ups = (a.chunks + kSzWin - 1) / kSzWin;    // units per block (1..UMAX)
+  const int first = ups < WAVES ? ups : WAVES;          // units taken without a claim
+
+  // claims unit i and finds its block: false when the unit lies past the work.
+  // Halfway through block jl (jl >= 1) the block after it is claimed, but
+  // only once jl's own block is known: the claims of one workgroup then land
+  // in order, so its blocks increase with jl and the first one past the
+  // matrix ends its work (two claims in flight at once could land swapped
+  // and strand a block).  A block past the matrix hands the same mark on
+  // without a claim.
+  const int uclaim = ups / 2;
+  auto resolve = [&](int i, int& jl, int& u, int& gb) -> bool {
+    jl = i / ups;
+    u = i - jl * ups;
+    if (jl >= cap) return false;
+    int v = 0;
+    if (lane == 0) {
+      v = lds_wait(&gblk[jl], -1, false);
+      if (jl >= 1 && u == uclaim && jl + 1 < cap) {
+        const int nx = v >= 0 && v < nb ? 2 * (int)gridDim.x + atomicAdd(&claim->next, 1) : nb;
+        __hip_atomic_store(&gblk[jl + 1], nx, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    gb = __builtin_amdgcn_readfirstlane(v);
+    return gb >= 0 && gb < nb;
+  };
+
+  // blocks 0 and 1 of a workgroup are its own (blockIdx.x and blockIdx.x +
+  // gridDim.x), so the launch starts without a claim; the claimed ones
+  // follow them
+  if (wave == 0) {
+    for (int j = lane; j < kMatrixMaxLocal; j += kWave)
+      gblk[j] = j == 0 ? (int)blockIdx.x : (j == 1 ? (int)(blockIdx.x + gridDim.x) : -1);
+    if (lane == 0) {
+      uctr = first;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        cnt[r] = 0;
+        freed[r] = r - R;
+      }
+    }
+  }
+
+  uint32_t av[A1][A2][4];
+#pragma unroll
+  for (int st = 0; st < A1; ++st)
+#pragma unroll
+    for (int j = 0; j < A2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) av[st][j][e] = 0u;
+  float y[RT][YS][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int st = 0; st < YS; ++st)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[rt][st][r] = 0.0f;
+
+  // the current unit (block jl of this workgroup = global block gb, window u)
+  int jl = 0, u = wave, gb = (int)blockIdx.x;
+  bool have = wave < first;
+  VerifyItem<RT, OCT> A, B;
+  SzWindow<RT> Z;
+  VerifyStage2<M, KW, WAVES * 64> stage;
+  stage.issue(a, ups * kSzWin);
+  __builtin_amdgcn_sched_barrier(0);
+  sz_load<RT, true>(a, have ? gb : 0, kSzWin * u, lane, Z, have);
+  // the words before the codes, as in the loop: a window's words are then
+  // older than the item in flight when they are published, on every path
+  // into the loop (otherwise the wait there drains the prefetch)
+  __builtin_amdgcn_sched_barrier(0);
+  verify_load<RT, OCT, LT>(a, have ? gb : 0, 0, IW * u, lane, A, have);
+  stage.finish(sh, ups * kSzWin);
+  __syncthreads();
+  if (!have) {
+    have = resolve(claim_batch(&uctr, lane), jl, u, gb);
+    sz_load<RT, true>(a, have ? gb : 0, kSzWin * u, lane, Z, have);
+    __builtin_amdgcn_sched_barrier(0);
+    verify_load<RT, OCT, LT>(a, have ? gb : 0, 0, IW * u, lane, A, have);
+  }
+
+  while (have) {
+    int jn, un, gn;
+    const bool more = resolve(claim_batch(&uctr, lane), jn, un, gn);
+    // the current window's words have arrived: publish them, request the next
+    sz_put<RT>(a, kSzWin * u, lane, Z, szb);
+    sz_load<RT, true>(a, more ? gn : 0, kSzWin * un, lane, Z, more);
+#pragma unroll
+    for (int h = 0; h < IW; h += 2) {
+      // the items' places in the window, opaque to the compiler: as
+      // constants they let it hoist every word address of the window out of
+      // the loop, which spills
+      int iz0 = h * GI, iz1 = (h + 1) * GI;
+      asm volatile("" : "+s"(iz0), "+s"(iz1));
+      verify_load<RT, OCT, LT>(a, gb, 0, IW * u + h + 1, lane, B);
+      verify_item<M, KW, RT, OCT, LT>(A, IW * u * GI + iz0, iz0, a.gshift, rq, col, sh, szb, kc, av, y, tile);
+      if (h + 2 < IW) {
+        verify_load<RT, OCT, LT>(a, gb, 0, IW * u + h + 2, lane, A);
+      } else {
+        verify_load<RT, OCT, LT>(a, more ? gn : 0, 0, IW * un, lane, A, more);
+      }
+      verify_item<M, KW, RT, OCT, LT>(B, IW * u * GI + iz1, iz1, a.gshift, rq, col, sh, szb, kc, av, y, tile);
+    }
+    // this unit's sums into its slot, once the slot's previous block is out
+    const int sl = jl % R;
+    if (lane == 0) lds_wait(&freed[sl], jl - R, true);
+    __builtin_amdgcn_wave_barrier();
+    verify_fold<M, RT, YS, R * UMAX>(a, gb, sl * UMAX + u, true, false, rq, col, y, part);
+    __builtin_amdgcn_wave_barrier();
+    int done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(&cnt[sl], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    done = __builtin_amdgcn_readfirstlane(done);
+    __builtin_amdgcn_wave_barrier();
+    if (done == ups - 1) {
+      // the block's last unit: add its units' sums in order and store them
+      const int64_t n0 = (int64_t)gb * RT * 16;
+      for (int i = lane; i < RT * 16 * M; i += kWave) {
+        const int r = i / M, t = i - r * M;
+        float v = part.v[sl * UMAX][r][t];
+        for (int w = 1; w < ups; ++w) v += part.v[sl * UMAX + w][r][t];
+        const int64_t row = n0 + r;
+        if (row < a.n) {
+          if (a.y32) *gmem(a.y32 + ((int64_t)t * a.n + row)) = v;
+          if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(v);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) {
+        __hip_atomic_store(&cnt[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&freed[sl], jl, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    jl = jn;
+    u = un;
+    gb = gn;
+    have = more;
+  }
+  wait_vmem_all();
+  __syncthreads();
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(&claim->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+    __hip_atomic_store(&claim->next, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&claim->done, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 }  // namespace wq

@@ -187,8 +187,10 @@ int wq_gemm_smallM_int4(const uint16_t* x, int64_t m, const uint8_t* qpacked, co
  * [README] "Int8 仅权重量化".  x bf16 [m][k], 1 <= m <= 8; q, scale as written
  * by wq_quantize_int8; y [m][n] with y[t][r] = scale[r] * sum_k x[t][k] q[r][k];
  * row t of y equals wq_gemv_int8 applied to row t of x (to fp32 rounding).
- * Each weight is read once (m >= 2: on the matrix cores; WQ_SMALLM_ENGINE as
- * for wq_gemm_smallM).  k % 16 == 0; k <= 65536 for m == 1 (the one-token
+ * Each weight is read once (m >= 2: on the matrix cores; WQ_SMALLM_ENGINE and
+ * WQ_SMALLM_KERNEL as for wq_gemm_smallM, the claiming kernel taken by
+ * default from 98304 rows on, for k from 8192 to 32768, with the same
+ * per-call slots).  k % 16 == 0; k <= 65536 for m == 1 (the one-token
  * matvec), k <= 2^24 and n * k <= 0xFFFFFF00 for m >= 2.  scale 2-byte
  * aligned.
  */

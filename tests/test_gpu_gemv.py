@@ -328,6 +328,39 @@ def test_gemm_small_m_kernels(wq, monkeypatch, m, group, n, k):
     assert rel_err(got["split"], got["claim"]) <= 1e-5
 
 
+# The int8 counterparts (WQ_SMALLM_KERNEL forces one): batches of 1, 2 and 4
+# tiles, 1..32 units of 8 passes per batch, more batches than workgroups,
+# ragged last batches and passes.
+I8_KERNEL_CASES = [(5, 45, 4096), (2, 3, 16), (8, 70, 8192), (3, 16411, 272), (5, 16448, 1024), (8, 20000, 528),
+                   (4, 9000, 16384), (2, 8200, 32768), (6, 17000, 4112), (7, 16400, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", I8_KERNEL_CASES)
+def test_gemm_small_m_int8_kernels(wq, monkeypatch, m, n, k):
+    """The fixed-stride and the claiming int8 matrix-core kernels each match
+    the oracle, each other to fp32 rounding, and themselves bit for bit."""
+    from oracle.matvec import gemm_small_m_int8
+    say(f"int8 kernels m={m} n={n} k={k}")
+    w = host_normal((n, k), 0.02, 955, m, n, k)
+    q, s = quantize_int8(w)
+    x = host_bf16_normal((m, k), 955, m, n, k + 1)
+    ref = gemm_small_m_int8(x, q, s)
+    qd, sd, xd = _d(q), dev(s), _d(x)
+    got = {}
+    for kind in ("split", "claim"):
+        monkeypatch.setenv("WQ_SMALLM_KERNEL", kind)
+        runs = []
+        for _ in range(2):
+            (b32, y32), (b16, y16) = _outputs(n, m)
+            wq.wq_gemm_smallM_int8(xd, m, qd, sd, n, k, y32, y16)
+            _compare(y32, y16, ref, (m, n))
+            _check_guards(b32, b16, m * n)
+            runs.append(host(y32).reshape(m, n))
+        assert_same(runs[1], runs[0])
+        got[kind] = runs[0]
+    assert rel_err(got["split"], got["claim"]) <= 1e-5
+
+
 ENGINE_CASES = [(fmt, m, n, k) for fmt in ("int4", "int8") for m in (2, 3, 5)
                 for (n, k) in [(45, 4096), (70, 8192), (3, 32), (130, 16384), (7, 0)]] + \
     [("int4", m, 19, 28672) for m in (2, 3, 5)] + [("int4", 5, 2, 32768), ("int8", 2, 9, 28672)]

@@ -506,6 +506,47 @@ int launch_i8m(const GemvArgs& a, hipStream_t stream) {
   return launch_i8m_u<M, 1>(a, stream);
 }
 
+// The claiming int8 kernel (gemm_i8_matrix_kernel): batches of U tiles as
+// above, units of kMtUnitPasses passes, batches past each workgroup's first
+// two claimed as the workgroups go.
+template <int M, int U>
+int launch_i8m_claim_u(GemvArgs a, hipStream_t stream) {
+  auto kern = gemm_i8_matrix_kernel<M, U, kI8mWaves>;
+  const int resident = resident_groups(reinterpret_cast<const void*>(kern), kI8mWaves * kWave);
+  const int64_t chunks = a.k / 16, per_pass = kMtPassChunks;
+  a.cpl = (int32_t)((chunks + per_pass - 1) / per_pass);
+  a.batches = (a.n + 16 * U - 1) / (16 * U);
+  const int64_t grid = a.batches < resident ? a.batches : resident;
+  if (grid <= 0) return WQ_OK;
+  const int64_t per = (a.batches + grid - 1) / grid;
+  if (per + 1 > kMatrixMaxLocal) return launch_i8m_u<M, U>(a, stream);
+  const int32_t cap = (int32_t)(2 * per + 2 < kMatrixMaxLocal ? 2 * per + 2 : kMatrixMaxLocal);
+  MatrixClaim* claim = matrix_claim_slot();
+  if (!claim) return fail(WQ_ERR_LAUNCH, "wq_gemm_smallM_int8: no claim slot on the current device");
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kI8mWaves * kWave), 0, stream, a, claim, cap);
+  return launch_status("wq_gemm_smallM_int8");
+}
+
+template <int M>
+int launch_i8m_claim(const GemvArgs& a, hipStream_t stream) {
+  if (a.n >= kI8mWideRows) return launch_i8m_claim_u<M, 4>(a, stream);
+  if (a.n >= kI8mMidRows && a.n * a.k >= kI8mMidBytes) return launch_i8m_claim_u<M, 2>(a, stream);
+  return launch_i8m_claim_u<M, 1>(a, stream);
+}
+
+// int8 counterpart of use_claim_kernel (rows of up to kMtMaxUnits units).
+// The int8 kernels are held by their decode arithmetic more than by how
+// the work is spread: at 2, 5 and 8 tokens the claiming kernel was measured
+// 2-3 % faster on 128256 x 8192, even on 57344 x 8192, and 10-30 % slower on
+// 28672 x 8192 and smaller or on 8192 x 28672, so "auto" takes it only from
+// 98304 rows on.
+static bool use_claim_kernel_i8(int64_t n, int64_t k) {
+  if (k <= 0 || k > (int64_t)kMtMaxUnits * kMtUnitPasses * 16 * kMtPassChunks) return false;
+  const VerifyKernel kind = smallm_kernel();
+  if (kind != VerifyKernel::kAuto) return kind == VerifyKernel::kClaim;
+  return k >= 8192 && n >= 98304;
+}
+
 }  // namespace wq
 
 extern "C" int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q, const uint16_t* scale, int64_t n,
@@ -530,6 +571,17 @@ extern "C" int wq_gemm_smallM_int8(const uint16_t* x, int64_t m, const int8_t* q
   if (m == 1) return run_gemv<FmtInt8, 1>(a, s, name);
   if (use_valu(true, m, a.chunks)) return run_gemv_m<FmtInt8>(a, m, s, name);
   // (k == 0: no passes; every output is the empty sum, 0)
+  if (use_claim_kernel_i8(n, k)) {
+    switch (m) {
+      case 2: return launch_i8m_claim<2>(a, s);
+      case 3: return launch_i8m_claim<3>(a, s);
+      case 4: return launch_i8m_claim<4>(a, s);
+      case 5: return launch_i8m_claim<5>(a, s);
+      case 6: return launch_i8m_claim<6>(a, s);
+      case 7: return launch_i8m_claim<7>(a, s);
+      default: return launch_i8m_claim<8>(a, s);
+    }
+  }
   switch (m) {
     case 2: return launch_i8m<2>(a, s);
     case 3: return launch_i8m<3>(a, s);

@@ -27,6 +27,7 @@
 
 #include <stdint.h>
 
+#include "wq_claim.hpp"
 #include "wq_gemv_kernel.hpp"
 #include "wq_mfma.hpp"
 #include "wq_step_shared.hpp"
@@ -285,6 +286,104 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_i8_smallm_kernel(GemvArgs a) 
     }
     __syncthreads();
   }
+}
+
+// One large matrix (wq_gemm_smallM_int8) in the claiming frame of
+// wq_claim.hpp: a block is a batch of U 16-row tiles, a unit kMtUnitPasses
+// passes (1024 inputs) of its rows.  A wave streams its units' passes with
+// two buffers alternating, the next unit's first pass requested while the
+// current unit's last one is reduced.  A unit's sums (the lanes of tokens
+// < M: four rows each per tile) go to its LDS slot; the block's last unit
+// adds the slots in unit order, scales and stores the rows.
+constexpr int kMtUnitPasses = 8;
+constexpr int kMtMaxUnits = 32;   // rows of up to 32768 inputs
+
+template <int M, int U, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemm_i8_matrix_kernel(GemvArgs a, MatrixClaim* claim, int32_t cap) {
+  constexpr int R = 2;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[WAVES][kMtTileLds];
+  __shared__ f32x4 part[R][kMtMaxUnits][U][4][M];   // slot, unit, tile, lane / 16, token
+  __shared__ MatrixUnitLds<R> ul;
+  const int lane = lane_id();
+  const int wave = (int)(threadIdx.x >> 6);
+  const int t = lane & 15, rq = lane >> 4;
+  uint8_t* lds = tiles[wave];
+  const int passes = a.cpl;
+  const int ups = (passes + kMtUnitPasses - 1) / kMtUnitPasses;   // units per block (1..kMtMaxUnits)
+  const int first = ups < WAVES ? ups : WAVES;
+  MatrixUnits<R> mu{ul, claim, ups, cap, (int)a.batches, lane};
+  mu.init(wave, first);
+  __syncthreads();
+
+  int jl = 0, u = wave, gb = (int)blockIdx.x;
+  bool have = wave < first;
+  if (!have) have = mu.claim_next(jl, u, gb);
+  if (!have) {
+    mu.end_launch();
+    return;
+  }
+  f32x4 acc[U];
+#pragma unroll
+  for (int i = 0; i < U; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int p = u * kMtUnitPasses;                                       // pass in A (then B, ...)
+  int pe = p + kMtUnitPasses < passes ? p + kMtUnitPasses : passes;
+  int jn = 0, un = 0, gn = 0;
+  bool more = mu.claim_next(jn, un, gn);                            // the unit after this one
+  MtPassBuf<U> A, B;
+  mt_load_pass<M, U>(a, gb, p, lane, A, true);
+
+  // consumes the pass in `cur` after requesting its successor into `nx`;
+  // false once the wave has no more work
+  auto step = [&](const MtPassBuf<U>& cur, MtPassBuf<U>& nx) -> bool {
+    const bool same = p + 1 < pe;
+    mt_load_pass<M, U>(a, same ? gb : gn, same ? p + 1 : un * kMtUnitPasses, lane, nx, same || more);
+    mt_accumulate<U>(cur, acc, lds, lane);
+    if (same) {
+      ++p;
+      return true;
+    }
+    // the unit is done: its sums into its slot, once the slot's previous
+    // block is out
+    const int sl = jl % R;
+    mu.wait_slot(jl);
+    if (t < M) {
+#pragma unroll
+      for (int i = 0; i < U; ++i) part[sl][u][i][rq][t < M ? t : 0] = acc[i];
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (mu.unit_done(jl)) {
+      // the block's last unit: add its units' sums in order, scale, store
+      f32x4 tot[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        tot[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (t < M) {
+          tot[i] = part[sl][0][i][rq][t < M ? t : 0];
+          for (int w = 1; w < ups; ++w) tot[i] += part[sl][w][i][rq][t < M ? t : 0];
+        }
+      }
+      int64_t rs = (int64_t)gb * 16 * U + (lane < 16 * U ? lane : 0);
+      if (rs >= a.n) rs = a.n - 1;
+      mt_store<M, U>(a, gb, lane, tot, (uint32_t)*gmem(a.scale + rs));
+      mu.release(jl);
+    }
+    if (!more) return false;
+    jl = jn;
+    u = un;
+    gb = gn;
+    p = u * kMtUnitPasses;
+    pe = p + kMtUnitPasses < passes ? p + kMtUnitPasses : passes;
+    more = mu.claim_next(jn, un, gn);
+    return true;
+  };
+  // the prefetch left in flight is drained on the way out
+  for (;;) {
+    if (!step(A, B)) break;
+    if (!step(B, A)) break;
+  }
+  wait_vmem_all();
+  mu.end_launch();
 }
 
 }  // namespace wq

@@ -39,6 +39,7 @@
 
 #include <stdint.h>
 
+#include "wq_claim.hpp"
 #include "wq_formats.hpp"
 #include "wq_step_shared.hpp"
 
@@ -46,8 +47,6 @@ namespace wq {
 
 // Longest row (inputs) the verify kernel accepts (offsets stay in 32 bits).
 constexpr int kVerifyMaxK = 131072;
-// Blocks one workgroup of the single-matrix verify kernel takes at most.
-constexpr int kMatrixMaxLocal = 64;
 
 // Per token count: waves per workgroup, 16-row tiles per block, quads per
 // item, groups per staged activation window, code tiles in LDS (chosen by
@@ -877,43 +876,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_step_kernel(const Gemv
   });
 }
 
-// Claim state of one single-matrix verify launch (gemm_verify_matrix_kernel):
-// blocks past each workgroup's first are claimed from `next`, and the
-// launch's last workgroup to finish (counted in `done`) returns both to
-// zero, so the slot is ready for its next launch.
-struct MatrixClaim {
-  int32_t next;
-  int32_t done;
-};
-
-// Waits for an LDS word written by another wave of the workgroup: until it
-// differs from `bad` (bad_is_value) or equals `want` (!bad_is_value).  The
-// waits of gemm_verify_matrix_kernel end once older work of the workgroup
-// has finished; the bound turns a broken invariant into wrong results
-// instead of a wave that never ends.
-__device__ __forceinline__ int lds_wait(const int* p, int v, bool until_equal) {
-  int x = 0;
-  for (int spin = 0; spin < (1 << 22); ++spin) {
-    x = __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if ((x == v) == until_equal) break;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return x;
-}
-
 // One matrix per launch (the single-matrix verify product), rows within one
-// activation window (k <= 32 KW).  The activations are staged once.  Work
-// units are (block of RT 16-row tiles, (scale, zero) window of kSzWin
-// groups = IW items): the waves of a workgroup claim them in order from an
-// LDS counter, so a slower wave simply takes fewer.  A workgroup's first
-// block is blockIdx.x; each further one is claimed from the launch's
-// MatrixClaim when the block before it is first entered (at most `cap`
-// blocks per workgroup), so faster workgroups take more blocks.  Each
-// unit's sums go to their own LDS slot; the wave that finishes a block's
-// last unit adds the slots in unit order and stores the rows, so results
-// do not depend on which wave or workgroup streamed what.  The next unit is
-// claimed, and its words and first item requested, before the current one
-// is reduced.
+// activation window (k <= 32 KW), in the claiming frame of wq_claim.hpp: a
+// block is RT 16-row tiles, a unit one (scale, zero) window of kSzWin groups
+// (IW items).  The activations are staged once, their loads issued before
+// the first unit's weights (a wait for a load also waits for everything
+// issued before it).  The next unit is claimed, and its words and first item
+// requested, before the current one is reduced.
 template <int M, int KW, int WAVES, int RT, int OCT, bool LT>
 __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs a, MatrixClaim* claim,
                                                                         int32_t cap) {
@@ -927,10 +896,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
   __shared__ __attribute__((aligned(16))) uint32_t szs[WAVES][RT][16][kSzRow];
   __shared__ VerifyPart<M, RT, R * UMAX> part;
   __shared__ __attribute__((aligned(16))) uint8_t tiles[LT ? WAVES : 1][LT ? kVerifyTile : 16];
-  __shared__ int gblk[kMatrixMaxLocal];   // global block of local block j; -1 until claimed
-  __shared__ int uctr;                    // units claimed
-  __shared__ int cnt[R];                  // units of the slot's block finished
-  __shared__ int freed[R];                // last local block summed out of the slot
+  __shared__ MatrixUnitLds<R> ul;
   const int lane = lane_id();
   const int wave = wave_id();
   const int rq = lane >> 4;
@@ -938,49 +904,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
   uint32_t (*szb)[16][kSzRow] = szs[wave];
   uint8_t* tile = tiles[LT ? wave : 0];
   const FmtInt4::K kc = FmtInt4::consts();
-  const int nb = (int)a.batches;
   const int ups = (a.chunks + kSzWin - 1) / kSzWin;    // units per block (1..UMAX)
   const int first = ups < WAVES ? ups : WAVES;          // units taken without a claim
-
-  // claims unit i and finds its block: false when the unit lies past the work.
-  // Halfway through block jl (jl >= 1) the block after it is claimed, but
-  // only once jl's own block is known: the claims of one workgroup then land
-  // in order, so its blocks increase with jl and the first one past the
-  // matrix ends its work (two claims in flight at once could land swapped
-  // and strand a block).  A block past the matrix hands the same mark on
-  // without a claim.
-  const int uclaim = ups / 2;
-  auto resolve = [&](int i, int& jl, int& u, int& gb) -> bool {
-    jl = i / ups;
-    u = i - jl * ups;
-    if (jl >= cap) return false;
-    int v = 0;
-    if (lane == 0) {
-      v = lds_wait(&gblk[jl], -1, false);
-      if (jl >= 1 && u == uclaim && jl + 1 < cap) {
-        const int nx = v >= 0 && v < nb ? 2 * (int)gridDim.x + atomicAdd(&claim->next, 1) : nb;
-        __hip_atomic_store(&gblk[jl + 1], nx, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
-    gb = __builtin_amdgcn_readfirstlane(v);
-    return gb >= 0 && gb < nb;
-  };
-
-  // blocks 0 and 1 of a workgroup are its own (blockIdx.x and blockIdx.x +
-  // gridDim.x), so the launch starts without a claim; the claimed ones
-  // follow them
-  if (wave == 0) {
-    for (int j = lane; j < kMatrixMaxLocal; j += kWave)
-      gblk[j] = j == 0 ? (int)blockIdx.x : (j == 1 ? (int)(blockIdx.x + gridDim.x) : -1);
-    if (lane == 0) {
-      uctr = first;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        cnt[r] = 0;
-        freed[r] = r - R;
-      }
-    }
-  }
+  MatrixUnits<R> mu{ul, claim, ups, cap, (int)a.batches, lane};
+  mu.init(wave, first);
 
   uint32_t av[A1][A2][4];
 #pragma unroll
@@ -1014,7 +941,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
   stage.finish(sh, ups * kSzWin);
   __syncthreads();
   if (!have) {
-    have = resolve(claim_batch(&uctr, lane), jl, u, gb);
+    have = mu.claim_next(jl, u, gb);
     sz_load<RT, true>(a, have ? gb : 0, kSzWin * u, lane, Z, have);
     __builtin_amdgcn_sched_barrier(0);
     verify_load<RT, OCT, LT>(a, have ? gb : 0, 0, IW * u, lane, A, have);
@@ -1022,7 +949,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
 
   while (have) {
     int jn, un, gn;
-    const bool more = resolve(claim_batch(&uctr, lane), jn, un, gn);
+    const bool more = mu.claim_next(jn, un, gn);
     // the current window's words have arrived: publish them, request the next
     sz_put<RT>(a, kSzWin * u, lane, Z, szb);
     sz_load<RT, true>(a, more ? gn : 0, kSzWin * un, lane, Z, more);
@@ -1044,15 +971,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
     }
     // this unit's sums into its slot, once the slot's previous block is out
     const int sl = jl % R;
-    if (lane == 0) lds_wait(&freed[sl], jl - R, true);
-    __builtin_amdgcn_wave_barrier();
+    mu.wait_slot(jl);
     verify_fold<M, RT, YS, R * UMAX>(a, gb, sl * UMAX + u, true, false, rq, col, y, part);
-    __builtin_amdgcn_wave_barrier();
-    int done = 0;
-    if (lane == 0) done = __hip_atomic_fetch_add(&cnt[sl], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
-    done = __builtin_amdgcn_readfirstlane(done);
-    __builtin_amdgcn_wave_barrier();
-    if (done == ups - 1) {
+    if (mu.unit_done(jl)) {
       // the block's last unit: add its units' sums in order and store them
       const int64_t n0 = (int64_t)gb * RT * 16;
       for (int i = lane; i < RT * 16 * M; i += kWave) {
@@ -1065,11 +986,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
           if (a.y16) *gmem(a.y16 + ((int64_t)t * a.n + row)) = f32_to_bf16(v);
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      if (lane == 0) {
-        __hip_atomic_store(&cnt[sl], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_store(&freed[sl], jl, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
+      mu.release(jl);
     }
     jl = jn;
     u = un;
@@ -1077,12 +994,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemm_verify_matrix_kernel(GemvArgs
     have = more;
   }
   wait_vmem_all();
-  __syncthreads();
-  if (threadIdx.x == 0 &&
-      __hip_atomic_fetch_add(&claim->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
-    __hip_atomic_store(&claim->next, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&claim->done, 0, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  mu.end_launch();
 }
 
 }  // namespace wq

@@ -82,18 +82,54 @@ __device__ __forceinline__ float dpp_row(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Stages activations of groups [g0, g0 + kw) for all M tokens into LDS.
+// Activations of groups [g0, g0 + kw) for all M tokens, staged into LDS in
+// two phases: issue() requests this thread's pieces (token, group) -- all
+// of them at once, through a buffer resource over the M token rows -- and
+// finish() writes them in the layout above.  Issued before a workgroup's
+// first weights, they arrive first, and their wait does not hold for the
+// weight loads behind them.
 template <int M, int RT, int KW, int WAVES>
-__device__ __forceinline__ void stage_window(const MfmaArgs& a, int g0, int kw, MfmaShared<M, RT, KW, WAVES>& sh) {
-  for (int it = threadIdx.x; it < M * kw; it += WAVES * 64) {
-    const int t = it / kw;
-    const int g = it - t * kw;
-    FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, g0 + g, true);
+struct MfmaStage {
+  static constexpr int kPieces = (M * KW + WAVES * 64 - 1) / (WAVES * 64);
+  u32x4 v[kPieces][4];
+
+  __device__ __forceinline__ void issue(const MfmaArgs& a, int g0, int kw) {
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, (uint32_t)(M * a.k * 2));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sh.xs[t][16 * g + i] = xv.p[i];
-    sh.gs[t][g] = xv.gsum;
+    for (int q = 0; q < kPieces; ++q) {
+      const int it = (int)threadIdx.x + q * WAVES * 64;
+      const int t = it / kw, g = it - (it / kw) * kw;
+      const uint32_t off = t < M ? (uint32_t)t * (uint32_t)(a.k * 2) + (uint32_t)(g0 + g) * 64u : 0x80000000u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) v[q][h] = buffer_load16(rx, off + 16u * h);
+    }
   }
-}
+  // One piece at a time instead (fewer registers), for a restaging inside
+  // the block loop where all of them in flight would spill.
+  __device__ static __forceinline__ void serial(const MfmaArgs& a, int g0, int kw, MfmaShared<M, RT, KW, WAVES>& sh) {
+    for (int it = threadIdx.x; it < M * kw; it += WAVES * 64) {
+      const int t = it / kw;
+      const int g = it - t * kw;
+      const FmtInt4::X xv = FmtInt4::load_x(a.x + (int64_t)t * a.k, g0 + g, true);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sh.xs[t][16 * g + i] = xv.p[i];
+      sh.gs[t][g] = xv.gsum;
+    }
+  }
+  __device__ __forceinline__ void finish(MfmaShared<M, RT, KW, WAVES>& sh, int kw) const {
+#pragma unroll
+    for (int q = 0; q < kPieces; ++q) {
+      const int it = (int)threadIdx.x + q * WAVES * 64;
+      const int t = it / kw, g = it - (it / kw) * kw;
+      if (t < M) {
+        const FmtInt4::X xv = FmtInt4::from_words(v[q]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sh.xs[t][16 * g + i] = xv.p[i];
+        sh.gs[t][g] = xv.gsum;
+      }
+    }
+  }
+};
 
 // One work item: OCT quads of a block's RT row tiles.  Lane (rq, col) loads
 // the 16 * OCT contiguous code bytes of groups gb + OCT rq + o (o < OCT) of
@@ -110,16 +146,18 @@ struct ItemData {
 // LT (line-wide, OCT = 2): the item's codes are read as two loads of 8 rows
 // x 128 bytes per tile (lane l: row l / 8 (+ 8), group gb + l % 8) and reach
 // the layout above through a per-wave LDS tile (mfma_blocks).
+// With !any every load reads zero (empty resources) without touching memory,
+// so a conditional request is issued like any other.
 template <int RT, int OCT, bool LT>
 __device__ __forceinline__ void load_item(const MfmaArgs& a, int64_t n0, int64_t gb, int rq, int col, int slot,
-                                          ItemData<RT, OCT>& q) {
+                                          ItemData<RT, OCT>& q, bool any = true) {
   static_assert(!LT || OCT == 2, "a line-wide item is 8 groups of 16 rows");
   const int lane = 16 * rq + col;
   const uint32_t row_bytes = (uint32_t)(a.k / 2);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int64_t rbase = n0 + 16 * rt;
-    const int64_t rows_left = a.n - rbase;
+    const int64_t rows_left = any ? a.n - rbase : 0;
     const uint32_t rows_ok = rows_left <= 0 ? 0u : (rows_left >= 16 ? 16u : (uint32_t)rows_left);
     const int64_t rb = rows_left > 0 ? rbase : 0;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(a.w + rb * (a.k / 2), rows_ok * row_bytes);
@@ -221,11 +259,24 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
   int64_t pblk = b_first;
   int pg0 = 0, pit = wave - WAVES;
   bool pending = false;
-  if (PF && pblk < b_end) {
-    pending = next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
-    if (pending) load_item<RT, OCT, LT>(a, pblk * 16 * RT, (int64_t)pg0 + 4 * OCT * pit, rq, col, slot, nxt);
+  // the first window's activations are requested before the first item and
+  // staged before the loop
+  const int kw0 = a.groups < KW ? a.groups : KW;
+  {
+    MfmaStage<M, RT, KW, WAVES> stage;
+    stage.issue(a, 0, kw0);
+    __builtin_amdgcn_sched_barrier(0);
+    // requested on every path (empty when there is none), so the staging's
+    // wait below holds only for the activations issued before it
+    if (PF) {
+      pending = pblk < b_end && next_item<KW, WAVES, OCT>(a, b_end, b_step, wave, pblk, pg0, pit);
+      load_item<RT, OCT, LT>(a, pending ? pblk * 16 * RT : 0, pending ? (int64_t)pg0 + 4 * OCT * pit : 0, rq, col,
+                             slot, nxt, pending);
+    }
+    stage.finish(sh, kw0);
   }
-  bool staged = false;
+  __syncthreads();
+  bool first_window = true;           // the first block's first window is staged
   uint32_t bop[SETS][4][4];          // B operands of the current quad (see below)
 #pragma unroll
   for (int st = 0; st < SETS; ++st)
@@ -246,12 +297,18 @@ __device__ __forceinline__ void mfma_blocks(const MfmaArgs& a_in, int64_t b_firs
 
     for (int g0 = 0; g0 < a.groups; g0 += KW) {
       const int kw = (a.groups - g0) < KW ? (a.groups - g0) : KW;
-      if (!single || !staged) {
+      if (!single && !first_window) {
         __syncthreads();                     // previous window fully consumed
-        stage_window<M, RT, KW, WAVES>(a, g0, kw, sh);
+        if constexpr (MfmaStage<M, RT, KW, WAVES>::kPieces <= 2) {
+          MfmaStage<M, RT, KW, WAVES> stage;
+          stage.issue(a, g0, kw);
+          stage.finish(sh, kw);
+        } else {
+          MfmaStage<M, RT, KW, WAVES>::serial(a, g0, kw, sh);
+        }
         __syncthreads();
-        staged = true;
       }
+      first_window = false;
       const int items = (kw + 4 * OCT - 1) / (4 * OCT);
       for (int it = wave; it < items; it += WAVES) {
         const int64_t gb = g0 + 4 * OCT * it;

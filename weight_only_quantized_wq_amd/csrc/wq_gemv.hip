@@ -274,12 +274,12 @@ extern "C" int wq_gemv_int4(const uint16_t* x, const uint8_t* qpacked, const uin
 
 namespace wq {
 
-// Verify product on the matrix cores (3 <= m <= 8): workgroups of 12 waves
-// over blocks of 32 rows, activations staged in LDS 256 groups (8192
+// Verify product on the matrix cores (2 <= m <= 8): workgroups of 12 waves
+// over blocks of RT 16-row tiles, activations staged in LDS 256 groups (8192
 // inputs) at a time, work items of 8 groups, one item prefetched.
-template <int M>
-int launch_mfma(const GemvArgs& g, hipStream_t stream) {
-  constexpr int RT = kMfmaRT, KW = kMfmaKW, WAVES = kMfmaWaves, PF = kMfmaPF, OCT = kMfmaOct;
+template <int M, int RT>
+int launch_mfma_rt(const GemvArgs& g, hipStream_t stream) {
+  constexpr int KW = kMfmaKW, WAVES = kMfmaWaves, PF = kMfmaPF, OCT = kMfmaOct;
   constexpr bool LT = M <= 7;   // the code tile fits beside the activation window
   auto kern = gemm_mfma_kernel<M, RT, KW, WAVES, PF, OCT, LT>;
   const int resident = resident_groups(reinterpret_cast<const void*>(kern), WAVES * kWave);
@@ -300,6 +300,26 @@ int launch_mfma(const GemvArgs& g, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WAVES * kWave), 0, stream, a);
   return launch_status("wq_gemm_smallM");
 }
+
+// Blocks of two tiles share each staged activation read between them, which
+// made one-tile blocks up to 25 % slower per tile (32000 x 4096: 13 % with
+// the same tiles per workgroup); one tile per block only where that gives a
+// workgroup at least a quarter fewer tiles (the largest workgroup share sets
+// the launch's time): 10240 x 8192 at 5 tokens 19.4 -> 18.0 us, 12288 x
+// 4096 12.6 -> 11.9 us.
+template <int M>
+int launch_mfma(const GemvArgs& g, hipStream_t stream) {
+  constexpr int kSlots = 256;   // one workgroup per CU
+  const int64_t tiles = (g.n + 15) / 16;
+  const int64_t per2 = 2 * (((tiles + 1) / 2 + kSlots - 1) / kSlots);   // tiles per workgroup, two-tile blocks
+  const int64_t per1 = (tiles + kSlots - 1) / kSlots;                   // one-tile blocks
+  if (4 * per1 <= 3 * per2) return launch_mfma_rt<M, 1>(g, stream);
+  return launch_mfma_rt<M, kMfmaRT>(g, stream);
+}
+
+}  // namespace wq
+
+namespace wq {
 
 // Claim slots of the single-matrix verify kernel, one per launch in turn;
 // each launch leaves its slot zero.  Up to kMatrixClaimSlots launches may be

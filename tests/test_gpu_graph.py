@@ -80,3 +80,54 @@ def test_moe_graph_replays_match_eager():
         torch.cuda.synchronize()
         for L, w in zip(ls.layers, want):
             assert torch.equal(L["y16"], w), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("fmt,m,n,k", [("int4", 5, 20000, 4096), ("int4", 2, 9000, 16384), ("int8", 5, 17000, 2048)])
+def test_claiming_kernel_streams_and_graph_replays(monkeypatch, fmt, m, n, k):
+    """The claiming single-matrix kernels take a claim slot per launch and
+    leave it zeroed: launches alternating between two streams (which may
+    overlap) and replays of a captured launch (one slot, reused) reproduce
+    the eager result bitwise."""
+    import torch
+    import weight_only_quantized_wq_amd as wq
+    monkeypatch.setenv("WQ_SMALLM_KERNEL", "claim")
+    say(f"claiming kernel streams/graph {fmt} m={m} n={n} k={k}")
+    if fmt == "int4":
+        p = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device="cuda")
+        sz = (torch.randint(0x3A00, 0x3C00, (n, k // 32, 2), dtype=torch.int32, device="cuda")).to(torch.int16)
+        call = lambda x, y: wq.wq_gemm_smallM(x, m, p, sz, n, k, y, None)
+    else:
+        q = torch.randint(-127, 128, (n, k), dtype=torch.int8, device="cuda")
+        s = torch.randint(0x3A00, 0x3C00, (n,), dtype=torch.int32, device="cuda").to(torch.int16)
+        call = lambda x, y: wq.wq_gemm_smallM_int8(x, m, q, s, n, k, y, None)
+    xs = [device_bf16_normal((m, k), "cuda", 956, i, m, n, k).view(torch.int16) for i in range(2)]
+    want = []
+    for x in xs:
+        y = torch.empty(m, n, dtype=torch.float32, device="cuda")
+        call(x, y)
+        torch.cuda.synchronize()
+        want.append(y.clone())
+    # two streams, launches alternating, each stream's output checked
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty(m, n, dtype=torch.float32, device="cuda") for _ in range(4)] for _ in range(2)]
+    torch.cuda.synchronize()
+    for r in range(4):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                call(xs[i], outs[i][r])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(4):
+            assert torch.equal(outs[i][r], want[i]), f"stream {i} launch {r} differs"
+    # a captured launch replayed: one slot, left zeroed by each replay
+    y = torch.empty(m, n, dtype=torch.float32, device="cuda")
+    g = _capture(lambda: call(xs[0], y))
+    junk = torch.randn(1 << 20, device="cuda")
+    for rep in range(4):
+        y.fill_(-1.0)                                 # eager work between replays
+        junk.mul_(1.0001).add_(0.5)
+        call(xs[1], torch.empty(m, n, dtype=torch.float32, device="cuda"))   # other slots in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want[0]), f"replay {rep} differs"

@@ -53,7 +53,8 @@ def test_status_strings(wq):
 
 
 def _rc(fn, *args):
-    return getattr(__import__("weight_only_quantized_wq_amd")._binding.lib, fn)(*args)
+    import importlib
+    return getattr(importlib.import_module("weight_only_quantized_wq_amd._binding").lib, fn)(*args)
 
 
 def test_null_pointers(wq):
